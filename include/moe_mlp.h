@@ -1,0 +1,188 @@
+/*
+ * moe_mlp.h -- C ABI of the MI355X (gfx950) routed MoE MLP library.
+ *
+ * The layer is the GLM-5.3-Flash MLP of the "Module glm5next_mlp" API page
+ * (GLM-5.3-Flash MLP production surface), section "The stack this layer
+ * runs":
+ *
+ *   ROUTED:  x -> gate.weight -> logits (f32) -> router_topk -> ids[K], weights[K]
+ *            x -> experts[id]: NVFP4 gate/up -> clamped SwiGLU -> NVFP4 down
+ *            x -> shared expert: BF16 gate/up -> clamped SwiGLU -> BF16 down
+ *            -> combine -> out
+ *   DENSE:   x -> gate/up -> clamped SwiGLU -> down -> out
+ *
+ * with the rules of that page's section "Traps this module exists to hold":
+ * the SwiGLU clamp is asymmetric (gate bounded above only, up bounded both
+ * ways, limit swiglu_limit, never defaulted); the router's correction bias
+ * steers selection only and the emitted weight is the unbiased sigmoid score
+ * renormalised over the chosen experts of the FULL expert count, then
+ * multiplied by routed_scaling_factor; the shared expert is not scaled by
+ * routed_scaling_factor.  "Constants, KERNEL_MAX_TOP_K": at most 16 experts
+ * per token.  The page's "forward" (decode, one token) and
+ * "forward_prefill_gemm" (grouped-GEMM prefill) are moe_mlp_decode and
+ * moe_mlp_prefill here.
+ *
+ * Conventions shared by every entry point:
+ *   - Every pointer argument except `stream` is a DEVICE pointer (HIP device
+ *     memory of the current device), unless stated otherwise.  Config and
+ *     weight-descriptor structs themselves are HOST memory.
+ *   - All tensors are row-major, contiguous, 16-byte aligned.  bf16 values
+ *     travel as uint16_t bit patterns.
+ *   - The caller owns every buffer, including the workspace.  The library
+ *     never allocates, frees or synchronises, keeps no pointer after return
+ *     and holds no global state; calls are reentrant.  Work is enqueued on
+ *     `stream` (a hipStream_t; NULL = the default stream) and the call
+ *     returns without waiting.  Device faults surface at the caller's next
+ *     synchronisation.
+ *   - Arguments are validated on the host before anything is enqueued; on an
+ *     error nothing is enqueued and the outputs are untouched.  T == 0 is a
+ *     no-op returning MOE_MLP_OK.
+ *   - Results are deterministic: the same inputs give the same bits on every
+ *     call (no floating-point atomics; fixed summation orders).
+ *
+ * Storage formats (the page names the routed experts NVFP4 W4A16):
+ *   - NVFP4 weight [rows, cols]: codes uint8 [rows, cols/2], the element in
+ *     column c is the low nibble of byte c/2 when c is even, the high nibble
+ *     when c is odd; each code is an FP4 E2M1 value (OCP Microscaling Formats
+ *     v1.0).  Block scales uint8 [rows, cols/16]: one OCP OFP8 E4M3 ("fn")
+ *     value per 16 consecutive columns of a row.  W[r][c] = e2m1 * e4m3.
+ *     One fp32 global scale per (expert, projection) multiplies the dot
+ *     product.
+ *   - x, shared/dense weights, the SwiGLU output h and the layer output are
+ *     bf16; h is rounded to bf16 (nearest even) before each down projection
+ *     and the output once after an fp32 combine.  Router logits, scores and
+ *     weights are fp32.
+ */
+#ifndef MOE_MLP_H
+#define MOE_MLP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes (return values; 0 = success, negative = error) ---- */
+#define MOE_MLP_OK                      0
+#define MOE_MLP_ERR_NULL_ARG           -1  /* a required pointer is NULL */
+#define MOE_MLP_ERR_BAD_SHAPE          -2  /* H, I, Is or Id not a positive multiple of 32; T < 0;
+                                              T above the entry point's maximum */
+#define MOE_MLP_ERR_BAD_TOPK           -3  /* top_k < 1, > MOE_MLP_MAX_TOP_K, or > num_experts */
+#define MOE_MLP_ERR_BAD_VALUE          -4  /* limit / rsf not finite and > 0; bad kind; E out of range;
+                                              n_shared_experts not 0 or 1 */
+#define MOE_MLP_ERR_MISALIGNED         -5  /* a device pointer is not 16-byte aligned */
+#define MOE_MLP_ERR_WORKSPACE_TOO_SMALL -6 /* ws_bytes below moe_mlp_workspace_size() */
+#define MOE_MLP_ERR_KIND_MISMATCH      -7  /* weights missing for the config's kind */
+#define MOE_MLP_ERR_HIP                -8  /* a kernel launch failed (hipGetLastError) */
+
+#define MOE_MLP_MAX_TOP_K      16    /* Module glm5next_mlp, Constants, KERNEL_MAX_TOP_K */
+#define MOE_MLP_MAX_EXPERTS    1024  /* one wavefront holds at most 16 scores per lane */
+#define MOE_MLP_DECODE_MAX_T   256   /* moe_mlp_decode handles up to this many tokens */
+
+#define MOE_MLP_KIND_ROUTED 0   /* router + routed NVFP4 experts + optional shared expert */
+#define MOE_MLP_KIND_DENSE  1   /* dense BF16 FFN (layers before first_k_dense_replace) */
+
+/*
+ * Layer geometry and constants.  Every field is read from the caller; none
+ * has a default ("Glm5NextMlpConfig: read from the checkpoint config --
+ * never defaulted", Module glm5next_mlp, Structs).
+ */
+typedef struct moe_mlp_config {
+  int32_t kind;                  /* MOE_MLP_KIND_ROUTED or MOE_MLP_KIND_DENSE */
+  int32_t hidden;                /* H; multiple of 32 */
+  int32_t moe_intermediate;      /* I, routed experts; multiple of 32 (ROUTED) */
+  int32_t num_experts;           /* E, the FULL expert count; 1..MOE_MLP_MAX_EXPERTS (ROUTED) */
+  int32_t top_k;                 /* K; 1..min(MOE_MLP_MAX_TOP_K, E) (ROUTED) */
+  int32_t n_shared_experts;      /* 0 or 1 (ROUTED) */
+  int32_t shared_intermediate;   /* Is; multiple of 32 when n_shared_experts == 1 */
+  int32_t dense_intermediate;    /* Id; multiple of 32 (DENSE) */
+  float   routed_scaling_factor; /* finite, > 0 (ROUTED); multiplies the top-k weights only */
+  float   swiglu_limit;          /* L; finite, > 0 */
+} moe_mlp_config;
+
+/*
+ * Weight contract for one layer (all device pointers, caller-owned).
+ * Fields that the config's kind does not use may be NULL.
+ */
+typedef struct moe_mlp_weights {
+  const float*    router_w;     /* [E, H] fp32 gate.weight */
+  const float*    router_bias;  /* [E] fp32 correction bias (selection only) */
+  const uint8_t*  w13_q;        /* [E, 2I, H/2] NVFP4 codes; rows [0,I) gate, [I,2I) up */
+  const uint8_t*  w13_s;        /* [E, 2I, H/16] E4M3 block scales */
+  const float*    w13_g;        /* [E, 2] fp32 global scales (gate, up) */
+  const uint8_t*  w2_q;         /* [E, H, I/2] NVFP4 codes of the down projection */
+  const uint8_t*  w2_s;         /* [E, H, I/16] E4M3 block scales */
+  const float*    w2_g;         /* [E] fp32 global scale of the down projection */
+  const uint16_t* shared_w13;   /* [2 Is, H] bf16: gate rows then up rows */
+  const uint16_t* shared_w2;    /* [H, Is] bf16 */
+  const uint16_t* dense_w13;    /* [2 Id, H] bf16: gate rows then up rows (DENSE) */
+  const uint16_t* dense_w2;     /* [H, Id] bf16 (DENSE) */
+} moe_mlp_weights;
+
+/*
+ * Workspace bytes that moe_mlp_decode (prefill == 0) or moe_mlp_prefill
+ * (prefill != 0) needs for T tokens.  `bytes` is a HOST pointer.  The
+ * workspace holds logits, routing, expert-sorted indices and intermediate
+ * activations; its contents need no initialisation and are garbage after a
+ * call.  Validates cfg like the compute calls (T limit included).
+ */
+int moe_mlp_workspace_size(const moe_mlp_config* cfg, int64_t T, int prefill, size_t* bytes);
+
+/*
+ * Decode form ("forward": the page's one-token decode), for 1..MOE_MLP_DECODE_MAX_T
+ * tokens.  Routed experts run as W4A16 GEMVs that stream the NVFP4 codes
+ * once per touched expert; the BF16 shared expert as a GEMV.
+ *   x        [T, H] bf16 input.
+ *   out      [T, H] bf16 output.
+ *   ids_out  [T, K] int32 chosen expert ids, descending biased score
+ *            (exact ties: lower id first); may be NULL.  ROUTED only.
+ *   w_out    [T, K] fp32 routing weights, same order; may be NULL.
+ *   workspace/ws_bytes: device scratch of at least moe_mlp_workspace_size(cfg, T, 0).
+ *   stream   hipStream_t (NULL = default stream).
+ */
+int moe_mlp_decode(const moe_mlp_config* cfg, const moe_mlp_weights* w, const uint16_t* x,
+                   int64_t T, uint16_t* out, int32_t* ids_out, float* w_out,
+                   void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * Prefill form ("forward_prefill_gemm": the page's grouped-GEMM prefill),
+ * any T >= 1 (bounded by INT32 index range: T * K < 2^31).  Tokens are
+ * sorted by expert id, each expert's rows run through a grouped GEMM that
+ * dequantises NVFP4 into bf16 MFMA operands, then are un-permuted and
+ * combined with the shared expert.  Arguments as moe_mlp_decode, with the
+ * workspace sized by moe_mlp_workspace_size(cfg, T, 1).
+ */
+int moe_mlp_prefill(const moe_mlp_config* cfg, const moe_mlp_weights* w, const uint16_t* x,
+                    int64_t T, uint16_t* out, int32_t* ids_out, float* w_out,
+                    void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * Router alone (test entry): logits = x . router_w^T (fp32), sigmoid scores,
+ * top-K of score + bias, weights = rsf * score / sum of chosen scores.
+ * Uses cfg->kind == ROUTED fields hidden, num_experts, top_k and
+ * routed_scaling_factor.  ids [T, K] int32, w [T, K] fp32 (both required).
+ * Workspace: moe_mlp_workspace_size(cfg, T, 1) bytes (prefill sizing).
+ */
+int moe_router_topk(const moe_mlp_config* cfg, const float* router_w, const float* router_bias,
+                     const uint16_t* x, int64_t T, int32_t* ids, float* w,
+                     void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * NVFP4 dequantisation (test entry), the same device routines the GEMV and
+ * grouped GEMM use: out[r][c] = global * e2m1(code[r][c]) * e4m3(scale[r][c/16]).
+ *   q [rows, cols/2], s [rows, cols/16]; cols a positive multiple of 32.
+ *   out_f32 [rows, cols] fp32 and/or out_bf16 [rows, cols] bf16 (RNE); at
+ *   least one non-NULL.  With global == 1 both outputs are exact.
+ */
+int moe_nvfp4_dequant(const uint8_t* q, const uint8_t* s, float global, int64_t rows,
+                      int64_t cols, float* out_f32, uint16_t* out_bf16, void* stream);
+
+/* Human-readable name of a status code (static string; never NULL). */
+const char* moe_mlp_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MLP_H */

@@ -1,0 +1,429 @@
+// C ABI of the routed MoE MLP library (declarations and contract in
+// include/moe_mlp.h).  Host code: argument validation (before anything is
+// enqueued), workspace layout, and the launch sequences of the decode and
+// prefill forms.  The library allocates nothing, never synchronises, and
+// keeps no state between calls.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "../../include/moe_mlp.h"
+#include "common.hpp"
+#include "gemm.hpp"
+#include "gemv.hpp"
+#include "permute.hpp"
+#include "router.hpp"
+
+namespace {
+
+using namespace moe;
+
+constexpr int64_t kMaxDim = 65536;
+
+bool finite_pos(float v) { return std::isfinite(v) && v > 0.0f; }
+bool aligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool bad_dim(int64_t d) { return d <= 0 || d % 32 != 0 || d > kMaxDim; }
+
+int validate_cfg(const moe_mlp_config* c, int64_t T, int prefill) {
+  if (!c) return MOE_MLP_ERR_NULL_ARG;
+  if (c->kind != MOE_MLP_KIND_ROUTED && c->kind != MOE_MLP_KIND_DENSE) return MOE_MLP_ERR_BAD_VALUE;
+  if (T < 0 || (!prefill && T > MOE_MLP_DECODE_MAX_T)) return MOE_MLP_ERR_BAD_SHAPE;
+  if (bad_dim(c->hidden)) return MOE_MLP_ERR_BAD_SHAPE;
+  if (!finite_pos(c->swiglu_limit)) return MOE_MLP_ERR_BAD_VALUE;
+  if (c->kind == MOE_MLP_KIND_DENSE) {
+    if (bad_dim(c->dense_intermediate)) return MOE_MLP_ERR_BAD_SHAPE;
+    return MOE_MLP_OK;
+  }
+  if (bad_dim(c->moe_intermediate)) return MOE_MLP_ERR_BAD_SHAPE;
+  if (c->n_shared_experts != 0 && c->n_shared_experts != 1) return MOE_MLP_ERR_BAD_VALUE;
+  if (c->n_shared_experts == 1 && bad_dim(c->shared_intermediate)) return MOE_MLP_ERR_BAD_SHAPE;
+  if (c->num_experts < 1 || c->num_experts > MOE_MLP_MAX_EXPERTS) return MOE_MLP_ERR_BAD_VALUE;
+  if (!finite_pos(c->routed_scaling_factor)) return MOE_MLP_ERR_BAD_VALUE;
+  if (c->top_k < 1 || c->top_k > MOE_MLP_MAX_TOP_K || c->top_k > c->num_experts) return MOE_MLP_ERR_BAD_TOPK;
+  if (T * c->top_k >= (int64_t(1) << 31)) return MOE_MLP_ERR_BAD_SHAPE;
+  return MOE_MLP_OK;
+}
+
+// Workspace regions, each 256-byte aligned.
+struct Plan {
+  size_t logits = 0, ids = 0, wts = 0;
+  size_t g_n = 0, g_expert = 0, g_count = 0, g_offset = 0, g_slots = 0;          // decode groups
+  size_t count = 0, offset = 0, perm = 0, n_tiles = 0, tile_e = 0, tile_m0 = 0;  // prefill permutation
+  size_t h = 0, hs = 0, y = 0, ys = 0;
+  size_t total = 0;
+  int64_t max_tiles = 0;
+};
+
+struct Alloc {
+  size_t cur = 0;
+  size_t take(size_t bytes) {
+    const size_t off = cur;
+    cur += (bytes + 255) & ~size_t(255);
+    return off;
+  }
+};
+
+Plan make_plan(const moe_mlp_config* c, int64_t T, int prefill) {
+  Plan p;
+  Alloc a;
+  if (c->kind == MOE_MLP_KIND_DENSE) {
+    p.h = a.take(size_t(T) * c->dense_intermediate * 2);
+    p.total = a.cur;
+    return p;
+  }
+  const int64_t E = c->num_experts, K = c->top_k, H = c->hidden, I = c->moe_intermediate;
+  const int64_t Is = c->n_shared_experts ? c->shared_intermediate : 0;
+  const int64_t S = T * K;
+  p.logits = a.take(size_t(T * E) * 4);
+  p.ids = a.take(size_t(S) * 4);
+  p.wts = a.take(size_t(S) * 4);
+  if (prefill) {
+    p.max_tiles = cdiv(S, GM_BM) + E;
+    p.count = a.take(size_t(E) * 4);
+    p.offset = a.take(size_t(E + 1) * 4);
+    p.perm = a.take(size_t(S) * 4);
+    p.n_tiles = a.take(4);
+    p.tile_e = a.take(size_t(p.max_tiles) * 4);
+    p.tile_m0 = a.take(size_t(p.max_tiles) * 4);
+  } else {
+    p.g_n = a.take(4);
+    p.g_expert = a.take(size_t(E) * 4);
+    p.g_count = a.take(size_t(E) * 4);
+    p.g_offset = a.take(size_t(E) * 4);
+    p.g_slots = a.take(size_t(S) * 4);
+  }
+  p.h = a.take(size_t(S * I) * 2);
+  if (Is) {
+    p.hs = a.take(size_t(T * Is) * 2);
+    p.ys = a.take(size_t(T * H) * 4);
+  }
+  p.y = a.take(size_t(S * H) * 4);
+  p.total = a.cur;
+  return p;
+}
+
+template <typename P>
+P* at(void* ws, size_t off) {
+  return reinterpret_cast<P*>(static_cast<char*>(ws) + off);
+}
+
+int validate_weights(const moe_mlp_config* c, const moe_mlp_weights* w) {
+  if (!w) return MOE_MLP_ERR_NULL_ARG;
+  const void* need[12];
+  int n = 0;
+  if (c->kind == MOE_MLP_KIND_DENSE) {
+    need[n++] = w->dense_w13;
+    need[n++] = w->dense_w2;
+  } else {
+    need[n++] = w->router_w;
+    need[n++] = w->router_bias;
+    need[n++] = w->w13_q;
+    need[n++] = w->w13_s;
+    need[n++] = w->w13_g;
+    need[n++] = w->w2_q;
+    need[n++] = w->w2_s;
+    need[n++] = w->w2_g;
+    if (c->n_shared_experts) {
+      need[n++] = w->shared_w13;
+      need[n++] = w->shared_w2;
+    }
+  }
+  for (int i = 0; i < n; ++i)
+    if (!need[i]) return MOE_MLP_ERR_KIND_MISMATCH;
+  for (int i = 0; i < n; ++i)
+    if (!aligned(need[i])) return MOE_MLP_ERR_MISALIGNED;
+  return MOE_MLP_OK;
+}
+
+int launch_status() { return hipGetLastError() == hipSuccess ? MOE_MLP_OK : MOE_MLP_ERR_HIP; }
+
+template <int NJ>
+void launch_topk_bucket(const float* logits, const float* bias, int T, int E, int K, float rsf, int32_t* ids,
+                        float* wts, int32_t* ids_out, float* w_out, Groups g, hipStream_t s) {
+  k_topk_bucket<NJ><<<1, 1024, 0, s>>>(logits, bias, T, E, K, rsf, ids, wts, ids_out, w_out, g);
+}
+
+void topk_bucket(int E, const float* logits, const float* bias, int T, int K, float rsf, int32_t* ids,
+                 float* wts, int32_t* ids_out, float* w_out, Groups g, hipStream_t s) {
+  const int nj = static_cast<int>(cdiv(E, 64));
+  if (nj <= 1) launch_topk_bucket<1>(logits, bias, T, E, K, rsf, ids, wts, ids_out, w_out, g, s);
+  else if (nj <= 2) launch_topk_bucket<2>(logits, bias, T, E, K, rsf, ids, wts, ids_out, w_out, g, s);
+  else if (nj <= 4) launch_topk_bucket<4>(logits, bias, T, E, K, rsf, ids, wts, ids_out, w_out, g, s);
+  else if (nj <= 8) launch_topk_bucket<8>(logits, bias, T, E, K, rsf, ids, wts, ids_out, w_out, g, s);
+  else launch_topk_bucket<16>(logits, bias, T, E, K, rsf, ids, wts, ids_out, w_out, g, s);
+}
+
+void topk_tokens(int E, const float* logits, const float* bias, int T, int K, float rsf, int32_t* ids,
+                 float* wts, int32_t* ids_out, float* w_out, hipStream_t s) {
+  const int nj = static_cast<int>(cdiv(E, 64));
+  const dim3 grid(static_cast<unsigned>(cdiv(T, 4)));
+  if (nj <= 1) k_topk<1><<<grid, 256, 0, s>>>(logits, bias, T, E, K, rsf, ids, wts, ids_out, w_out);
+  else if (nj <= 2) k_topk<2><<<grid, 256, 0, s>>>(logits, bias, T, E, K, rsf, ids, wts, ids_out, w_out);
+  else if (nj <= 4) k_topk<4><<<grid, 256, 0, s>>>(logits, bias, T, E, K, rsf, ids, wts, ids_out, w_out);
+  else if (nj <= 8) k_topk<8><<<grid, 256, 0, s>>>(logits, bias, T, E, K, rsf, ids, wts, ids_out, w_out);
+  else k_topk<16><<<grid, 256, 0, s>>>(logits, bias, T, E, K, rsf, ids, wts, ids_out, w_out);
+}
+
+void router_logits(const uint16_t* x, const float* wr, float* logits, int64_t T, int H, int E, hipStream_t s) {
+  if (T <= 16) {
+    k_logits_gemv<<<E, 256, 0, s>>>(x, wr, logits, static_cast<int>(T), H, E);
+  } else {
+    const dim3 grid(static_cast<unsigned>(cdiv(T, 64)), static_cast<unsigned>(cdiv(E, 64)));
+    k_logits_gemm<<<grid, 256, 0, s>>>(x, wr, logits, static_cast<int>(T), H, E);
+  }
+}
+
+template <bool NVFP4, int MODE, int RW>
+void gemv(const GemvArgs& a, int groups, hipStream_t s) {
+  const dim3 grid(static_cast<unsigned>(cdiv(a.half_rows, 4 * RW)), static_cast<unsigned>(groups));
+  k_gemv<NVFP4, MODE, RW><<<grid, 256, 0, s>>>(a);
+}
+
+template <bool NVFP4, int MODE, bool ROUTED>
+void gemm(const GemmArgs& a, int64_t m_tiles, hipStream_t s) {
+  const int nb = MODE == GEMM_GATEUP ? 128 : 256;
+  const dim3 grid(static_cast<unsigned>(m_tiles), static_cast<unsigned>(cdiv(a.half_n, nb)));
+  k_gemm<NVFP4, MODE, ROUTED><<<grid, 256, 0, s>>>(a);
+}
+
+GemvArgs bf16_gemv_args(const uint16_t* w, int half_rows, int cols, int T, const uint16_t* in, void* out,
+                        float limit) {
+  GemvArgs a{};
+  a.wb = w;
+  a.half_rows = half_rows;
+  a.cols = cols;
+  a.T = T;
+  a.K = 1;
+  a.in = in;
+  a.out = out;
+  a.limit = limit;
+  return a;
+}
+
+GemmArgs bf16_gemm_args(const uint16_t* act, int kdim, const uint16_t* w, int half_n, int T, void* out, int ldo,
+                        float limit) {
+  GemmArgs a{};
+  a.a = act;
+  a.kdim = kdim;
+  a.bb = w;
+  a.half_n = half_n;
+  a.T = T;
+  a.K = 1;
+  a.out = out;
+  a.ldo = ldo;
+  a.limit = limit;
+  return a;
+}
+
+int run_layer(const moe_mlp_config* c, const moe_mlp_weights* w, const uint16_t* x, int64_t T, uint16_t* out,
+              int32_t* ids_out, float* w_out, void* ws, size_t ws_bytes, void* stream, int prefill) {
+  int st = validate_cfg(c, T, prefill);
+  if (st) return st;
+  if (T == 0) return MOE_MLP_OK;
+  if ((st = validate_weights(c, w))) return st;
+  if (!x || !out || !ws) return MOE_MLP_ERR_NULL_ARG;
+  if (!aligned(x) || !aligned(out) || !aligned(ws)) return MOE_MLP_ERR_MISALIGNED;
+  if (c->kind == MOE_MLP_KIND_ROUTED && ((ids_out && !aligned(ids_out)) || (w_out && !aligned(w_out))))
+    return MOE_MLP_ERR_MISALIGNED;
+  const Plan p = make_plan(c, T, prefill);
+  if (ws_bytes < p.total) return MOE_MLP_ERR_WORKSPACE_TOO_SMALL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int H = c->hidden;
+  const float L = c->swiglu_limit;
+  const int Ti = static_cast<int>(T);
+
+  if (c->kind == MOE_MLP_KIND_DENSE) {
+    const int Id = c->dense_intermediate;
+    uint16_t* h = at<uint16_t>(ws, p.h);
+    if (prefill) {
+      const int64_t mt = cdiv(T, GM_BM);
+      gemm<false, GEMM_GATEUP, false>(bf16_gemm_args(x, H, w->dense_w13, Id, Ti, h, Id, L), mt, s);
+      gemm<false, GEMM_DOWN_BF16, false>(bf16_gemm_args(h, Id, w->dense_w2, H, Ti, out, H, L), mt, s);
+    } else {
+      gemv<false, GEMV_GATEUP, 2>(bf16_gemv_args(w->dense_w13, Id, H, Ti, x, h, L), 1, s);
+      gemv<false, GEMV_DOWN_BF16, 2>(bf16_gemv_args(w->dense_w2, H, Id, Ti, h, out, L), 1, s);
+    }
+    return launch_status();
+  }
+
+  const int E = c->num_experts, K = c->top_k, I = c->moe_intermediate;
+  const int Is = c->n_shared_experts ? c->shared_intermediate : 0;
+  float* logits = at<float>(ws, p.logits);
+  int32_t* ids = at<int32_t>(ws, p.ids);
+  float* wts = at<float>(ws, p.wts);
+  uint16_t* h = at<uint16_t>(ws, p.h);
+  float* y = at<float>(ws, p.y);
+  uint16_t* hs = Is ? at<uint16_t>(ws, p.hs) : nullptr;
+  float* ys = Is ? at<float>(ws, p.ys) : nullptr;
+  const int64_t S = T * K;
+
+  router_logits(x, w->router_w, logits, T, H, E, s);
+  if (prefill) {
+    topk_tokens(E, logits, w->router_bias, Ti, K, c->routed_scaling_factor, ids, wts, ids_out, w_out, s);
+    Perm pm{at<int32_t>(ws, p.count), at<int32_t>(ws, p.offset), at<int32_t>(ws, p.perm),
+            at<int32_t>(ws, p.n_tiles), at<int32_t>(ws, p.tile_e), at<int32_t>(ws, p.tile_m0)};
+    k_expert_count<<<E, 256, 0, s>>>(ids, static_cast<int>(S), pm);
+    k_schedule<<<1, 1024, 0, s>>>(E, GM_BM, pm);
+    k_expert_scatter<<<E, 256, 0, s>>>(ids, static_cast<int>(S), pm);
+    GemmArgs g{};
+    g.n_tiles = pm.n_tiles;
+    g.tile_expert = pm.tile_expert;
+    g.tile_m0 = pm.tile_m0;
+    g.count = pm.count;
+    g.offset = pm.offset;
+    g.perm = pm.perm;
+    g.K = K;
+    g.limit = L;
+    // routed gate/up + SwiGLU -> h (expert-sorted rows)
+    GemmArgs gu = g;
+    gu.a = x;
+    gu.kdim = H;
+    gu.bq = w->w13_q;
+    gu.bs = w->w13_s;
+    gu.stride_q = int64_t(2) * I * H / 2;
+    gu.stride_s = int64_t(2) * I * H / 16;
+    gu.gscale = w->w13_g;
+    gu.half_n = I;
+    gu.out = h;
+    gu.ldo = I;
+    gemm<true, GEMM_GATEUP, true>(gu, p.max_tiles, s);
+    // routed down -> y (slot rows)
+    GemmArgs gd = g;
+    gd.a = h;
+    gd.kdim = I;
+    gd.bq = w->w2_q;
+    gd.bs = w->w2_s;
+    gd.stride_q = int64_t(H) * I / 2;
+    gd.stride_s = int64_t(H) * I / 16;
+    gd.gscale = w->w2_g;
+    gd.half_n = H;
+    gd.out = y;
+    gd.ldo = H;
+    gemm<true, GEMM_DOWN_SLOT_F32, true>(gd, p.max_tiles, s);
+    if (Is) {
+      const int64_t mt = cdiv(T, GM_BM);
+      gemm<false, GEMM_GATEUP, false>(bf16_gemm_args(x, H, w->shared_w13, Is, Ti, hs, Is, L), mt, s);
+      gemm<false, GEMM_DOWN_F32, false>(bf16_gemm_args(hs, Is, w->shared_w2, H, Ti, ys, H, L), mt, s);
+    }
+  } else {
+    Groups gr{at<int32_t>(ws, p.g_n), at<int32_t>(ws, p.g_expert), at<int32_t>(ws, p.g_count),
+              at<int32_t>(ws, p.g_offset), at<int32_t>(ws, p.g_slots)};
+    topk_bucket(E, logits, w->router_bias, Ti, K, c->routed_scaling_factor, ids, wts, ids_out, w_out, gr, s);
+    const int groups = static_cast<int>(S < E ? S : E);
+    if (Is) gemv<false, GEMV_GATEUP, 1>(bf16_gemv_args(w->shared_w13, Is, H, Ti, x, hs, L), 1, s);
+    GemvArgs r{};
+    r.n_groups = gr.n_groups;
+    r.g_expert = gr.expert;
+    r.g_count = gr.count;
+    r.g_offset = gr.offset;
+    r.g_slots = gr.slots;
+    r.T = Ti;
+    r.K = K;
+    r.limit = L;
+    GemvArgs gu = r;
+    gu.wq = w->w13_q;
+    gu.ws = w->w13_s;
+    gu.stride_q = int64_t(2) * I * H / 2;
+    gu.stride_s = int64_t(2) * I * H / 16;
+    gu.gscale = w->w13_g;
+    gu.half_rows = I;
+    gu.cols = H;
+    gu.in = x;
+    gu.out = h;
+    gemv<true, GEMV_GATEUP, 2>(gu, groups, s);
+    if (Is) gemv<false, GEMV_DOWN_F32, 2>(bf16_gemv_args(w->shared_w2, H, Is, Ti, hs, ys, L), 1, s);
+    GemvArgs gd = r;
+    gd.wq = w->w2_q;
+    gd.ws = w->w2_s;
+    gd.stride_q = int64_t(H) * I / 2;
+    gd.stride_s = int64_t(H) * I / 16;
+    gd.gscale = w->w2_g;
+    gd.half_rows = H;
+    gd.cols = I;
+    gd.in = h;
+    gd.out = y;
+    gemv<true, GEMV_DOWN_F32, 4>(gd, groups, s);
+  }
+  const int64_t nq = T * (H / 4);
+  k_combine<<<static_cast<unsigned>(cdiv(nq, 256)), 256, 0, s>>>(y, ys, wts, Ti, K, H, out);
+  return launch_status();
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_mlp_workspace_size(const moe_mlp_config* cfg, int64_t T, int prefill, size_t* bytes) {
+  const int st = validate_cfg(cfg, T, prefill);
+  if (st) return st;
+  if (!bytes) return MOE_MLP_ERR_NULL_ARG;
+  *bytes = make_plan(cfg, T, prefill).total;
+  return MOE_MLP_OK;
+}
+
+int moe_mlp_decode(const moe_mlp_config* cfg, const moe_mlp_weights* w, const uint16_t* x, int64_t T,
+                   uint16_t* out, int32_t* ids_out, float* w_out, void* workspace, size_t ws_bytes,
+                   void* stream) {
+  return run_layer(cfg, w, x, T, out, ids_out, w_out, workspace, ws_bytes, stream, 0);
+}
+
+int moe_mlp_prefill(const moe_mlp_config* cfg, const moe_mlp_weights* w, const uint16_t* x, int64_t T,
+                    uint16_t* out, int32_t* ids_out, float* w_out, void* workspace, size_t ws_bytes,
+                    void* stream) {
+  return run_layer(cfg, w, x, T, out, ids_out, w_out, workspace, ws_bytes, stream, 1);
+}
+
+int moe_router_topk(const moe_mlp_config* cfg, const float* router_w, const float* router_bias,
+                    const uint16_t* x, int64_t T, int32_t* ids, float* w, void* workspace, size_t ws_bytes,
+                    void* stream) {
+  int st = validate_cfg(cfg, T, 1);
+  if (st) return st;
+  if (cfg->kind != MOE_MLP_KIND_ROUTED) return MOE_MLP_ERR_KIND_MISMATCH;
+  if (T == 0) return MOE_MLP_OK;
+  if (!router_w || !router_bias || !x || !ids || !w || !workspace) return MOE_MLP_ERR_NULL_ARG;
+  if (!aligned(router_w) || !aligned(router_bias) || !aligned(x) || !aligned(ids) || !aligned(w) ||
+      !aligned(workspace))
+    return MOE_MLP_ERR_MISALIGNED;
+  const Plan p = make_plan(cfg, T, 1);
+  if (ws_bytes < p.total) return MOE_MLP_ERR_WORKSPACE_TOO_SMALL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float* logits = at<float>(workspace, p.logits);
+  router_logits(x, router_w, logits, T, cfg->hidden, cfg->num_experts, s);
+  topk_tokens(cfg->num_experts, logits, router_bias, static_cast<int>(T), cfg->top_k,
+              cfg->routed_scaling_factor, ids, w, nullptr, nullptr, s);
+  return launch_status();
+}
+
+int moe_nvfp4_dequant(const uint8_t* q, const uint8_t* s, float global, int64_t rows, int64_t cols,
+                      float* out_f32, uint16_t* out_bf16, void* stream) {
+  if (!q || !s || (!out_f32 && !out_bf16)) return MOE_MLP_ERR_NULL_ARG;
+  if (rows < 0 || bad_dim(cols)) return MOE_MLP_ERR_BAD_SHAPE;
+  if (!std::isfinite(global)) return MOE_MLP_ERR_BAD_VALUE;
+  if (!aligned(q) || (out_f32 && !aligned(out_f32)) || (out_bf16 && !aligned(out_bf16)))
+    return MOE_MLP_ERR_MISALIGNED;
+  if ((reinterpret_cast<uintptr_t>(s) & 1u) != 0) return MOE_MLP_ERR_MISALIGNED;
+  if (rows == 0) return MOE_MLP_OK;
+  const int64_t n = rows * (cols / 32);
+  k_nvfp4_dequant<<<static_cast<unsigned>(cdiv(n, 256)), 256, 0, static_cast<hipStream_t>(stream)>>>(
+      q, s, global, rows, static_cast<int>(cols), out_f32, out_bf16);
+  return launch_status();
+}
+
+const char* moe_mlp_status_string(int status) {
+  switch (status) {
+    case MOE_MLP_OK: return "MOE_MLP_OK";
+    case MOE_MLP_ERR_NULL_ARG: return "MOE_MLP_ERR_NULL_ARG";
+    case MOE_MLP_ERR_BAD_SHAPE: return "MOE_MLP_ERR_BAD_SHAPE";
+    case MOE_MLP_ERR_BAD_TOPK: return "MOE_MLP_ERR_BAD_TOPK";
+    case MOE_MLP_ERR_BAD_VALUE: return "MOE_MLP_ERR_BAD_VALUE";
+    case MOE_MLP_ERR_MISALIGNED: return "MOE_MLP_ERR_MISALIGNED";
+    case MOE_MLP_ERR_WORKSPACE_TOO_SMALL: return "MOE_MLP_ERR_WORKSPACE_TOO_SMALL";
+    case MOE_MLP_ERR_KIND_MISMATCH: return "MOE_MLP_ERR_KIND_MISMATCH";
+    case MOE_MLP_ERR_HIP: return "MOE_MLP_ERR_HIP";
+    default: return "MOE_MLP_ERR_UNKNOWN";
+  }
+}
+
+}  // extern "C"

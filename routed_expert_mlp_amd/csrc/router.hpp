@@ -1,0 +1,295 @@
+// Sigmoid router top-k of the GLM-5.3-Flash routed MLP ("Module glm5next_mlp":
+// "The stack this layer runs": gate.weight -> logits (f32) -> router_topk ->
+// ids[K], weights[K]; "Traps this module exists to hold": the correction bias
+// steers selection only, the weight is the unbiased sigmoid score
+// renormalised over the chosen experts of the full count, then multiplied by
+// routed_scaling_factor; Constants, KERNEL_MAX_TOP_K: K <= 16).
+//
+// Logits are fp32 with a blocked accumulation order (short sequential runs,
+// then a tree or a sum of partials) so the emitted weights stay within 1e-6
+// relative of an fp64 evaluation.
+#pragma once
+
+#include "common.hpp"
+
+namespace moe {
+
+// ---------------------------------------------------------------------------
+// Logits for few tokens (decode): one workgroup per expert, threads stride
+// over H in float4 chunks, tokens processed in groups of TG.
+// ---------------------------------------------------------------------------
+constexpr int LOGIT_TG = 8;
+
+__global__ __launch_bounds__(256) void k_logits_gemv(const uint16_t* __restrict__ x,
+                                                     const float* __restrict__ wr,
+                                                     float* __restrict__ logits, int T, int H, int E) {
+  const int e = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int nchunk = H >> 2;                    // float4 chunks per row
+  const float4* wrow = reinterpret_cast<const float4*>(wr + static_cast<int64_t>(e) * H);
+  __shared__ float red[4][LOGIT_TG];
+  for (int t0 = 0; t0 < T; t0 += LOGIT_TG) {
+    const int nt = min(LOGIT_TG, T - t0);
+    float acc[LOGIT_TG];
+#pragma unroll
+    for (int t = 0; t < LOGIT_TG; ++t) acc[t] = 0.0f;
+    for (int c = tid; c < nchunk; c += 256) {
+      const float4 w4 = wrow[c];
+#pragma unroll
+      for (int t = 0; t < LOGIT_TG; ++t) {
+        if (t < nt) {
+          const uint2 xb = *reinterpret_cast<const uint2*>(x + static_cast<int64_t>(t0 + t) * H + 4 * c);
+          float a = acc[t];
+          a = fmaf(__uint_as_float(xb.x << 16), w4.x, a);
+          a = fmaf(__uint_as_float(xb.x & 0xffff0000u), w4.y, a);
+          a = fmaf(__uint_as_float(xb.y << 16), w4.z, a);
+          a = fmaf(__uint_as_float(xb.y & 0xffff0000u), w4.w, a);
+          acc[t] = a;
+        }
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < LOGIT_TG; ++t) {
+      const float s = wave_sum(acc[t]);
+      if (lane == 0) red[wv][t] = s;
+    }
+    __syncthreads();
+    if (tid < nt) {
+      const float s = (red[0][tid] + red[1][tid]) + (red[2][tid] + red[3][tid]);
+      logits[static_cast<int64_t>(t0 + tid) * E + e] = s;
+    }
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Logits for many tokens (prefill): fp32 tiled GEMM on the vector ALUs,
+// 64 tokens x 64 experts per workgroup, each thread 4 x 4 outputs.  Every
+// 32-wide k tile is summed into a fresh partial before joining the total.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_logits_gemm(const uint16_t* __restrict__ x,
+                                                     const float* __restrict__ wr,
+                                                     float* __restrict__ logits, int T, int H, int E) {
+  constexpr int BT = 64, BE = 64, BKk = 32;
+  __shared__ float xs[BKk][BT + 4];
+  __shared__ float ws[BKk][BE + 4];
+  const int tid = threadIdx.x;
+  const int t0 = blockIdx.x * BT, e0 = blockIdx.y * BE;   // x: token tiles, y: expert tiles
+  const int ty = tid >> 4, tx = tid & 15;
+  float acc[4][4], part[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = 0.0f;
+  // loaders: x tile 64 x 32 bf16 -> each thread 8 bf16; w tile 64 x 32 fp32 -> each thread 8 fp32
+  const int lr = tid >> 2, lk = (tid & 3) * 8;
+  for (int k0 = 0; k0 < H; k0 += BKk) {
+    {
+      const int t = t0 + lr;
+      uint4 xv = make_uint4(0, 0, 0, 0);
+      if (t < T) xv = *reinterpret_cast<const uint4*>(x + static_cast<int64_t>(t) * H + k0 + lk);
+      const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        xs[lk + 2 * q][lr] = __uint_as_float(xw[q] << 16);
+        xs[lk + 2 * q + 1][lr] = __uint_as_float(xw[q] & 0xffff0000u);
+      }
+      const int e = e0 + lr;
+      float4 w0 = make_float4(0, 0, 0, 0), w1 = w0;
+      if (e < E) {
+        const float4* p = reinterpret_cast<const float4*>(wr + static_cast<int64_t>(e) * H + k0 + lk);
+        w0 = p[0];
+        w1 = p[1];
+      }
+      ws[lk + 0][lr] = w0.x; ws[lk + 1][lr] = w0.y; ws[lk + 2][lr] = w0.z; ws[lk + 3][lr] = w0.w;
+      ws[lk + 4][lr] = w1.x; ws[lk + 5][lr] = w1.y; ws[lk + 6][lr] = w1.z; ws[lk + 7][lr] = w1.w;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) part[i][j] = 0.0f;
+#pragma unroll 8
+    for (int k = 0; k < BKk; ++k) {
+      float a[4], b[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = xs[k][ty * 4 + i];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) b[j] = ws[k][tx * 4 + j];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) part[i][j] = fmaf(a[i], b[j], part[i][j]);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] += part[i][j];
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int t = t0 + ty * 4 + i;
+    if (t >= T) continue;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = e0 + tx * 4 + j;
+      if (e < E) logits[static_cast<int64_t>(t) * E + e] = acc[i][j];
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Top-k of one token by one wavefront.  Lane l holds experts l, l+64, ...
+// (NJ per lane, E <= 64 * NJ).  Each of K rounds takes the largest biased
+// score (exact ties: lower expert id), then the weights are the chosen
+// unbiased scores over their sum, times rsf.
+// ---------------------------------------------------------------------------
+template <int NJ>
+__device__ __forceinline__ void topk_wave(const float* __restrict__ lrow, const float* __restrict__ bias,
+                                          int E, int K, float rsf, int32_t* ids, float* wts,
+                                          int32_t* ids2, float* wts2) {
+  const int lane = threadIdx.x & 63;
+  float sel[NJ], sc[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const int e = lane + 64 * j;
+    if (e < E) {
+      const float s = 1.0f / (1.0f + expf(-lrow[e]));
+      sc[j] = s;
+      sel[j] = s + bias[e];
+    } else {
+      sc[j] = 0.0f;
+      sel[j] = -INFINITY;
+    }
+  }
+  uint32_t taken = 0;
+  int my_id = 0;
+  float my_s = 0.0f, sum = 0.0f;
+  for (int k = 0; k < K; ++k) {
+    float best = -INFINITY, bs = 0.0f;
+    int be = 0x7fffffff;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int e = lane + 64 * j;
+      if (e < E && !((taken >> j) & 1u) && (sel[j] > best || be == 0x7fffffff)) {
+        best = sel[j];
+        bs = sc[j];
+        be = e;
+      }
+    }
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) {
+      const float ob = __shfl_xor(best, m, 64);
+      const float os = __shfl_xor(bs, m, 64);
+      const int oe = __shfl_xor(be, m, 64);
+      if (ob > best || (ob == best && oe < be)) {
+        best = ob;
+        bs = os;
+        be = oe;
+      }
+    }
+    if ((be & 63) == lane) taken |= 1u << (be >> 6);
+    if (lane == k) {
+      my_id = be;
+      my_s = bs;
+    }
+    sum += bs;
+  }
+  if (lane < K) {
+    const float w = my_s / sum * rsf;
+    ids[lane] = my_id;
+    wts[lane] = w;
+    if (ids2) ids2[lane] = my_id;
+    if (wts2) wts2[lane] = w;
+  }
+}
+
+template <int NJ>
+__global__ __launch_bounds__(256) void k_topk(const float* __restrict__ logits, const float* __restrict__ bias,
+                                              int T, int E, int K, float rsf, int32_t* __restrict__ ids,
+                                              float* __restrict__ wts, int32_t* ids_out, float* w_out) {
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const int64_t o = static_cast<int64_t>(t) * K;
+  topk_wave<NJ>(logits + static_cast<int64_t>(t) * E, bias, E, K, rsf, ids + o, wts + o,
+                ids_out ? ids_out + o : nullptr, w_out ? w_out + o : nullptr);
+}
+
+// ---------------------------------------------------------------------------
+// Decode: top-k for every token plus the per-expert token lists, in one
+// workgroup of 1024 threads (T * K <= 4096 slots).  Groups are the touched
+// experts in ascending id order; a group's slot list order is unspecified
+// (each slot's result does not depend on it).
+// ---------------------------------------------------------------------------
+struct Groups {
+  int32_t* n_groups;   // [1]
+  int32_t* expert;     // [E]
+  int32_t* count;      // [E]
+  int32_t* offset;     // [E]
+  int32_t* slots;      // [T*K]
+};
+
+template <int NJ>
+__global__ __launch_bounds__(1024) void k_topk_bucket(const float* __restrict__ logits,
+                                                      const float* __restrict__ bias, int T, int E, int K,
+                                                      float rsf, int32_t* __restrict__ ids,
+                                                      float* __restrict__ wts, int32_t* ids_out,
+                                                      float* w_out, Groups g) {
+  __shared__ int32_t s_cnt[1024];
+  __shared__ int32_t s_off[1024];
+  __shared__ int32_t s_wsum[16];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  for (int e = tid; e < E; e += 1024) s_cnt[e] = 0;
+  for (int t = wv; t < T; t += 16) {
+    const int64_t o = static_cast<int64_t>(t) * K;
+    topk_wave<NJ>(logits + static_cast<int64_t>(t) * E, bias, E, K, rsf, ids + o, wts + o,
+                  ids_out ? ids_out + o : nullptr, w_out ? w_out + o : nullptr);
+  }
+  __threadfence_block();
+  __syncthreads();
+  const int nslot = T * K;
+  for (int i = tid; i < nslot; i += 1024) atomicAdd(&s_cnt[ids[i]], 1);
+  __syncthreads();
+  // exclusive scans over experts of (count) and (count > 0): one element per thread
+  const int c = tid < E ? s_cnt[tid] : 0;
+  const int flag = c > 0 ? 1 : 0;
+  int inc_c = c, inc_f = flag;
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) {
+    const int a = __shfl_up(inc_c, m, 64);
+    const int b = __shfl_up(inc_f, m, 64);
+    if (lane >= m) {
+      inc_c += a;
+      inc_f += b;
+    }
+  }
+  if (lane == 63) s_wsum[wv] = (inc_c & 0xffff) | (inc_f << 16);
+  __syncthreads();
+  int base_c = 0, base_f = 0;
+  for (int w = 0; w < wv; ++w) {
+    base_c += s_wsum[w] & 0xffff;
+    base_f += s_wsum[w] >> 16;
+  }
+  const int off = base_c + inc_c - c;
+  const int grp = base_f + inc_f - flag;
+  if (tid < E) {
+    s_off[tid] = off;
+    if (flag) {
+      g.expert[grp] = tid;
+      g.count[grp] = c;
+      g.offset[grp] = off;
+    }
+    if (tid == E - 1) *g.n_groups = grp + flag;
+  }
+  __syncthreads();
+  for (int e = tid; e < E; e += 1024) s_cnt[e] = 0;
+  __syncthreads();
+  for (int i = tid; i < nslot; i += 1024) {
+    const int e = ids[i];
+    const int pos = s_off[e] + atomicAdd(&s_cnt[e], 1);
+    g.slots[pos] = i;
+  }
+}
+
+}  // namespace moe

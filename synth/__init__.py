@@ -192,6 +192,18 @@ for _n in ("flash_decode_t1", "flash_decode_t16", "flash_decode_t64", "prefill_t
     _add(_w.with_(name=_n + "_literal_bias", seed=_w.seed + 100, bias_amp=0.1))
 
 
+# Small parity workloads that still span several GEMM tiles and ragged tails:
+# H = 416 and I = 160 are not multiples of the 128-wide k blocks and output
+# tiles; T*K/E = 250 rows per expert crosses the 128-row M tiles.
+_X_SCALE_H416 = X_SCALE_H256 * math.sqrt(256 / 416)
+_add(Workload("ragged_prefill", T=1000, H=416, I=160, E=8, K=2, Is=96, seed=2001,
+              x_scale=_X_SCALE_H416, bias_amp=0.05, prefill=True))
+_add(Workload("ragged_decode", T=200, H=416, I=160, E=8, K=2, Is=96, seed=2002,
+              x_scale=_X_SCALE_H416, bias_amp=0.05))
+_add(Workload("ragged_dense_prefill", T=300, H=416, I=0, E=0, K=0, Is=0, seed=2003,
+              x_scale=_X_SCALE_H416, bias_amp=0.0, kind="dense", Id=160, prefill=True))
+
+
 def workload(name: str, **overrides) -> Workload:
     w = WORKLOADS[name]
     return w.with_(**overrides) if overrides else w

@@ -1,0 +1,178 @@
+"""C ABI checks that need no GPU: the library loads, exports every entry point
+include/moe_mlp.h declares, and validates its arguments (every error path
+returns before anything is enqueued, so fake device addresses are safe)."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+import routed_expert_mlp_amd as R
+from routed_expert_mlp_amd import capi
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x7F0000000000          # 16-byte aligned fake device address (never dereferenced)
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "moe_mlp.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\**\s*(moe_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_library_exports_every_declared_function():
+    names = header_functions()
+    assert set(names) == set(capi.EXPORTED)
+    L = R.lib()
+    for n in names:
+        assert getattr(L, n) is not None
+
+
+def test_status_strings():
+    for code, name in [(0, "MOE_MLP_OK"), (-1, "NULL_ARG"), (-2, "BAD_SHAPE"), (-3, "BAD_TOPK"),
+                       (-4, "BAD_VALUE"), (-5, "MISALIGNED"), (-6, "WORKSPACE_TOO_SMALL"),
+                       (-7, "KIND_MISMATCH"), (-8, "ERR_HIP"), (-99, "UNKNOWN")]:
+        assert name in R.moe_mlp_status_string(code)
+
+
+def cfg(**kw):
+    base = dict(kind=0, hidden=256, moe_intermediate=128, num_experts=16, top_k=4, n_shared_experts=1,
+                shared_intermediate=128, dense_intermediate=0, routed_scaling_factor=2.5, swiglu_limit=7.0)
+    base.update(kw)
+    return capi.moe_mlp_config(**base)
+
+
+def full_weights(**override):
+    names = [f[0] for f in capi.moe_mlp_weights._fields_]
+    vals = {n: FAKE + 0x100000 * i for i, n in enumerate(names)}
+    vals.update(override)
+    return capi.moe_mlp_weights(**vals)
+
+
+def ws_size(c, T, prefill):
+    n = ctypes.c_size_t(0)
+    st = R.lib().moe_mlp_workspace_size(ctypes.byref(c), T, prefill, ctypes.byref(n))
+    return st, n.value
+
+
+def call(entry, c, w, T=1, x=FAKE, out=FAKE + 0x10000, ids=None, wo=None, ws=FAKE + 0x20000, wsb=None):
+    if wsb is None:
+        st, wsb = ws_size(c, max(T, 0), entry == "moe_mlp_prefill") if c is not None else (1, 0)
+        if st:
+            wsb = 1 << 40
+    fn = getattr(R.lib(), entry)
+    return fn(ctypes.byref(c) if c is not None else None, ctypes.byref(w) if w is not None else None,
+              x, T, out, ids, wo, ws, wsb, None)
+
+
+ENTRIES = ["moe_mlp_decode", "moe_mlp_prefill"]
+
+
+@pytest.mark.parametrize("entry", ENTRIES)
+def test_null_and_kind(entry):
+    assert call(entry, None, full_weights()) == capi.ERR_NULL_ARG
+    assert call(entry, cfg(), None) == capi.ERR_NULL_ARG
+    assert call(entry, cfg(kind=7), full_weights()) == capi.ERR_BAD_VALUE
+    assert call(entry, cfg(), full_weights(), x=None) == capi.ERR_NULL_ARG
+    assert call(entry, cfg(), full_weights(), out=None) == capi.ERR_NULL_ARG
+    assert call(entry, cfg(), full_weights(), ws=None) == capi.ERR_NULL_ARG
+
+
+@pytest.mark.parametrize("entry", ENTRIES)
+@pytest.mark.parametrize("kw,code", [
+    (dict(hidden=100), capi.ERR_BAD_SHAPE), (dict(hidden=0), capi.ERR_BAD_SHAPE),
+    (dict(hidden=-32), capi.ERR_BAD_SHAPE), (dict(hidden=1 << 17), capi.ERR_BAD_SHAPE),
+    (dict(moe_intermediate=48), capi.ERR_BAD_SHAPE), (dict(shared_intermediate=40), capi.ERR_BAD_SHAPE),
+    (dict(n_shared_experts=2), capi.ERR_BAD_VALUE),
+    (dict(num_experts=0), capi.ERR_BAD_VALUE), (dict(num_experts=1025, top_k=4), capi.ERR_BAD_VALUE),
+    (dict(top_k=0), capi.ERR_BAD_TOPK), (dict(top_k=17, num_experts=64), capi.ERR_BAD_TOPK),
+    (dict(top_k=5, num_experts=4), capi.ERR_BAD_TOPK),
+    (dict(swiglu_limit=0.0), capi.ERR_BAD_VALUE), (dict(swiglu_limit=-1.0), capi.ERR_BAD_VALUE),
+    (dict(swiglu_limit=math.nan), capi.ERR_BAD_VALUE), (dict(swiglu_limit=math.inf), capi.ERR_BAD_VALUE),
+    (dict(routed_scaling_factor=0.0), capi.ERR_BAD_VALUE),
+    (dict(routed_scaling_factor=math.nan), capi.ERR_BAD_VALUE),
+    (dict(kind=1, dense_intermediate=0), capi.ERR_BAD_SHAPE),
+    (dict(kind=1, dense_intermediate=33), capi.ERR_BAD_SHAPE),
+])
+def test_config_validation(entry, kw, code):
+    assert call(entry, cfg(**kw), full_weights()) == code
+    assert ws_size(cfg(**kw), 1, entry == "moe_mlp_prefill")[0] == code
+
+
+def test_token_count_limits():
+    assert call("moe_mlp_decode", cfg(), full_weights(), T=-1) == capi.ERR_BAD_SHAPE
+    assert call("moe_mlp_decode", cfg(), full_weights(), T=capi.DECODE_MAX_T + 1) == capi.ERR_BAD_SHAPE
+    assert ws_size(cfg(), capi.DECODE_MAX_T + 1, 1)[0] == capi.OK
+    assert ws_size(cfg(top_k=16), 1 << 27, 1)[0] == capi.ERR_BAD_SHAPE     # T*K >= 2^31
+
+
+@pytest.mark.parametrize("entry", ENTRIES)
+def test_zero_tokens_is_a_noop(entry):
+    assert call(entry, cfg(), full_weights(), T=0, x=None, out=None, ws=None, wsb=0) == capi.OK
+
+
+@pytest.mark.parametrize("entry", ENTRIES)
+@pytest.mark.parametrize("missing", ["router_w", "router_bias", "w13_q", "w13_s", "w13_g", "w2_q", "w2_s",
+                                     "w2_g", "shared_w13", "shared_w2"])
+def test_missing_weights(entry, missing):
+    assert call(entry, cfg(), full_weights(**{missing: None})) == capi.ERR_KIND_MISMATCH
+
+
+@pytest.mark.parametrize("entry", ENTRIES)
+def test_weights_per_kind(entry):
+    # no shared expert: its tensors are not needed
+    assert call(entry, cfg(n_shared_experts=0), full_weights(shared_w13=None, shared_w2=None),
+                wsb=0) == capi.ERR_WORKSPACE_TOO_SMALL
+    dense = cfg(kind=1, dense_intermediate=512)
+    assert call(entry, dense, full_weights(dense_w2=None)) == capi.ERR_KIND_MISMATCH
+    assert call(entry, dense, full_weights(router_w=None, w13_q=None), wsb=0) == capi.ERR_WORKSPACE_TOO_SMALL
+
+
+@pytest.mark.parametrize("entry", ENTRIES)
+def test_alignment(entry):
+    assert call(entry, cfg(), full_weights(), x=FAKE + 8) == capi.ERR_MISALIGNED
+    assert call(entry, cfg(), full_weights(), out=FAKE + 2) == capi.ERR_MISALIGNED
+    assert call(entry, cfg(), full_weights(w13_q=FAKE + 4)) == capi.ERR_MISALIGNED
+    assert call(entry, cfg(), full_weights(), ids=FAKE + 4) == capi.ERR_MISALIGNED
+
+
+@pytest.mark.parametrize("entry", ENTRIES)
+def test_workspace_too_small(entry):
+    st, need = ws_size(cfg(), 5, entry == "moe_mlp_prefill")
+    assert st == 0 and need > 0
+    assert call(entry, cfg(), full_weights(), T=5, wsb=need - 1) == capi.ERR_WORKSPACE_TOO_SMALL
+
+
+def test_workspace_grows_with_tokens():
+    for pf in (0, 1):
+        sizes = [ws_size(cfg(), T, pf)[1] for T in (1, 2, 16, 64, 256)]
+        assert sizes == sorted(sizes) and sizes[0] > 0
+    assert ws_size(cfg(), 1, 0)[0] == capi.OK
+    n = ctypes.c_size_t(0)
+    assert R.lib().moe_mlp_workspace_size(ctypes.byref(cfg()), 1, 0, None) == capi.ERR_NULL_ARG
+
+
+def test_router_topk_validation():
+    L = R.lib()
+    c = cfg()
+    assert L.moe_router_topk(ctypes.byref(c), None, FAKE, FAKE, 4, FAKE, FAKE, FAKE, 1 << 30, None) == capi.ERR_NULL_ARG
+    assert L.moe_router_topk(ctypes.byref(cfg(top_k=20)), FAKE, FAKE, FAKE, 4, FAKE, FAKE, FAKE, 1 << 30,
+                             None) == capi.ERR_BAD_TOPK
+    assert L.moe_router_topk(ctypes.byref(cfg(kind=1, dense_intermediate=64)), FAKE, FAKE, FAKE, 4, FAKE, FAKE,
+                             FAKE, 1 << 30, None) == capi.ERR_KIND_MISMATCH
+    assert L.moe_router_topk(ctypes.byref(c), FAKE, FAKE, FAKE, 4, FAKE, FAKE, FAKE, 16, None) == \
+        capi.ERR_WORKSPACE_TOO_SMALL
+    assert L.moe_router_topk(ctypes.byref(c), FAKE, FAKE, FAKE, 0, None, None, None, 0, None) == capi.OK
+
+
+def test_dequant_validation():
+    L = R.lib()
+    assert L.moe_nvfp4_dequant(None, FAKE, 1.0, 4, 64, FAKE, None, None) == capi.ERR_NULL_ARG
+    assert L.moe_nvfp4_dequant(FAKE, FAKE, 1.0, 4, 64, None, None, None) == capi.ERR_NULL_ARG
+    assert L.moe_nvfp4_dequant(FAKE, FAKE, 1.0, 4, 48, FAKE, None, None) == capi.ERR_BAD_SHAPE
+    assert L.moe_nvfp4_dequant(FAKE, FAKE, 1.0, -1, 64, FAKE, None, None) == capi.ERR_BAD_SHAPE
+    assert L.moe_nvfp4_dequant(FAKE, FAKE, math.inf, 4, 64, FAKE, None, None) == capi.ERR_BAD_VALUE
+    assert L.moe_nvfp4_dequant(FAKE + 4, FAKE, 1.0, 4, 64, FAKE, None, None) == capi.ERR_MISALIGNED
+    assert L.moe_nvfp4_dequant(FAKE, FAKE + 1, 1.0, 4, 64, FAKE, None, None) == capi.ERR_MISALIGNED
+    assert L.moe_nvfp4_dequant(FAKE, FAKE, 1.0, 0, 64, FAKE, None, None) == capi.OK

@@ -1,0 +1,200 @@
+"""GPU parity, level 4 (plus ids/weights from the layer calls): moe_mlp_decode
+and moe_mlp_prefill through the C ABI against the fp64 oracle in contract
+mode, on the same seeded inputs.
+
+Tolerance: rel-L2 <= 5e-3 and max-abs <= 1e-2 * max|ref| for the bf16 output;
+ids bit-exact; weights within 1e-6 relative.  Full-size workloads compare
+every token's ids/weights and a sample of tokens' outputs (the oracle computes
+those one by one); the others compare everything.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import synth
+from gpu_util import (DEV, DeviceRouted, assert_output_close, assert_router_close, bf16_dev, bf16_host_bits,
+                      config_of, device_workload, rel_l2, say)
+from inputs import RoutedInputs
+from routed_expert_mlp_amd import capi
+
+pytestmark = pytest.mark.gpu
+
+
+def _sample(T, n, seed=0):
+    if T <= n:
+        return np.arange(T)
+    rng = np.random.default_rng(seed)
+    s = np.sort(rng.choice(T, size=n, replace=False))
+    s[0], s[-1] = 0, T - 1                  # always the first and the last token
+    return np.unique(s)
+
+
+def _check_layer(d: DeviceRouted, prefill: bool, n_sample: int, what: str):
+    w = d.w
+    say(f"[case] {what}: {'prefill' if prefill else 'decode'} T={w.T} H={w.H} I={w.I} E={w.E} K={w.K}")
+    out, ids, wts = d.run(prefill)
+    torch.cuda.synchronize()
+    ids_ref, w_ref, _, _ = O.route(O.decode_bf16(d.inp.x), d.inp.router_w, d.inp.router_bias, w.K, w.rsf)
+    assert_router_close(ids.cpu().numpy(), wts.cpu().numpy(), ids_ref, w_ref, what)
+    toks = _sample(w.T, n_sample)
+    ref, _, _ = d.inp.oracle(tokens=toks)
+    assert_output_close(bf16_host_bits(out)[toks], ref, f"{what} ({len(toks)} of {w.T} tokens)")
+    return out
+
+
+DECODE = [("tiny_decode", 1), ("ragged_decode", 200), ("flash_decode_t1", 1), ("flash_decode_t16", 6),
+          ("flash_decode_t64", 5), ("skewed_decode_t64_k16", 5), ("flash_decode_t16_literal_bias", 5),
+          ("flash_decode_t64_literal_bias", 4)]
+
+
+@pytest.mark.parametrize("name,n_sample", DECODE, ids=[d[0] for d in DECODE])
+def test_decode_parity(name, n_sample):
+    _check_layer(device_workload(name), False, n_sample, name)
+
+
+PREFILL = [("ragged_prefill", 1000), ("prefill_t4096", 8), ("prefill_t4096_literal_bias", 6)]
+
+
+@pytest.mark.parametrize("name,n_sample", PREFILL, ids=[p[0] for p in PREFILL])
+def test_prefill_parity(name, n_sample):
+    _check_layer(device_workload(name), True, n_sample, name)
+
+
+def test_decode_and_prefill_agree_on_every_token():
+    """Two different kernel paths (GEMV vs MFMA grouped GEMM) on the same 64 tokens."""
+    d = device_workload("flash_decode_t64")
+    a, ida, wa = d.run(False)
+    b, idb, wb = d.run(True)
+    torch.cuda.synchronize()
+    assert torch.equal(ida, idb)
+    assert torch.allclose(wa, wb, rtol=1e-6, atol=0)
+    r = rel_l2(a.float().cpu().numpy(), b.float().cpu().numpy())
+    say(f"[parity] decode vs prefill (64 tokens): rel_l2={r:.3e}")
+    assert r < 5e-3
+
+
+def test_prefill_matches_decode_on_a_token_subset():
+    """Tokens are independent: prefill over 4096 tokens equals decode of any subset (within tolerance)."""
+    d = device_workload("prefill_t4096")
+    out, ids, _ = d.run(True)
+    sub = torch.arange(0, 4096, 16, device=DEV)[:256]
+    o2, ids2, _ = d.run(False, x=d.x[sub].contiguous())
+    torch.cuda.synchronize()
+    assert torch.equal(ids[sub], ids2)
+    r = rel_l2(out[sub].float().cpu().numpy(), o2.float().cpu().numpy())
+    say(f"[parity] prefill vs decode on 256 sampled tokens: rel_l2={r:.3e}")
+    assert r < 5e-3
+
+
+@pytest.mark.parametrize("prefill", [False, True])
+def test_runs_are_bitwise_deterministic(prefill):
+    d = device_workload("flash_decode_t64")
+    a = d.run(prefill)
+    b = d.run(prefill)
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x.view(torch.int8) if x.dtype == torch.bfloat16 else x,
+                           y.view(torch.int8) if y.dtype == torch.bfloat16 else y)
+
+
+def test_concurrent_streams_equal_solo():
+    d = device_workload("flash_decode_t64")
+    solo_d = d.run(False)[0]
+    solo_p = d.run(True)[0]
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    with torch.cuda.stream(s1):
+        c_d = d.run(False, stream=s1)[0]
+    with torch.cuda.stream(s2):
+        c_p = d.run(True, stream=s2)[0]
+    torch.cuda.synchronize()
+    assert torch.equal(solo_d.view(torch.int16), c_d.view(torch.int16))
+    assert torch.equal(solo_p.view(torch.int16), c_p.view(torch.int16))
+
+
+# ---------------------------------------------------------------------------
+# Edge cases (tiny shapes, full oracle).
+# ---------------------------------------------------------------------------
+
+def _fresh(name, prefill, n_sample=64, w13_g=None, w2_g=None, **overrides):
+    w = synth.workload(name, **overrides)
+    d = DeviceRouted(RoutedInputs(w), w13_g=w13_g, w2_g=w2_g)
+    return _check_layer(d, prefill, n_sample, f"{name} {overrides or ''}")
+
+
+@pytest.mark.parametrize("prefill", [False, True])
+def test_top_k_equals_e_at_the_kernel_limit(prefill):
+    _fresh("tiny_decode", prefill, T=8, K=16)
+
+
+@pytest.mark.parametrize("prefill", [False, True])
+def test_single_expert(prefill):
+    _fresh("tiny_decode", prefill, T=5, E=1, K=1)
+
+
+@pytest.mark.parametrize("prefill", [False, True])
+def test_no_shared_expert(prefill):
+    _fresh("tiny_decode", prefill, T=7, Is=0)
+
+
+@pytest.mark.parametrize("prefill", [False, True])
+def test_global_scales(prefill):
+    E = 16
+    g13 = np.stack([np.full(E, 0.75), np.full(E, 2.0 ** -3)], axis=1).astype(np.float32)
+    g2 = np.linspace(0.5, 2.0, E).astype(np.float32)
+    _fresh("tiny_decode", prefill, T=9, w13_g=g13, w2_g=g2)
+
+
+@pytest.mark.parametrize("prefill", [False, True])
+def test_minimum_hidden_size(prefill):
+    _fresh("tiny_decode", prefill, T=3, H=32, I=32, Is=32)
+
+
+def test_decode_maximum_tokens():
+    _fresh("ragged_decode", False, n_sample=256, T=capi.DECODE_MAX_T)
+
+
+def test_prefill_one_token():
+    _fresh("tiny_decode", True, T=1)
+
+
+@pytest.mark.parametrize("prefill", [False, True])
+def test_zero_tokens(prefill):
+    d = device_workload("tiny_decode")
+    x = torch.empty((0, d.w.H), dtype=torch.bfloat16, device=DEV)
+    out = torch.empty((0, d.w.H), dtype=torch.bfloat16, device=DEV)
+    fn = capi.moe_mlp_prefill if prefill else capi.moe_mlp_decode
+    fn(d.cfg, d.weights, x, out)
+
+
+# ---------------------------------------------------------------------------
+# Dense FFN variant.
+# ---------------------------------------------------------------------------
+
+def _dense(name, prefill, n_sample, **overrides):
+    w = synth.workload(name, **overrides)
+    say(f"[case] dense {name} {'prefill' if prefill else 'decode'} T={w.T} H={w.H} Id={w.Id}")
+    x = synth.x_rows(w)
+    w13, w2 = synth.dense_w13(w), synth.dense_w2(w)
+    cfg = config_of(w)
+    wt = capi.Weights(dense_w13=bf16_dev(w13), dense_w2=bf16_dev(w2))
+    out = torch.empty((w.T, w.H), dtype=torch.bfloat16, device=DEV)
+    (capi.moe_mlp_prefill if prefill else capi.moe_mlp_decode)(cfg, wt, bf16_dev(x), out)
+    torch.cuda.synchronize()
+    toks = _sample(w.T, n_sample)
+    ref = O.dense_ffn(x, w13, w2, w.swiglu_limit, tokens=toks)
+    assert_output_close(bf16_host_bits(out)[toks], ref, f"dense {name} T={w.T}")
+
+
+@pytest.mark.parametrize("prefill", [False, True])
+def test_dense_ragged(prefill):
+    _dense("ragged_dense_prefill", prefill, 300, T=256 if not prefill else 300)
+
+
+def test_dense_prefill_full_size():
+    _dense("dense_prefill_t4096", True, 6)
+
+
+def test_dense_decode_full_width():
+    _dense("dense_prefill_t4096", False, 4, T=4)
