@@ -158,6 +158,31 @@ int moe_mlp_prefill(const moe_mlp_config* cfg, const moe_mlp_weights* w, const u
                     void* workspace, size_t ws_bytes, void* stream);
 
 /*
+ * Measurement entry: exactly the kernels of moe_mlp_decode (prefill == 0) or
+ * moe_mlp_prefill (prefill != 0) on `stream`, with stage i's start event
+ * events[2i] attached to the dispatch of the stage's first kernel and its
+ * stop event events[2i+1] to the completion of its last kernel
+ * (hipExtLaunchKernelGGL), so hipEventElapsedTime(events[2i], events[2i+1])
+ * is the stage's kernel execution time as a kernel trace reports it.
+ * `events` is a HOST array of n_events caller-created hipEvent_t handles
+ * (none NULL); n_events >= 2 * n_stages, else MOE_MLP_ERR_BAD_VALUE.
+ * Stages (moe_mlp_stage_name): ROUTED one-token decode (T == 1, H <= 4096,
+ * I and Is <= 2048) logits_shared_gateup, topk, routed_gateup, down_combine;
+ * other ROUTED decode router_logits, topk_bucket, shared_gateup,
+ * routed_gateup, shared_down, routed_down, combine; ROUTED prefill
+ * router_logits, topk, permute, routed_gateup, routed_down, shared_gateup,
+ * shared_down, combine; DENSE dense_gateup, dense_down.  A stage with
+ * nothing to run (no shared expert) records both events back to back.
+ */
+int moe_mlp_forward_profiled(const moe_mlp_config* cfg, const moe_mlp_weights* w, const uint16_t* x,
+                             int64_t T, uint16_t* out, int32_t* ids_out, float* w_out, void* workspace,
+                             size_t ws_bytes, void* stream, int prefill, void* const* events, int n_events);
+
+/* Name of stage `stage` of the decode (prefill == 0) or prefill form for the
+ * config and token count T (static string), or NULL past the last stage. */
+const char* moe_mlp_stage_name(const moe_mlp_config* cfg, int64_t T, int prefill, int stage);
+
+/*
  * Router alone (test entry): logits = x . router_w^T (fp32), sigmoid scores,
  * top-K of score + bias, weights = rsf * score / sum of chosen scores.
  * Uses cfg->kind == ROUTED fields hidden, num_experts, top_k and

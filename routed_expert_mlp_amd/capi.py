@@ -35,8 +35,8 @@ DECODE_MAX_T = 256
 KIND_ROUTED = 0
 KIND_DENSE = 1
 
-EXPORTED = ("moe_mlp_workspace_size", "moe_mlp_decode", "moe_mlp_prefill", "moe_router_topk",
-            "moe_nvfp4_dequant", "moe_mlp_status_string")
+EXPORTED = ("moe_mlp_workspace_size", "moe_mlp_decode", "moe_mlp_prefill", "moe_mlp_forward_profiled",
+            "moe_mlp_stage_name", "moe_router_topk", "moe_nvfp4_dequant", "moe_mlp_status_string")
 
 
 class MoeMlpError(RuntimeError):
@@ -73,11 +73,17 @@ def lib() -> ctypes.CDLL:
         L.moe_mlp_workspace_size.argtypes = [cfgp, i64, ctypes.c_int, ctypes.POINTER(sz)]
         for f in (L.moe_mlp_decode, L.moe_mlp_prefill):
             f.argtypes = [cfgp, wp, vp, i64, vp, vp, vp, vp, sz, vp]
+        L.moe_mlp_forward_profiled.argtypes = [cfgp, wp, vp, i64, vp, vp, vp, vp, sz, vp, ctypes.c_int,
+                                               ctypes.POINTER(vp), ctypes.c_int]
+        L.moe_mlp_forward_profiled.restype = ctypes.c_int
+        L.moe_mlp_stage_name.argtypes = [cfgp, i64, ctypes.c_int, ctypes.c_int]
+        L.moe_mlp_stage_name.restype = ctypes.c_char_p
         L.moe_router_topk.argtypes = [cfgp, vp, vp, vp, i64, vp, vp, vp, sz, vp]
         L.moe_nvfp4_dequant.argtypes = [vp, vp, ctypes.c_float, i64, i64, vp, vp, vp]
         L.moe_mlp_status_string.argtypes = [ctypes.c_int]
         L.moe_mlp_status_string.restype = ctypes.c_char_p
-        for n in EXPORTED[:-1]:
+        for n in ("moe_mlp_workspace_size", "moe_mlp_decode", "moe_mlp_prefill", "moe_router_topk",
+                  "moe_nvfp4_dequant"):
             getattr(L, n).restype = ctypes.c_int
         _LIB = L
     return _LIB
@@ -220,6 +226,38 @@ def moe_mlp_decode(cfg: Config, w: Weights, x: torch.Tensor, out: torch.Tensor, 
 def moe_mlp_prefill(cfg: Config, w: Weights, x: torch.Tensor, out: torch.Tensor, ids_out=None, w_out=None,
                     ws: Optional[torch.Tensor] = None, stream=None) -> None:
     _layer("moe_mlp_prefill", cfg, w, x, out, ids_out, w_out, ws, stream, prefill=True)
+
+
+def moe_mlp_stage_name(cfg: Config, T: int, prefill: bool, stage: int) -> Optional[str]:
+    r = lib().moe_mlp_stage_name(ctypes.byref(cfg.c()), int(T), int(bool(prefill)), int(stage))
+    return None if r is None else r.decode()
+
+
+def stage_names(cfg: Config, T: int, prefill: bool):
+    names = []
+    while True:
+        n = moe_mlp_stage_name(cfg, T, prefill, len(names))
+        if n is None:
+            return names
+        names.append(n)
+
+
+def moe_mlp_forward_profiled(cfg: Config, w: Weights, x: torch.Tensor, out: torch.Tensor, prefill: bool,
+                             events, ids_out=None, w_out=None, ws: Optional[torch.Tensor] = None,
+                             stream=None) -> None:
+    """As moe_mlp_decode / moe_mlp_prefill, with stage i's kernels bracketed by the raw
+    hipEvent_t handles events[2i] (start) and events[2i+1] (stop)."""
+    T = x.shape[0]
+    _check_tensor(x, "x", (T, cfg.hidden), torch.bfloat16)
+    _check_tensor(out, "out", (T, cfg.hidden), torch.bfloat16)
+    w.check(cfg)
+    if ws is None:
+        ws = workspace(cfg, T, prefill, x.device)
+    ev = (ctypes.c_void_p * len(events))(*events)
+    st = lib().moe_mlp_forward_profiled(ctypes.byref(cfg.c()), ctypes.byref(w.c()), x.data_ptr(), T,
+                                        out.data_ptr(), _ptr(ids_out), _ptr(w_out), ws.data_ptr(), ws.numel(),
+                                        _stream(stream), int(bool(prefill)), ev, len(events))
+    _check(st, "moe_mlp_forward_profiled")
 
 
 def moe_router_topk(cfg: Config, router_w: torch.Tensor, router_bias: torch.Tensor, x: torch.Tensor,

@@ -98,10 +98,72 @@ __device__ __forceinline__ void e2m1x8_scaled_bf16(uint32_t codes, float scale, 
   out4[3] = pack_bf16x2(d.x * scale, d.y * scale);
 }
 
-__device__ __forceinline__ float wave_sum(float v) {
+// Lane permutes within rows of 16 lanes (DPP): a few cycles each, unlike
+// __shfl_xor, which goes through the LDS crossbar.
+template <int CTRL>
+__device__ __forceinline__ int dpp_mov(int v) {
+  return __builtin_amdgcn_mov_dpp(v, CTRL, 0xF, 0xF, true);
+}
+constexpr int DPP_QUAD_1032 = 0xB1;      // quad_perm [1,0,3,2]
+constexpr int DPP_QUAD_2301 = 0x4E;      // quad_perm [2,3,0,1]
+constexpr int DPP_ROW_HALF_MIRROR = 0x141;
+constexpr int DPP_ROW_MIRROR = 0x140;
+
+// Keep (v, i, a) of the larger v; on equal v the smaller i.
+__device__ __forceinline__ void argmax_take(float& v, int& i, float& a, float ov, int oi, float oa) {
+  const bool take = (ov > v) || (ov == v && oi < i);
+  v = take ? ov : v;
+  i = take ? oi : i;
+  a = take ? oa : a;
+}
+
+template <int CTRL>
+__device__ __forceinline__ void argmax_dpp_step(float& v, int& i, float& a) {
+  const float ov = __int_as_float(dpp_mov<CTRL>(__float_as_int(v)));
+  const int oi = dpp_mov<CTRL>(i);
+  const float oa = __int_as_float(dpp_mov<CTRL>(__float_as_int(a)));
+  argmax_take(v, i, a, ov, oi, oa);
+}
+
+// Wave-wide argmax of (v, i) (larger v, then smaller i), carrying a; every
+// lane returns the winner.  All 64 lanes must be active.
+__device__ __forceinline__ void wave_argmax(float& v, int& i, float& a) {
+  argmax_dpp_step<DPP_QUAD_1032>(v, i, a);
+  argmax_dpp_step<DPP_QUAD_2301>(v, i, a);
+  argmax_dpp_step<DPP_ROW_HALF_MIRROR>(v, i, a);
+  argmax_dpp_step<DPP_ROW_MIRROR>(v, i, a);      // every lane now holds its row's winner
+  float bv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  int bi = __builtin_amdgcn_readlane(i, 0);
+  float ba = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(a), 0));
 #pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, WAVE);
-  return v;
+  for (int r = 1; r < 4; ++r) {
+    const float ov = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16 * r));
+    const int oi = __builtin_amdgcn_readlane(i, 16 * r);
+    const float oa = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(a), 16 * r));
+    argmax_take(bv, bi, ba, ov, oi, oa);
+  }
+  v = bv;
+  i = bi;
+  a = ba;
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_add(float v) {
+  return v + __int_as_float(dpp_mov<CTRL>(__float_as_int(v)));
+}
+
+// Sum over the 64 lanes; every lane returns the same bits (each step adds a
+// commutative pair).  All 64 lanes must be active.
+__device__ __forceinline__ float wave_sum(float v) {
+  v = dpp_add<DPP_QUAD_1032>(v);
+  v = dpp_add<DPP_QUAD_2301>(v);
+  v = dpp_add<DPP_ROW_HALF_MIRROR>(v);
+  v = dpp_add<DPP_ROW_MIRROR>(v);
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return (r0 + r1) + (r2 + r3);
 }
 
 // SiLU(min(g, L)) * clamp(u, -L, L): the asymmetric clamped SwiGLU.

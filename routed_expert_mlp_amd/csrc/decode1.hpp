@@ -1,0 +1,267 @@
+// One-token decode ("Module glm5next_mlp", modules: forward -- the GLM MLP
+// decode forward, one token).  Four launches stream every weight byte once:
+//
+//   1. k_dec_logits_shared: router logits (fp32 rows of gate.weight) and the
+//      BF16 shared expert's gate/up + clamped SwiGLU, both of which only need
+//      x, in one grid;
+//   2. k_topk (router.hpp): one wavefront picks the K largest biased scores
+//      by K wavefront argmax rounds (DPP lane permutes), weights renormalised
+//      over the chosen unbiased scores, times rsf ("Traps": bias steers
+//      selection only);
+//   3. k_dec_gateup: routed NVFP4 gate/up rows of the K chosen experts +
+//      clamped SwiGLU -> h (bf16);
+//   4. k_dec_down_combine: routed NVFP4 down rows of all K experts, the BF16
+//      shared down rows, and the combine out = bf16(shared + sum_k w_k y_k)
+//      for a block of output rows (fixed k order).
+//
+// Each wavefront issues all loads of its rows before using any of them, so a
+// wavefront has its whole share of the weight stream in flight at once.
+#pragma once
+
+#include "common.hpp"
+#include "gemv.hpp"
+
+namespace moe {
+
+// Lane l of a wavefront covers chunks l, l+64, ..., of a row (one coalesced
+// 1 KB load per instruction); a chunk is 16 bytes.
+
+// -------------------------------------------------------------------------
+// 1. logits + shared gate/up.  Blocks [0, n_logit_blocks) take 4 router rows
+// each (one per wavefront), the rest take 4 shared (gate, up) row pairs.
+//   NR: float4 chunks per lane of a router row (>= H / 256)
+//   NS: 8-bf16 chunks per lane of a shared row (>= H / 512)
+// -------------------------------------------------------------------------
+template <int NR, int NS>
+__global__ __launch_bounds__(256) void k_dec_logits_shared(const uint16_t* __restrict__ x,
+                                                           const float* __restrict__ wr, float* __restrict__ logits,
+                                                           int E, int H, const uint16_t* __restrict__ sw13, int Is,
+                                                           uint16_t* __restrict__ hs, float L, int n_logit_blocks) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  if (static_cast<int>(blockIdx.x) < n_logit_blocks) {
+    const int e = blockIdx.x * 4 + wv;
+    if (e >= E) return;
+    const float4* row = reinterpret_cast<const float4*>(wr + static_cast<int64_t>(e) * H);
+    const uint2* xv = reinterpret_cast<const uint2*>(x);
+    float4 w[NR];
+    uint2 xs[NR];
+    const int nch = H >> 2;
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+      const int c = lane + 64 * i;
+      w[i] = c < nch ? row[c] : make_float4(0, 0, 0, 0);
+      xs[i] = c < nch ? xv[c] : make_uint2(0, 0);
+    }
+    float acc = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+      acc = fmaf(__uint_as_float(xs[i].x << 16), w[i].x, acc);
+      acc = fmaf(__uint_as_float(xs[i].x & 0xffff0000u), w[i].y, acc);
+      acc = fmaf(__uint_as_float(xs[i].y << 16), w[i].z, acc);
+      acc = fmaf(__uint_as_float(xs[i].y & 0xffff0000u), w[i].w, acc);
+    }
+    acc = wave_sum(acc);
+    if (lane == 0) logits[e] = acc;
+  } else {
+    const int j = (blockIdx.x - n_logit_blocks) * 4 + wv;
+    if (j >= Is) return;
+    const uint4* g = reinterpret_cast<const uint4*>(sw13 + static_cast<int64_t>(j) * H);
+    const uint4* u = reinterpret_cast<const uint4*>(sw13 + static_cast<int64_t>(Is + j) * H);
+    const uint4* xv = reinterpret_cast<const uint4*>(x);
+    const int nch = H >> 3;
+    uint4 wg[NS], wu[NS], xs[NS];
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+      const int c = lane + 64 * i;
+      const bool ok = c < nch;
+      wg[i] = ok ? g[c] : make_uint4(0, 0, 0, 0);
+      wu[i] = ok ? u[c] : make_uint4(0, 0, 0, 0);
+      xs[i] = ok ? xv[c] : make_uint4(0, 0, 0, 0);
+    }
+    float ag = 0.0f, au = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+      const uint32_t xp[4] = {xs[i].x, xs[i].y, xs[i].z, xs[i].w};
+      ag = dot2_bf16(wg[i].x, xp[0], ag); ag = dot2_bf16(wg[i].y, xp[1], ag);
+      ag = dot2_bf16(wg[i].z, xp[2], ag); ag = dot2_bf16(wg[i].w, xp[3], ag);
+      au = dot2_bf16(wu[i].x, xp[0], au); au = dot2_bf16(wu[i].y, xp[1], au);
+      au = dot2_bf16(wu[i].z, xp[2], au); au = dot2_bf16(wu[i].w, xp[3], au);
+    }
+    ag = wave_sum(ag);
+    au = wave_sum(au);
+    if (lane == 0) hs[j] = f32_to_bf16(swiglu_clamped(ag, au, L));
+  }
+}
+
+// -------------------------------------------------------------------------
+// 3. routed gate/up for one token.  Grid (I / (4*RJ), K): block (jb, k) runs
+// gate rows j = (jb*4 + wave)*RJ .. +RJ and the up rows I + j of expert
+// ids[k].  Lane l covers the 16-byte chunks l, l+64, ... (NC of them) of each
+// row, so every load instruction reads 1 KB contiguous.
+// -------------------------------------------------------------------------
+template <int RJ, int NC>
+__global__ __launch_bounds__(256) void k_dec_gateup(const uint16_t* __restrict__ x, const uint8_t* __restrict__ q13,
+                                                    const uint8_t* __restrict__ s13, const float* __restrict__ g13,
+                                                    const int32_t* __restrict__ ids, int E, int H, int I, float L,
+                                                    uint16_t* __restrict__ h) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int k = blockIdx.y;
+  const int e = min(max(ids[k], 0), E - 1);
+  const int j0 = (blockIdx.x * 4 + wv) * RJ;
+  if (j0 >= I) return;
+  const int64_t rq = H >> 1, rs = H >> 4;                 // code / scale bytes per row
+  const uint8_t* qe = q13 + static_cast<int64_t>(e) * 2 * I * rq;
+  const uint8_t* se = s13 + static_cast<int64_t>(e) * 2 * I * rs;
+  const int nch = H >> 5;
+  uint4 cg[RJ][NC], cu[RJ][NC];
+  uint32_t sg[RJ][NC], su[RJ][NC];
+#pragma unroll
+  for (int r = 0; r < RJ; ++r) {
+    const int j = min(j0 + r, I - 1);
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
+      const int c = lane + 64 * i;
+      const bool ok = c < nch;
+      cg[r][i] = ok ? *reinterpret_cast<const uint4*>(qe + j * rq + 16 * c) : make_uint4(0, 0, 0, 0);
+      cu[r][i] = ok ? *reinterpret_cast<const uint4*>(qe + (I + j) * rq + 16 * c) : make_uint4(0, 0, 0, 0);
+      sg[r][i] = ok ? *reinterpret_cast<const uint16_t*>(se + j * rs + 2 * c) : 0u;
+      su[r][i] = ok ? *reinterpret_cast<const uint16_t*>(se + (I + j) * rs + 2 * c) : 0u;
+    }
+  }
+  float ag[RJ], au[RJ];
+#pragma unroll
+  for (int r = 0; r < RJ; ++r) {
+    ag[r] = 0.0f;
+    au[r] = 0.0f;
+  }
+#pragma unroll
+  for (int i = 0; i < NC; ++i) {
+    const int c = lane + 64 * i;
+    uint32_t xp[16];
+    const uint4* xv = reinterpret_cast<const uint4*>(x + 32 * c);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint4 v = c < nch ? xv[q] : make_uint4(0, 0, 0, 0);
+      xp[4 * q] = v.x; xp[4 * q + 1] = v.y; xp[4 * q + 2] = v.z; xp[4 * q + 3] = v.w;
+    }
+#pragma unroll
+    for (int r = 0; r < RJ; ++r) {
+      ag[r] = nvfp4_chunk_dot(cg[r][i], sg[r][i], xp, ag[r]);
+      au[r] = nvfp4_chunk_dot(cu[r][i], su[r][i], xp, au[r]);
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < RJ; ++r) {
+    ag[r] = wave_sum(ag[r]);
+    au[r] = wave_sum(au[r]);
+  }
+  if (lane < RJ) {
+    float gg = ag[0], uu = au[0];
+#pragma unroll
+    for (int r = 1; r < RJ; ++r)
+      if (lane == r) {
+        gg = ag[r];
+        uu = au[r];
+      }
+    const int j = j0 + lane;
+    if (j < I)
+      h[static_cast<int64_t>(k) * I + j] =
+          f32_to_bf16(swiglu_clamped(g13[2 * e] * gg, g13[2 * e + 1] * uu, L));
+  }
+}
+
+// -------------------------------------------------------------------------
+// 4. down + combine for one token.  Block b owns output rows
+// r0 = b*R .. +R and has KW >= K wavefronts: wavefront k streams those R rows
+// of expert ids[k]'s NVFP4 down projection against its h_k (one 16-byte
+// chunk per lane, lanes < I/32, h_k chunk in registers), and the shared
+// expert's BF16 down rows r0 + w, r0 + w + KW, ... are spread over all KW
+// wavefronts.  Per-row partials meet in LDS and thread r writes
+// out[r0+r] = bf16(ys + sum_k (w_k * g2_k) * acc_k), k in order.
+// -------------------------------------------------------------------------
+template <int R, int KW, int NS>
+__global__ __launch_bounds__(KW * 64) void k_dec_down_combine(
+    const uint16_t* __restrict__ h, const uint16_t* __restrict__ hs, const uint8_t* __restrict__ q2,
+    const uint8_t* __restrict__ s2, const float* __restrict__ g2, const uint16_t* __restrict__ sw2,
+    const int32_t* __restrict__ ids, const float* __restrict__ wts, int E, int K, int H, int I, int Is,
+    uint16_t* __restrict__ out) {
+  constexpr int SR = (R + KW - 1) / KW;             // shared rows per wavefront
+  __shared__ float part[KW + 1][R];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int r0 = blockIdx.x * R;
+  const bool routed = wv < K;
+  const int e = routed ? min(max(ids[wv], 0), E - 1) : 0;
+  const int64_t rq = I >> 1, rs = I >> 4;
+  const bool act = routed && lane < (I >> 5);
+  uint4 cw[R];
+  uint32_t sc[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int64_t base = static_cast<int64_t>(e) * H + min(r0 + r, H - 1);
+    cw[r] = act ? *reinterpret_cast<const uint4*>(q2 + base * rq + 16 * lane) : make_uint4(0, 0, 0, 0);
+    sc[r] = act ? *reinterpret_cast<const uint16_t*>(s2 + base * rs + 2 * lane) : 0u;
+  }
+  const int nsc = Is >> 3;                           // 8-bf16 chunks per shared row
+  uint4 shw[SR][NS];
+#pragma unroll
+  for (int r = 0; r < SR; ++r) {
+    const int rr = wv + KW * r;                      // row within the block
+    const int row = min(r0 + rr, H - 1);
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+      const int c = lane + 64 * i;
+      shw[r][i] = (rr < R && c < nsc) ? reinterpret_cast<const uint4*>(sw2 + static_cast<int64_t>(row) * Is)[c]
+                                      : make_uint4(0, 0, 0, 0);
+    }
+  }
+  uint32_t xp[16];
+  {
+    const uint4* hp = reinterpret_cast<const uint4*>(h + static_cast<int64_t>(wv) * I + 32 * lane);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint4 v = act ? hp[q] : make_uint4(0, 0, 0, 0);
+      xp[4 * q] = v.x; xp[4 * q + 1] = v.y; xp[4 * q + 2] = v.z; xp[4 * q + 3] = v.w;
+    }
+  }
+  uint32_t hsp[NS][4];
+#pragma unroll
+  for (int i = 0; i < NS; ++i) {
+    const int c = lane + 64 * i;
+    const uint4 v = c < nsc ? reinterpret_cast<const uint4*>(hs)[c] : make_uint4(0, 0, 0, 0);
+    hsp[i][0] = v.x; hsp[i][1] = v.y; hsp[i][2] = v.z; hsp[i][3] = v.w;
+  }
+  float acc[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    acc[r] = fmaf(e2m1x16_dot(cw[r].x, cw[r].y, xp), e4m3_to_f32<0>(sc[r]), 0.0f);
+    acc[r] = fmaf(e2m1x16_dot(cw[r].z, cw[r].w, xp + 8), e4m3_to_f32<1>(sc[r]), acc[r]);
+  }
+  float accs[SR];
+#pragma unroll
+  for (int r = 0; r < SR; ++r) {
+    accs[r] = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NS; ++i) accs[r] = bf16_chunk_dot(shw[r][i], hsp[i], accs[r]);
+  }
+#pragma unroll
+  for (int r = 0; r < R; ++r) acc[r] = wave_sum(acc[r]);
+#pragma unroll
+  for (int r = 0; r < SR; ++r) accs[r] = wave_sum(accs[r]);
+  if (lane == 0) {
+    const float wk = routed ? wts[wv] * g2[e] : 0.0f;
+#pragma unroll
+    for (int r = 0; r < R; ++r) part[wv][r] = wk * acc[r];
+#pragma unroll
+    for (int r = 0; r < SR; ++r)
+      if (wv + KW * r < R) part[KW][wv + KW * r] = accs[r];
+  }
+  __syncthreads();
+  const int t = threadIdx.x;
+  if (t < R && r0 + t < H) {
+    float o = part[KW][t];
+    for (int k = 0; k < K; ++k) o += part[k][t];
+    out[r0 + t] = f32_to_bf16(o);
+  }
+}
+
+}  // namespace moe

@@ -3,6 +3,7 @@
 // enqueued), workspace layout, and the launch sequences of the decode and
 // prefill forms.  The library allocates nothing, never synchronises, and
 // keeps no state between calls.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -11,6 +12,7 @@
 
 #include "../../include/moe_mlp.h"
 #include "common.hpp"
+#include "decode1.hpp"
 #include "gemm.hpp"
 #include "gemv.hpp"
 #include "permute.hpp"
@@ -139,53 +141,74 @@ int validate_weights(const moe_mlp_config* c, const moe_mlp_weights* w) {
 
 int launch_status() { return hipGetLastError() == hipSuccess ? MOE_MLP_OK : MOE_MLP_ERR_HIP; }
 
+// Stage timing: a stage's start event is attached to its first kernel's
+// dispatch packet and its stop event to its last (hipExtLaunchKernelGGL), so
+// the interval is the kernels' own execution, as a kernel trace reports it.
+// Null events give an ordinary launch.
+struct Ev {
+  hipEvent_t a = nullptr, b = nullptr;
+};
+
+template <typename F, typename... Args>
+void launch(F kernel, dim3 grid, dim3 block, hipStream_t s, hipEvent_t e0, hipEvent_t e1, Args... args) {
+  hipExtLaunchKernelGGL(kernel, grid, block, 0, s, e0, e1, 0, args...);
+}
+
 template <int NJ>
 void launch_topk_bucket(const float* logits, const float* bias, int T, int E, int K, float rsf, int32_t* ids,
-                        float* wts, int32_t* ids_out, float* w_out, Groups g, hipStream_t s) {
-  k_topk_bucket<NJ><<<1, 1024, 0, s>>>(logits, bias, T, E, K, rsf, ids, wts, ids_out, w_out, g);
+                        float* wts, int32_t* ids_out, float* w_out, Groups g, hipStream_t s, Ev ev) {
+  launch(k_topk_bucket<NJ>, dim3(1), dim3(1024), s, ev.a, ev.b, logits, bias, T, E, K, rsf, ids, wts, ids_out,
+         w_out, g);
 }
 
 void topk_bucket(int E, const float* logits, const float* bias, int T, int K, float rsf, int32_t* ids,
-                 float* wts, int32_t* ids_out, float* w_out, Groups g, hipStream_t s) {
+                 float* wts, int32_t* ids_out, float* w_out, Groups g, hipStream_t s, Ev ev) {
   const int nj = static_cast<int>(cdiv(E, 64));
-  if (nj <= 1) launch_topk_bucket<1>(logits, bias, T, E, K, rsf, ids, wts, ids_out, w_out, g, s);
-  else if (nj <= 2) launch_topk_bucket<2>(logits, bias, T, E, K, rsf, ids, wts, ids_out, w_out, g, s);
-  else if (nj <= 4) launch_topk_bucket<4>(logits, bias, T, E, K, rsf, ids, wts, ids_out, w_out, g, s);
-  else if (nj <= 8) launch_topk_bucket<8>(logits, bias, T, E, K, rsf, ids, wts, ids_out, w_out, g, s);
-  else launch_topk_bucket<16>(logits, bias, T, E, K, rsf, ids, wts, ids_out, w_out, g, s);
+  if (nj <= 1) launch_topk_bucket<1>(logits, bias, T, E, K, rsf, ids, wts, ids_out, w_out, g, s, ev);
+  else if (nj <= 2) launch_topk_bucket<2>(logits, bias, T, E, K, rsf, ids, wts, ids_out, w_out, g, s, ev);
+  else if (nj <= 4) launch_topk_bucket<4>(logits, bias, T, E, K, rsf, ids, wts, ids_out, w_out, g, s, ev);
+  else if (nj <= 8) launch_topk_bucket<8>(logits, bias, T, E, K, rsf, ids, wts, ids_out, w_out, g, s, ev);
+  else launch_topk_bucket<16>(logits, bias, T, E, K, rsf, ids, wts, ids_out, w_out, g, s, ev);
+}
+
+template <int NJ>
+void launch_topk(const float* logits, const float* bias, int T, int E, int K, float rsf, int32_t* ids, float* wts,
+                 int32_t* ids_out, float* w_out, hipStream_t s, Ev ev) {
+  launch(k_topk<NJ>, dim3(static_cast<unsigned>(cdiv(T, 4))), dim3(256), s, ev.a, ev.b, logits, bias, T, E, K,
+         rsf, ids, wts, ids_out, w_out);
 }
 
 void topk_tokens(int E, const float* logits, const float* bias, int T, int K, float rsf, int32_t* ids,
-                 float* wts, int32_t* ids_out, float* w_out, hipStream_t s) {
+                 float* wts, int32_t* ids_out, float* w_out, hipStream_t s, Ev ev) {
   const int nj = static_cast<int>(cdiv(E, 64));
-  const dim3 grid(static_cast<unsigned>(cdiv(T, 4)));
-  if (nj <= 1) k_topk<1><<<grid, 256, 0, s>>>(logits, bias, T, E, K, rsf, ids, wts, ids_out, w_out);
-  else if (nj <= 2) k_topk<2><<<grid, 256, 0, s>>>(logits, bias, T, E, K, rsf, ids, wts, ids_out, w_out);
-  else if (nj <= 4) k_topk<4><<<grid, 256, 0, s>>>(logits, bias, T, E, K, rsf, ids, wts, ids_out, w_out);
-  else if (nj <= 8) k_topk<8><<<grid, 256, 0, s>>>(logits, bias, T, E, K, rsf, ids, wts, ids_out, w_out);
-  else k_topk<16><<<grid, 256, 0, s>>>(logits, bias, T, E, K, rsf, ids, wts, ids_out, w_out);
+  if (nj <= 1) launch_topk<1>(logits, bias, T, E, K, rsf, ids, wts, ids_out, w_out, s, ev);
+  else if (nj <= 2) launch_topk<2>(logits, bias, T, E, K, rsf, ids, wts, ids_out, w_out, s, ev);
+  else if (nj <= 4) launch_topk<4>(logits, bias, T, E, K, rsf, ids, wts, ids_out, w_out, s, ev);
+  else if (nj <= 8) launch_topk<8>(logits, bias, T, E, K, rsf, ids, wts, ids_out, w_out, s, ev);
+  else launch_topk<16>(logits, bias, T, E, K, rsf, ids, wts, ids_out, w_out, s, ev);
 }
 
-void router_logits(const uint16_t* x, const float* wr, float* logits, int64_t T, int H, int E, hipStream_t s) {
+void router_logits(const uint16_t* x, const float* wr, float* logits, int64_t T, int H, int E, hipStream_t s,
+                   Ev ev) {
   if (T <= 16) {
-    k_logits_gemv<<<E, 256, 0, s>>>(x, wr, logits, static_cast<int>(T), H, E);
+    launch(k_logits_gemv, dim3(E), dim3(256), s, ev.a, ev.b, x, wr, logits, static_cast<int>(T), H, E);
   } else {
     const dim3 grid(static_cast<unsigned>(cdiv(T, 64)), static_cast<unsigned>(cdiv(E, 64)));
-    k_logits_gemm<<<grid, 256, 0, s>>>(x, wr, logits, static_cast<int>(T), H, E);
+    launch(k_logits_gemm, grid, dim3(256), s, ev.a, ev.b, x, wr, logits, static_cast<int>(T), H, E);
   }
 }
 
 template <bool NVFP4, int MODE, int RW>
-void gemv(const GemvArgs& a, int groups, hipStream_t s) {
+void gemv(const GemvArgs& a, int groups, hipStream_t s, Ev ev) {
   const dim3 grid(static_cast<unsigned>(cdiv(a.half_rows, 4 * RW)), static_cast<unsigned>(groups));
-  k_gemv<NVFP4, MODE, RW><<<grid, 256, 0, s>>>(a);
+  launch(k_gemv<NVFP4, MODE, RW>, grid, dim3(256), s, ev.a, ev.b, a);
 }
 
 template <bool NVFP4, int MODE, bool ROUTED>
-void gemm(const GemmArgs& a, int64_t m_tiles, hipStream_t s) {
+void gemm(const GemmArgs& a, int64_t m_tiles, hipStream_t s, Ev ev) {
   const int nb = MODE == GEMM_GATEUP ? 128 : 256;
   const dim3 grid(static_cast<unsigned>(m_tiles), static_cast<unsigned>(cdiv(a.half_n, nb)));
-  k_gemm<NVFP4, MODE, ROUTED><<<grid, 256, 0, s>>>(a);
+  launch(k_gemm<NVFP4, MODE, ROUTED>, grid, dim3(256), s, ev.a, ev.b, a);
 }
 
 GemvArgs bf16_gemv_args(const uint16_t* w, int half_rows, int cols, int T, const uint16_t* in, void* out,
@@ -217,10 +240,80 @@ GemmArgs bf16_gemm_args(const uint16_t* act, int kdim, const uint16_t* w, int ha
   return a;
 }
 
+const char* const kDecodeStages[] = {"router_logits", "topk_bucket", "shared_gateup", "routed_gateup",
+                                    "shared_down", "routed_down", "combine"};
+const char* const kDecode1Stages[] = {"logits_shared_gateup", "topk", "routed_gateup", "down_combine"};
+const char* const kPrefillStages[] = {"router_logits", "topk", "permute", "routed_gateup", "routed_down",
+                                     "shared_gateup", "shared_down", "combine"};
+const char* const kDenseStages[] = {"dense_gateup", "dense_down"};
+
+// The one-token decode kernels hold a row's chunks in registers: they take
+// H <= 4096 and I, Is <= 2048.
+constexpr int kDec1MaxH = 4096;
+
+int dec1_kw(int K) { return K <= 4 ? 4 : K <= 8 ? 8 : 16; }
+
+bool decode1_ok(const moe_mlp_config* c, int64_t T, int prefill) {
+  if (prefill || T != 1 || c->kind != MOE_MLP_KIND_ROUTED) return false;
+  const int Is = c->n_shared_experts ? c->shared_intermediate : 0;
+  return c->hidden <= kDec1MaxH && c->moe_intermediate <= 2048 && Is <= 2048;
+}
+
+int n_stages(const moe_mlp_config* c, int64_t T, int prefill) {
+  if (c->kind == MOE_MLP_KIND_DENSE) return 2;
+  if (decode1_ok(c, T, prefill)) return 4;
+  return prefill ? 8 : 7;
+}
+
+template <int KW, int NS>
+void launch_down_combine(const uint16_t* h, const uint16_t* hs, const moe_mlp_weights* w, const int32_t* ids,
+                         const float* wts, int E, int K, int H, int I, int Is, uint16_t* out, hipStream_t s, Ev ev) {
+  constexpr int R = 8;
+  launch(k_dec_down_combine<R, KW, NS>, dim3(static_cast<unsigned>(cdiv(H, R))), dim3(KW * 64), s, ev.a, ev.b, h,
+         hs, w->w2_q, w->w2_s, w->w2_g, w->shared_w2, ids, wts, E, K, H, I, Is, out);
+}
+
+template <int KW>
+void launch_down_combine_ns(const uint16_t* h, const uint16_t* hs, const moe_mlp_weights* w, const int32_t* ids,
+                            const float* wts, int E, int K, int H, int I, int Is, uint16_t* out, hipStream_t s,
+                            Ev ev) {
+  const int ns = static_cast<int>(cdiv(Is / 8, 64));
+  if (ns <= 1) launch_down_combine<KW, 1>(h, hs, w, ids, wts, E, K, H, I, Is, out, s, ev);
+  else if (ns <= 2) launch_down_combine<KW, 2>(h, hs, w, ids, wts, E, K, H, I, Is, out, s, ev);
+  else launch_down_combine<KW, 4>(h, hs, w, ids, wts, E, K, H, I, Is, out, s, ev);
+}
+
+// One-token decode: 4 launches (see decode1.hpp).
+void decode1(const moe_mlp_config* c, const moe_mlp_weights* w, const uint16_t* x, uint16_t* out,
+             int32_t* ids_out, float* w_out, float* logits, int32_t* ids, float* wts, uint16_t* h, uint16_t* hs,
+             hipStream_t s, Ev e0, Ev e1, Ev e2, Ev e3) {
+  const int H = c->hidden, E = c->num_experts, K = c->top_k, I = c->moe_intermediate;
+  const int Is = c->n_shared_experts ? c->shared_intermediate : 0;
+  const float L = c->swiglu_limit;
+  const int nlb = static_cast<int>(cdiv(E, 4)), nsb = static_cast<int>(cdiv(Is, 4));
+  launch(k_dec_logits_shared<16, 8>, dim3(nlb + nsb), dim3(256), s, e0.a, e0.b, x, w->router_w, logits, E, H,
+         w->shared_w13, Is, hs, L, nlb);
+  topk_tokens(E, logits, w->router_bias, 1, K, c->routed_scaling_factor, ids, wts, ids_out, w_out, s, e1);
+  constexpr int RJ = 4;
+  const dim3 g3(static_cast<unsigned>(cdiv(I, 4 * RJ)), static_cast<unsigned>(K));
+  if ((H >> 5) <= 64)
+    launch(k_dec_gateup<RJ, 1>, g3, dim3(256), s, e2.a, e2.b, x, w->w13_q, w->w13_s, w->w13_g,
+           static_cast<const int32_t*>(ids), E, H, I, L, h);
+  else
+    launch(k_dec_gateup<RJ, 2>, g3, dim3(256), s, e2.a, e2.b, x, w->w13_q, w->w13_s, w->w13_g,
+           static_cast<const int32_t*>(ids), E, H, I, L, h);
+  const int kw = dec1_kw(K);
+  if (kw == 4) launch_down_combine_ns<4>(h, hs, w, ids, wts, E, K, H, I, Is, out, s, e3);
+  else if (kw == 8) launch_down_combine_ns<8>(h, hs, w, ids, wts, E, K, H, I, Is, out, s, e3);
+  else launch_down_combine_ns<16>(h, hs, w, ids, wts, E, K, H, I, Is, out, s, e3);
+}
+
 int run_layer(const moe_mlp_config* c, const moe_mlp_weights* w, const uint16_t* x, int64_t T, uint16_t* out,
-              int32_t* ids_out, float* w_out, void* ws, size_t ws_bytes, void* stream, int prefill) {
+              int32_t* ids_out, float* w_out, void* ws, size_t ws_bytes, void* stream, int prefill,
+              void* const* events = nullptr, int n_events = 0) {
   int st = validate_cfg(c, T, prefill);
   if (st) return st;
+  if (events && n_events < 2 * n_stages(c, T, prefill)) return MOE_MLP_ERR_BAD_VALUE;
   if (T == 0) return MOE_MLP_OK;
   if ((st = validate_weights(c, w))) return st;
   if (!x || !out || !ws) return MOE_MLP_ERR_NULL_ARG;
@@ -233,17 +326,32 @@ int run_layer(const moe_mlp_config* c, const moe_mlp_weights* w, const uint16_t*
   const int H = c->hidden;
   const float L = c->swiglu_limit;
   const int Ti = static_cast<int>(T);
+  // Stage i's (start, stop) events, or none.
+  auto ev = [&](int i) {
+    Ev e;
+    if (events) {
+      e.a = static_cast<hipEvent_t>(events[2 * i]);
+      e.b = static_cast<hipEvent_t>(events[2 * i + 1]);
+    }
+    return e;
+  };
+  auto empty_stage = [&](Ev e) {   // nothing to run: a zero-length interval
+    if (e.a) {
+      (void)hipEventRecord(e.a, s);
+      (void)hipEventRecord(e.b, s);
+    }
+  };
 
   if (c->kind == MOE_MLP_KIND_DENSE) {
     const int Id = c->dense_intermediate;
     uint16_t* h = at<uint16_t>(ws, p.h);
     if (prefill) {
       const int64_t mt = cdiv(T, GM_BM);
-      gemm<false, GEMM_GATEUP, false>(bf16_gemm_args(x, H, w->dense_w13, Id, Ti, h, Id, L), mt, s);
-      gemm<false, GEMM_DOWN_BF16, false>(bf16_gemm_args(h, Id, w->dense_w2, H, Ti, out, H, L), mt, s);
+      gemm<false, GEMM_GATEUP, false>(bf16_gemm_args(x, H, w->dense_w13, Id, Ti, h, Id, L), mt, s, ev(0));
+      gemm<false, GEMM_DOWN_BF16, false>(bf16_gemm_args(h, Id, w->dense_w2, H, Ti, out, H, L), mt, s, ev(1));
     } else {
-      gemv<false, GEMV_GATEUP, 2>(bf16_gemv_args(w->dense_w13, Id, H, Ti, x, h, L), 1, s);
-      gemv<false, GEMV_DOWN_BF16, 2>(bf16_gemv_args(w->dense_w2, H, Id, Ti, h, out, L), 1, s);
+      gemv<false, GEMV_GATEUP, 2>(bf16_gemv_args(w->dense_w13, Id, H, Ti, x, h, L), 1, s, ev(0));
+      gemv<false, GEMV_DOWN_BF16, 2>(bf16_gemv_args(w->dense_w2, H, Id, Ti, h, out, L), 1, s, ev(1));
     }
     return launch_status();
   }
@@ -258,15 +366,21 @@ int run_layer(const moe_mlp_config* c, const moe_mlp_weights* w, const uint16_t*
   uint16_t* hs = Is ? at<uint16_t>(ws, p.hs) : nullptr;
   float* ys = Is ? at<float>(ws, p.ys) : nullptr;
   const int64_t S = T * K;
+  const float rsf = c->routed_scaling_factor;
 
-  router_logits(x, w->router_w, logits, T, H, E, s);
+  if (decode1_ok(c, T, prefill)) {
+    decode1(c, w, x, out, ids_out, w_out, logits, ids, wts, h, hs, s, ev(0), ev(1), ev(2), ev(3));
+    return launch_status();
+  }
+  router_logits(x, w->router_w, logits, T, H, E, s, ev(0));
   if (prefill) {
-    topk_tokens(E, logits, w->router_bias, Ti, K, c->routed_scaling_factor, ids, wts, ids_out, w_out, s);
+    topk_tokens(E, logits, w->router_bias, Ti, K, rsf, ids, wts, ids_out, w_out, s, ev(1));
     Perm pm{at<int32_t>(ws, p.count), at<int32_t>(ws, p.offset), at<int32_t>(ws, p.perm),
             at<int32_t>(ws, p.n_tiles), at<int32_t>(ws, p.tile_e), at<int32_t>(ws, p.tile_m0)};
-    k_expert_count<<<E, 256, 0, s>>>(ids, static_cast<int>(S), pm);
-    k_schedule<<<1, 1024, 0, s>>>(E, GM_BM, pm);
-    k_expert_scatter<<<E, 256, 0, s>>>(ids, static_cast<int>(S), pm);
+    const Ev pe = ev(2);
+    launch(k_expert_count, dim3(E), dim3(256), s, pe.a, nullptr, ids, static_cast<int>(S), pm);
+    launch(k_schedule, dim3(1), dim3(1024), s, nullptr, nullptr, E, GM_BM, pm);
+    launch(k_expert_scatter, dim3(E), dim3(256), s, nullptr, pe.b, ids, static_cast<int>(S), pm);
     GemmArgs g{};
     g.n_tiles = pm.n_tiles;
     g.tile_expert = pm.tile_expert;
@@ -288,7 +402,7 @@ int run_layer(const moe_mlp_config* c, const moe_mlp_weights* w, const uint16_t*
     gu.half_n = I;
     gu.out = h;
     gu.ldo = I;
-    gemm<true, GEMM_GATEUP, true>(gu, p.max_tiles, s);
+    gemm<true, GEMM_GATEUP, true>(gu, p.max_tiles, s, ev(3));
     // routed down -> y (slot rows)
     GemmArgs gd = g;
     gd.a = h;
@@ -301,18 +415,22 @@ int run_layer(const moe_mlp_config* c, const moe_mlp_weights* w, const uint16_t*
     gd.half_n = H;
     gd.out = y;
     gd.ldo = H;
-    gemm<true, GEMM_DOWN_SLOT_F32, true>(gd, p.max_tiles, s);
+    gemm<true, GEMM_DOWN_SLOT_F32, true>(gd, p.max_tiles, s, ev(4));
+    const int64_t mt = cdiv(T, GM_BM);
     if (Is) {
-      const int64_t mt = cdiv(T, GM_BM);
-      gemm<false, GEMM_GATEUP, false>(bf16_gemm_args(x, H, w->shared_w13, Is, Ti, hs, Is, L), mt, s);
-      gemm<false, GEMM_DOWN_F32, false>(bf16_gemm_args(hs, Is, w->shared_w2, H, Ti, ys, H, L), mt, s);
+      gemm<false, GEMM_GATEUP, false>(bf16_gemm_args(x, H, w->shared_w13, Is, Ti, hs, Is, L), mt, s, ev(5));
+      gemm<false, GEMM_DOWN_F32, false>(bf16_gemm_args(hs, Is, w->shared_w2, H, Ti, ys, H, L), mt, s, ev(6));
+    } else {
+      empty_stage(ev(5));
+      empty_stage(ev(6));
     }
   } else {
     Groups gr{at<int32_t>(ws, p.g_n), at<int32_t>(ws, p.g_expert), at<int32_t>(ws, p.g_count),
               at<int32_t>(ws, p.g_offset), at<int32_t>(ws, p.g_slots)};
-    topk_bucket(E, logits, w->router_bias, Ti, K, c->routed_scaling_factor, ids, wts, ids_out, w_out, gr, s);
+    topk_bucket(E, logits, w->router_bias, Ti, K, rsf, ids, wts, ids_out, w_out, gr, s, ev(1));
     const int groups = static_cast<int>(S < E ? S : E);
-    if (Is) gemv<false, GEMV_GATEUP, 1>(bf16_gemv_args(w->shared_w13, Is, H, Ti, x, hs, L), 1, s);
+    if (Is) gemv<false, GEMV_GATEUP, 1>(bf16_gemv_args(w->shared_w13, Is, H, Ti, x, hs, L), 1, s, ev(2));
+    else empty_stage(ev(2));
     GemvArgs r{};
     r.n_groups = gr.n_groups;
     r.g_expert = gr.expert;
@@ -332,8 +450,9 @@ int run_layer(const moe_mlp_config* c, const moe_mlp_weights* w, const uint16_t*
     gu.cols = H;
     gu.in = x;
     gu.out = h;
-    gemv<true, GEMV_GATEUP, 2>(gu, groups, s);
-    if (Is) gemv<false, GEMV_DOWN_F32, 2>(bf16_gemv_args(w->shared_w2, H, Is, Ti, hs, ys, L), 1, s);
+    gemv<true, GEMV_GATEUP, 2>(gu, groups, s, ev(3));
+    if (Is) gemv<false, GEMV_DOWN_F32, 2>(bf16_gemv_args(w->shared_w2, H, Is, Ti, hs, ys, L), 1, s, ev(4));
+    else empty_stage(ev(4));
     GemvArgs gd = r;
     gd.wq = w->w2_q;
     gd.ws = w->w2_s;
@@ -344,10 +463,13 @@ int run_layer(const moe_mlp_config* c, const moe_mlp_weights* w, const uint16_t*
     gd.cols = I;
     gd.in = h;
     gd.out = y;
-    gemv<true, GEMV_DOWN_F32, 4>(gd, groups, s);
+    gemv<true, GEMV_DOWN_F32, 4>(gd, groups, s, ev(5));
   }
   const int64_t nq = T * (H / 4);
-  k_combine<<<static_cast<unsigned>(cdiv(nq, 256)), 256, 0, s>>>(y, ys, wts, Ti, K, H, out);
+  const Ev ce = ev(prefill ? 7 : 6);
+  launch(k_combine, dim3(static_cast<unsigned>(cdiv(nq, 256))), dim3(256), s, ce.a, ce.b,
+         static_cast<const float*>(y), static_cast<const float*>(ys), static_cast<const float*>(wts), Ti, K, H,
+         out);
   return launch_status();
 }
 
@@ -375,6 +497,24 @@ int moe_mlp_prefill(const moe_mlp_config* cfg, const moe_mlp_weights* w, const u
   return run_layer(cfg, w, x, T, out, ids_out, w_out, workspace, ws_bytes, stream, 1);
 }
 
+int moe_mlp_forward_profiled(const moe_mlp_config* cfg, const moe_mlp_weights* w, const uint16_t* x, int64_t T,
+                             uint16_t* out, int32_t* ids_out, float* w_out, void* workspace, size_t ws_bytes,
+                             void* stream, int prefill, void* const* events, int n_events) {
+  if (!events) return MOE_MLP_ERR_NULL_ARG;
+  for (int i = 0; i < n_events; ++i)
+    if (!events[i]) return MOE_MLP_ERR_NULL_ARG;
+  return run_layer(cfg, w, x, T, out, ids_out, w_out, workspace, ws_bytes, stream, prefill ? 1 : 0, events,
+                   n_events);
+}
+
+const char* moe_mlp_stage_name(const moe_mlp_config* cfg, int64_t T, int prefill, int stage) {
+  if (!cfg || stage < 0) return nullptr;
+  if (cfg->kind == MOE_MLP_KIND_DENSE) return stage < 2 ? kDenseStages[stage] : nullptr;
+  if (decode1_ok(cfg, T, prefill)) return stage < 4 ? kDecode1Stages[stage] : nullptr;
+  if (prefill) return stage < 8 ? kPrefillStages[stage] : nullptr;
+  return stage < 7 ? kDecodeStages[stage] : nullptr;
+}
+
 int moe_router_topk(const moe_mlp_config* cfg, const float* router_w, const float* router_bias,
                     const uint16_t* x, int64_t T, int32_t* ids, float* w, void* workspace, size_t ws_bytes,
                     void* stream) {
@@ -390,9 +530,9 @@ int moe_router_topk(const moe_mlp_config* cfg, const float* router_w, const floa
   if (ws_bytes < p.total) return MOE_MLP_ERR_WORKSPACE_TOO_SMALL;
   hipStream_t s = static_cast<hipStream_t>(stream);
   float* logits = at<float>(workspace, p.logits);
-  router_logits(x, router_w, logits, T, cfg->hidden, cfg->num_experts, s);
+  router_logits(x, router_w, logits, T, cfg->hidden, cfg->num_experts, s, Ev{});
   topk_tokens(cfg->num_experts, logits, router_bias, static_cast<int>(T), cfg->top_k,
-              cfg->routed_scaling_factor, ids, w, nullptr, nullptr, s);
+              cfg->routed_scaling_factor, ids, w, nullptr, nullptr, s, Ev{});
   return launch_status();
 }
 

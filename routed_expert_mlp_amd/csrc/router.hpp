@@ -178,17 +178,7 @@ __device__ __forceinline__ void topk_wave(const float* __restrict__ lrow, const 
         be = e;
       }
     }
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) {
-      const float ob = __shfl_xor(best, m, 64);
-      const float os = __shfl_xor(bs, m, 64);
-      const int oe = __shfl_xor(be, m, 64);
-      if (ob > best || (ob == best && oe < be)) {
-        best = ob;
-        bs = os;
-        be = oe;
-      }
-    }
+    wave_argmax(best, be, bs);
     if ((be & 63) == lane) taken |= 1u << (be >> 6);
     if (lane == k) {
       my_id = be;

@@ -198,3 +198,37 @@ def test_dense_prefill_full_size():
 
 def test_dense_decode_full_width():
     _dense("dense_prefill_t4096", False, 4, T=4)
+
+
+def test_single_token_general_path():
+    """I > 2048 takes the general decode kernels at T=1 (not the one-token path)."""
+    _fresh("tiny_decode", False, T=1, I=2080)
+
+
+@pytest.mark.parametrize("name,prefill", [("flash_decode_t1", False), ("flash_decode_t16", False),
+                                          ("ragged_prefill", True)])
+def test_profiled_entry_matches_plain_call(name, prefill):
+    import ctypes
+    d = device_workload(name)
+    out, ids, wts = d.run(prefill)
+    names = capi.stage_names(d.cfg, d.w.T, prefill)
+    hip = ctypes.CDLL("libamdhip64.so.7")
+    evs = []
+    for _ in range(2 * len(names)):
+        e = ctypes.c_void_p()
+        assert hip.hipEventCreate(ctypes.byref(e)) == 0
+        evs.append(e.value)
+    out2 = torch.empty_like(out)
+    capi.moe_mlp_forward_profiled(d.cfg, d.weights, d.x, out2, prefill, evs)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
+    times = []
+    for i in range(len(names)):
+        ms = ctypes.c_float()
+        assert hip.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(evs[2 * i]),
+                                       ctypes.c_void_p(evs[2 * i + 1])) == 0
+        times.append(ms.value)
+        hip.hipEventDestroy(ctypes.c_void_p(evs[2 * i]))
+        hip.hipEventDestroy(ctypes.c_void_p(evs[2 * i + 1]))
+    say(f"[stages] {name}: " + ", ".join(f"{n}={t * 1e3:.1f}us" for n, t in zip(names, times)))
+    assert all(t >= 0 for t in times) and sum(times) > 0
