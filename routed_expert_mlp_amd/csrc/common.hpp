@@ -173,6 +173,12 @@ __device__ __forceinline__ float swiglu_clamped(float g, float u, float L) {
   return g / (1.0f + expf(-g)) * u;
 }
 
+// s_waitcnt immediate that waits until at most n vector-memory operations are
+// outstanding (expcnt and lgkmcnt left unconstrained).
+__host__ __device__ constexpr int waitcnt_vm(int n) {
+  return (n & 0xF) | (0x7 << 4) | (0xF << 8) | ((n >> 4) << 14);
+}
+
 __host__ __device__ __forceinline__ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 }  // namespace moe

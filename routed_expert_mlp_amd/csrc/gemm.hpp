@@ -25,6 +25,8 @@
 
 #include "common.hpp"
 
+#include <type_traits>
+
 namespace moe {
 
 constexpr int GM_BM = 128;
@@ -58,6 +60,7 @@ struct GemmArgs {
   void* out;
   int ldo;
   float limit;
+  int n_blocks;              // output-column blocks (fast kernel's 1-D work mapping)
 };
 
 template <bool NVFP4, int MODE, bool ROUTED>
@@ -233,6 +236,228 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
             static_cast<uint16_t*>(a.out)[orow * a.ldo + n] = f32_to_bf16(acc[mt][nt][i]);
           else
             static_cast<float*>(a.out)[orow * a.ldo + n] = g0 * acc[mt][nt][i];
+        }
+      }
+    }
+  }
+}
+
+
+// ---------------------------------------------------------------------------
+// Fast grouped / dense GEMM (kdim % 64 == 0): v_mfma_f32_32x32x16_bf16.
+//   * workgroup tile 128 rows x 256 output columns (gate/up: 128 gate + the
+//     matching 128 up columns), 4 wavefronts of 128 x 64 (4 x 2 MFMA tiles);
+//   * A goes global -> LDS directly (global_load_lds_dwordx4) into an NST-deep
+//     ring in MFMA-fragment order: lane l of wavefront w loads 64 contiguous
+//     bytes of row 32w + l%32 at k0 + 32*(l/32);
+//   * B (NVFP4 16-byte code chunks + their 2 E4M3 scale bytes, or BF16) goes
+//     into an NST-deep register ring and is turned into bf16 operands per
+//     k-step;
+//   * the main loop is instantiated per valid 32-row m-tile count, so it has
+//     no branches;
+//   * 1-D grid, XCD-aware: block b runs on XCD b % 8, and each XCD takes a
+//     contiguous chunk of (tile, column-block) work with the column blocks of
+//     a tile back to back, so the tile's A rows stay in that XCD's L2.
+// ---------------------------------------------------------------------------
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// v_mfma_f32_32x32x16 output: lane l, element j -> row (j/4)*8 + (l/32)*4 + j%4, column l%32.
+__device__ __forceinline__ int c32_row(int lane, int j) { return (j >> 2) * 8 + (lane >> 5) * 4 + (j & 3); }
+
+template <bool NVFP4, int NST>
+struct BRing {
+  static constexpr int BW = NVFP4 ? 1 : 4;
+  uint4 b[NST][2][BW];
+  uint32_t s[NST][2];
+};
+
+template <bool NVFP4, int NST, int MTV>
+__device__ __forceinline__ void gemm_fast_mainloop(const GemmArgs& a, uint4 (&L0)[1024], uint4 (&L1)[1024],
+                                                   uint4 (&L2)[1024], uint4 (&L3)[1024], const uint16_t* arow,
+                                                   const uint8_t* bq, const uint8_t* bs, const int (&brow)[2],
+                                                   int wv, int lane, int g, int kdim, f32x16 (&acc)[4][2]) {
+  constexpr int BK = 64;
+  constexpr int BW = NVFP4 ? 1 : 4;
+  constexpr int LOADS = 4 + (NVFP4 ? 4 : 8);      // vector memory instructions per stage per lane
+  const int nkb = kdim / BK;
+  BRing<NVFP4, NST> r;
+  auto slot_lds = [&](auto slot_c) -> uint4* {
+    constexpr int SL = decltype(slot_c)::value;
+    if constexpr (SL == 0) return L0;
+    else if constexpr (SL == 1) return L1;
+    else if constexpr (SL == 2) return L2;
+    else return L3;
+  };
+  auto issue = [&](int k, auto slot_c) {
+    constexpr int SL = decltype(slot_c)::value;
+    const int kg = k * BK + 32 * g;
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(arow + kg + 8 * s),
+                                       (void __attribute__((address_space(3)))*)&slot_lds(slot_c)[(wv * 4 + s) * 64],
+                                       16, 0, 0);
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      if (NVFP4) {
+        r.b[SL][nt][0] = *reinterpret_cast<const uint4*>(bq + static_cast<int64_t>(brow[nt]) * (kdim >> 1) + (kg >> 1));
+        r.s[SL][nt] = *reinterpret_cast<const uint16_t*>(bs + static_cast<int64_t>(brow[nt]) * (kdim >> 4) + (kg >> 4));
+      } else {
+#pragma unroll
+        for (int q = 0; q < BW; ++q)
+          r.b[SL][nt][q] = *reinterpret_cast<const uint4*>(a.bb + static_cast<int64_t>(brow[nt]) * kdim + kg + 8 * q);
+      }
+    }
+  };
+  auto compute = [&](auto slot_c) {
+    constexpr int SL = decltype(slot_c)::value;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      bf16x8 af[MTV];
+#pragma unroll
+      for (int mt = 0; mt < MTV; ++mt) af[mt] = __builtin_bit_cast(bf16x8, slot_lds(slot_c)[(mt * 4 + s) * 64 + lane]);
+      bf16x8 bfrag[2];
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        uint4 v;
+        if (NVFP4) {
+          const uint4 c = r.b[SL][nt][0];
+          const uint32_t cw = s == 0 ? c.x : s == 1 ? c.y : s == 2 ? c.z : c.w;
+          const float scale = (s < 2) ? e4m3_to_f32<0>(r.s[SL][nt]) : e4m3_to_f32<1>(r.s[SL][nt]);
+          uint32_t o[4];
+          e2m1x8_scaled_bf16(cw, scale, o);
+          v = make_uint4(o[0], o[1], o[2], o[3]);
+        } else {
+          v = r.b[SL][nt][s];
+        }
+        bfrag[nt] = __builtin_bit_cast(bf16x8, v);
+      }
+#pragma unroll
+      for (int mt = 0; mt < MTV; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+          acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mt], bfrag[nt], acc[mt][nt], 0, 0, 0);
+    }
+  };
+  if (0 < nkb) issue(0, std::integral_constant<int, 0>{});
+  if (NST > 2 && 1 < nkb) issue(1, std::integral_constant<int, 1 % NST>{});
+  if (NST > 3 && 2 < nkb) issue(2, std::integral_constant<int, 2 % NST>{});
+  auto step = [&](int k, auto slot_c) {
+    constexpr int SL = decltype(slot_c)::value;
+    if (k >= nkb) return;
+    const int ahead = min(nkb - 1 - k, NST - 2);   // stages issued after k still allowed in flight
+    if (ahead >= 2) __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * LOADS));
+    else if (ahead == 1) __builtin_amdgcn_s_waitcnt(waitcnt_vm(LOADS));
+    else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    __syncthreads();
+    if (k + NST - 1 < nkb) issue(k + NST - 1, std::integral_constant<int, (SL + NST - 1) % NST>{});
+    compute(slot_c);
+  };
+  for (int k = 0; k < nkb; k += NST) {
+    step(k, std::integral_constant<int, 0>{});
+    step(k + 1, std::integral_constant<int, 1 % NST>{});
+    step(k + 2, std::integral_constant<int, 2 % NST>{});
+    if (NST == 4) step(k + 3, std::integral_constant<int, 3 % NST>{});
+  }
+}
+
+template <bool NVFP4, int MODE, bool ROUTED, int NST>
+__global__ __launch_bounds__(256, 2) void k_gemm_fast(GemmArgs a) {
+  __shared__ uint4 L0[1024];
+  __shared__ uint4 L1[1024];
+  __shared__ uint4 L2[NST > 2 ? 1024 : 1];
+  __shared__ uint4 L3[NST > 3 ? 1024 : 1];
+  // work item -> (tile, column block), XCD-aware (see above)
+  const int nbn = a.n_blocks;
+  const int ntl = ROUTED ? *a.n_tiles : static_cast<int>(cdiv(a.T, GM_BM));
+  const int total = ntl * nbn, chunk = (total + 7) >> 3;
+  const int kk = blockIdx.x >> 3;
+  if (kk >= chunk) return;
+  const int w = (blockIdx.x & 7) * chunk + kk;
+  if (w >= total) return;
+  const int tile = w / nbn, nblk = w - tile * nbn;
+  int e = 0, valid, p0;
+  if (ROUTED) {
+    e = a.tile_expert[tile];
+    const int m0 = a.tile_m0[tile];
+    valid = min(GM_BM, a.count[e] - m0);
+    p0 = a.offset[e] + m0;
+  } else {
+    p0 = tile * GM_BM;
+    valid = min(GM_BM, a.T - p0);
+  }
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int g = lane >> 5, ln = lane & 31;
+  const int kdim = a.kdim;
+  const int mt_valid = (valid + 31) >> 5;
+  const uint16_t* arow;
+  {
+    const int r0 = wv * 32 + ln;
+    const int rr = r0 < valid ? r0 : 0;                  // rows past the tile reload row 0 (outputs dropped)
+    if (ROUTED && MODE == GEMM_GATEUP) arow = a.a + static_cast<int64_t>(a.perm[p0 + rr] / a.K) * kdim;
+    else arow = a.a + static_cast<int64_t>(p0 + rr) * kdim;
+  }
+  int brow[2];
+  bool bvalid[2];
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    if (MODE == GEMM_GATEUP) {
+      const int j = nblk * 128 + wv * 32 + ln;
+      bvalid[nt] = j < a.half_n;
+      const int jj = bvalid[nt] ? j : 0;
+      brow[nt] = nt == 0 ? jj : a.half_n + jj;
+    } else {
+      const int n = nblk * 256 + wv * 64 + nt * 32 + ln;
+      bvalid[nt] = n < a.half_n;
+      brow[nt] = bvalid[nt] ? n : 0;
+    }
+  }
+  const uint8_t* bq = NVFP4 ? a.bq + e * a.stride_q : nullptr;
+  const uint8_t* bs = NVFP4 ? a.bs + e * a.stride_s : nullptr;
+  f32x16 acc[4][2];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) acc[mt][nt][j] = 0.0f;
+  switch (mt_valid) {
+    case 1: gemm_fast_mainloop<NVFP4, NST, 1>(a, L0, L1, *reinterpret_cast<uint4(*)[1024]>(&L2[0]), *reinterpret_cast<uint4(*)[1024]>(&L3[0]), arow, bq, bs, brow, wv, lane, g, kdim, acc); break;
+    case 2: gemm_fast_mainloop<NVFP4, NST, 2>(a, L0, L1, *reinterpret_cast<uint4(*)[1024]>(&L2[0]), *reinterpret_cast<uint4(*)[1024]>(&L3[0]), arow, bq, bs, brow, wv, lane, g, kdim, acc); break;
+    case 3: gemm_fast_mainloop<NVFP4, NST, 3>(a, L0, L1, *reinterpret_cast<uint4(*)[1024]>(&L2[0]), *reinterpret_cast<uint4(*)[1024]>(&L3[0]), arow, bq, bs, brow, wv, lane, g, kdim, acc); break;
+    default: gemm_fast_mainloop<NVFP4, NST, 4>(a, L0, L1, *reinterpret_cast<uint4(*)[1024]>(&L2[0]), *reinterpret_cast<uint4(*)[1024]>(&L3[0]), arow, bq, bs, brow, wv, lane, g, kdim, acc); break;
+  }
+  float g0 = 1.0f, g1 = 1.0f;
+  if (ROUTED && a.gscale) {
+    if (MODE == GEMM_GATEUP) {
+      g0 = a.gscale[2 * e];
+      g1 = a.gscale[2 * e + 1];
+    } else {
+      g0 = a.gscale[e];
+    }
+  }
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+    if (mt >= mt_valid) continue;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int row = mt * 32 + c32_row(lane, j);
+      if (row >= valid) continue;
+      if (MODE == GEMM_GATEUP) {
+        if (!bvalid[0]) continue;
+        const int jc = nblk * 128 + wv * 32 + ln;
+        static_cast<uint16_t*>(a.out)[static_cast<int64_t>(p0 + row) * a.ldo + jc] =
+            f32_to_bf16(swiglu_clamped(g0 * acc[mt][0][j], g1 * acc[mt][1][j], a.limit));
+      } else {
+        const int64_t orow = (MODE == GEMM_DOWN_SLOT_F32) ? static_cast<int64_t>(a.perm[p0 + row])
+                                                          : static_cast<int64_t>(p0 + row);
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+          if (!bvalid[nt]) continue;
+          const int n = nblk * 256 + wv * 64 + nt * 32 + ln;
+          if (MODE == GEMM_DOWN_BF16)
+            static_cast<uint16_t*>(a.out)[orow * a.ldo + n] = f32_to_bf16(acc[mt][nt][j]);
+          else
+            static_cast<float*>(a.out)[orow * a.ldo + n] = g0 * acc[mt][nt][j];
         }
       }
     }

@@ -204,11 +204,22 @@ void gemv(const GemvArgs& a, int groups, hipStream_t s, Ev ev) {
   launch(k_gemv<NVFP4, MODE, RW>, grid, dim3(256), s, ev.a, ev.b, a);
 }
 
+// Reduction lengths that are a multiple of 64 take the 32x32x16-MFMA kernel
+// (k_gemm_fast); others the general 16x16x32 kernel.
 template <bool NVFP4, int MODE, bool ROUTED>
-void gemm(const GemmArgs& a, int64_t m_tiles, hipStream_t s, Ev ev) {
-  const int nb = MODE == GEMM_GATEUP ? 128 : 256;
-  const dim3 grid(static_cast<unsigned>(m_tiles), static_cast<unsigned>(cdiv(a.half_n, nb)));
-  launch(k_gemm<NVFP4, MODE, ROUTED>, grid, dim3(256), s, ev.a, ev.b, a);
+void gemm(const GemmArgs& a0, int64_t m_tiles, hipStream_t s, Ev ev) {
+  GemmArgs a = a0;
+  if (a.kdim % 64 == 0) {
+    a.n_blocks = static_cast<int>(cdiv(a.half_n, MODE == GEMM_GATEUP ? 128 : 256));
+    const int64_t work = m_tiles * a.n_blocks;
+    const dim3 grid(static_cast<unsigned>(8 * cdiv(work, 8)));
+    constexpr int NST = NVFP4 ? 4 : 3;
+    launch(k_gemm_fast<NVFP4, MODE, ROUTED, NST>, grid, dim3(256), s, ev.a, ev.b, a);
+  } else {
+    const int nb = MODE == GEMM_GATEUP ? 128 : 256;
+    const dim3 grid(static_cast<unsigned>(m_tiles), static_cast<unsigned>(cdiv(a.half_n, nb)));
+    launch(k_gemm<NVFP4, MODE, ROUTED>, grid, dim3(256), s, ev.a, ev.b, a);
+  }
 }
 
 GemvArgs bf16_gemv_args(const uint16_t* w, int half_rows, int cols, int T, const uint16_t* in, void* out,
