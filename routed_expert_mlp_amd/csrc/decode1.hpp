@@ -1,16 +1,17 @@
 // One-token decode ("Module glm5next_mlp", modules: forward -- the GLM MLP
-// decode forward, one token).  Four launches stream every weight byte once:
+// decode forward, one token).  Three launches stream every weight byte once:
 //
 //   1. k_dec_logits_shared: router logits (fp32 rows of gate.weight) and the
 //      BF16 shared expert's gate/up + clamped SwiGLU, both of which only need
 //      x, in one grid;
-//   2. k_topk (router.hpp): one wavefront picks the K largest biased scores
-//      by K wavefront argmax rounds (DPP lane permutes), weights renormalised
-//      over the chosen unbiased scores, times rsf ("Traps": bias steers
-//      selection only);
-//   3. k_dec_gateup: routed NVFP4 gate/up rows of the K chosen experts +
-//      clamped SwiGLU -> h (bf16);
-//   4. k_dec_down_combine: routed NVFP4 down rows of all K experts, the BF16
+//   2. k_dec_gateup: every wavefront first redoes the router top-k from the
+//      E logits (K wavefront argmax rounds over DPP lane permutes; "Traps":
+//      bias steers selection only, weights are the renormalised unbiased
+//      scores times rsf) to learn which expert its block serves, then streams
+//      that expert's NVFP4 gate/up rows + clamped SwiGLU -> h (bf16).  One
+//      wavefront also writes ids and weights.  Recomputing the selection
+//      (~1 KB of logits per wavefront) is cheaper than a launch of its own;
+//   3. k_dec_down_combine: routed NVFP4 down rows of all K experts, the BF16
 //      shared down rows, and the combine out = bf16(shared + sum_k w_k y_k)
 //      for a block of output rows (fixed k order).
 //
@@ -20,6 +21,7 @@
 
 #include "common.hpp"
 #include "gemv.hpp"
+#include "router.hpp"
 
 namespace moe {
 
@@ -94,21 +96,27 @@ __global__ __launch_bounds__(256) void k_dec_logits_shared(const uint16_t* __res
 }
 
 // -------------------------------------------------------------------------
-// 3. routed gate/up for one token.  Grid (I / (4*RJ), K): block (jb, k) runs
-// gate rows j = (jb*4 + wave)*RJ .. +RJ and the up rows I + j of expert
-// ids[k].  Lane l covers the 16-byte chunks l, l+64, ... (NC of them) of each
-// row, so every load instruction reads 1 KB contiguous.
+// 2. top-k + routed gate/up for one token.  Grid (I / (4*RJ), K): block
+// (jb, k) finds the expert in slot k (topk_wave, NJ >= E / 64) and runs its
+// gate rows j = (jb*4 + wave)*RJ .. +RJ and up rows I + j.  Lane l covers the
+// 16-byte chunks l, l+64, ... (NC of them) of each row, so every load
+// instruction reads 1 KB contiguous.  Wavefront 0 of block (0, 0) runs all K
+// rounds and writes ids/wts (and ids_out/w_out when not null).
 // -------------------------------------------------------------------------
-template <int RJ, int NC>
+template <int RJ, int NC, int NJ>
 __global__ __launch_bounds__(256) void k_dec_gateup(const uint16_t* __restrict__ x, const uint8_t* __restrict__ q13,
                                                     const uint8_t* __restrict__ s13, const float* __restrict__ g13,
-                                                    const int32_t* __restrict__ ids, int E, int H, int I, float L,
-                                                    uint16_t* __restrict__ h) {
+                                                    const float* __restrict__ logits, const float* __restrict__ bias,
+                                                    int K, float rsf, int32_t* __restrict__ ids,
+                                                    float* __restrict__ wts, int32_t* ids_out, float* w_out, int E,
+                                                    int H, int I, float L, uint16_t* __restrict__ h) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int k = blockIdx.y;
-  const int e = min(max(ids[k], 0), E - 1);
   const int j0 = (blockIdx.x * 4 + wv) * RJ;
   if (j0 >= I) return;
+  const bool writer = blockIdx.x == 0 && k == 0 && wv == 0;
+  const int sel = topk_wave<NJ>(logits, bias, E, K, rsf, writer ? ids : nullptr, wts, ids_out, w_out, k);
+  const int e = min(max(sel, 0), E - 1);
   const int64_t rq = H >> 1, rs = H >> 4;                 // code / scale bytes per row
   const uint8_t* qe = q13 + static_cast<int64_t>(e) * 2 * I * rq;
   const uint8_t* se = s13 + static_cast<int64_t>(e) * 2 * I * rs;

@@ -253,7 +253,7 @@ GemmArgs bf16_gemm_args(const uint16_t* act, int kdim, const uint16_t* w, int ha
 
 const char* const kDecodeStages[] = {"router_logits", "topk_bucket", "shared_gateup", "routed_gateup",
                                     "shared_down", "routed_down", "combine"};
-const char* const kDecode1Stages[] = {"logits_shared_gateup", "topk", "routed_gateup", "down_combine"};
+const char* const kDecode1Stages[] = {"logits_shared_gateup", "topk_routed_gateup", "down_combine"};
 const char* const kPrefillStages[] = {"router_logits", "topk", "permute", "routed_gateup", "routed_down",
                                      "shared_gateup", "shared_down", "combine"};
 const char* const kDenseStages[] = {"dense_gateup", "dense_down"};
@@ -272,7 +272,7 @@ bool decode1_ok(const moe_mlp_config* c, int64_t T, int prefill) {
 
 int n_stages(const moe_mlp_config* c, int64_t T, int prefill) {
   if (c->kind == MOE_MLP_KIND_DENSE) return 2;
-  if (decode1_ok(c, T, prefill)) return 4;
+  if (decode1_ok(c, T, prefill)) return 3;
   return prefill ? 8 : 7;
 }
 
@@ -294,29 +294,44 @@ void launch_down_combine_ns(const uint16_t* h, const uint16_t* hs, const moe_mlp
   else launch_down_combine<KW, 4>(h, hs, w, ids, wts, E, K, H, I, Is, out, s, ev);
 }
 
-// One-token decode: 4 launches (see decode1.hpp).
+template <int NC, int NJ>
+void launch_dec_gateup(const moe_mlp_config* c, const moe_mlp_weights* w, const uint16_t* x, const float* logits,
+                       int32_t* ids, float* wts, int32_t* ids_out, float* w_out, uint16_t* h, hipStream_t s, Ev ev) {
+  constexpr int RJ = 4;
+  const int I = c->moe_intermediate, K = c->top_k;
+  const dim3 grid(static_cast<unsigned>(cdiv(I, 4 * RJ)), static_cast<unsigned>(K));
+  launch(k_dec_gateup<RJ, NC, NJ>, grid, dim3(256), s, ev.a, ev.b, x, w->w13_q, w->w13_s, w->w13_g, logits,
+         w->router_bias, K, c->routed_scaling_factor, ids, wts, ids_out, w_out, c->num_experts, c->hidden, I,
+         c->swiglu_limit, h);
+}
+
+template <int NC>
+void dec_gateup_nj(const moe_mlp_config* c, const moe_mlp_weights* w, const uint16_t* x, const float* logits,
+                   int32_t* ids, float* wts, int32_t* ids_out, float* w_out, uint16_t* h, hipStream_t s, Ev ev) {
+  const int nj = static_cast<int>(cdiv(c->num_experts, 64));
+  if (nj <= 1) launch_dec_gateup<NC, 1>(c, w, x, logits, ids, wts, ids_out, w_out, h, s, ev);
+  else if (nj <= 2) launch_dec_gateup<NC, 2>(c, w, x, logits, ids, wts, ids_out, w_out, h, s, ev);
+  else if (nj <= 4) launch_dec_gateup<NC, 4>(c, w, x, logits, ids, wts, ids_out, w_out, h, s, ev);
+  else if (nj <= 8) launch_dec_gateup<NC, 8>(c, w, x, logits, ids, wts, ids_out, w_out, h, s, ev);
+  else launch_dec_gateup<NC, 16>(c, w, x, logits, ids, wts, ids_out, w_out, h, s, ev);
+}
+
+// One-token decode: 3 launches (see decode1.hpp).
 void decode1(const moe_mlp_config* c, const moe_mlp_weights* w, const uint16_t* x, uint16_t* out,
              int32_t* ids_out, float* w_out, float* logits, int32_t* ids, float* wts, uint16_t* h, uint16_t* hs,
-             hipStream_t s, Ev e0, Ev e1, Ev e2, Ev e3) {
+             hipStream_t s, Ev e0, Ev e1, Ev e2) {
   const int H = c->hidden, E = c->num_experts, K = c->top_k, I = c->moe_intermediate;
   const int Is = c->n_shared_experts ? c->shared_intermediate : 0;
   const float L = c->swiglu_limit;
   const int nlb = static_cast<int>(cdiv(E, 4)), nsb = static_cast<int>(cdiv(Is, 4));
   launch(k_dec_logits_shared<16, 8>, dim3(nlb + nsb), dim3(256), s, e0.a, e0.b, x, w->router_w, logits, E, H,
          w->shared_w13, Is, hs, L, nlb);
-  topk_tokens(E, logits, w->router_bias, 1, K, c->routed_scaling_factor, ids, wts, ids_out, w_out, s, e1);
-  constexpr int RJ = 4;
-  const dim3 g3(static_cast<unsigned>(cdiv(I, 4 * RJ)), static_cast<unsigned>(K));
-  if ((H >> 5) <= 64)
-    launch(k_dec_gateup<RJ, 1>, g3, dim3(256), s, e2.a, e2.b, x, w->w13_q, w->w13_s, w->w13_g,
-           static_cast<const int32_t*>(ids), E, H, I, L, h);
-  else
-    launch(k_dec_gateup<RJ, 2>, g3, dim3(256), s, e2.a, e2.b, x, w->w13_q, w->w13_s, w->w13_g,
-           static_cast<const int32_t*>(ids), E, H, I, L, h);
+  if ((H >> 5) <= 64) dec_gateup_nj<1>(c, w, x, logits, ids, wts, ids_out, w_out, h, s, e1);
+  else dec_gateup_nj<2>(c, w, x, logits, ids, wts, ids_out, w_out, h, s, e1);
   const int kw = dec1_kw(K);
-  if (kw == 4) launch_down_combine_ns<4>(h, hs, w, ids, wts, E, K, H, I, Is, out, s, e3);
-  else if (kw == 8) launch_down_combine_ns<8>(h, hs, w, ids, wts, E, K, H, I, Is, out, s, e3);
-  else launch_down_combine_ns<16>(h, hs, w, ids, wts, E, K, H, I, Is, out, s, e3);
+  if (kw == 4) launch_down_combine_ns<4>(h, hs, w, ids, wts, E, K, H, I, Is, out, s, e2);
+  else if (kw == 8) launch_down_combine_ns<8>(h, hs, w, ids, wts, E, K, H, I, Is, out, s, e2);
+  else launch_down_combine_ns<16>(h, hs, w, ids, wts, E, K, H, I, Is, out, s, e2);
 }
 
 int run_layer(const moe_mlp_config* c, const moe_mlp_weights* w, const uint16_t* x, int64_t T, uint16_t* out,
@@ -380,7 +395,7 @@ int run_layer(const moe_mlp_config* c, const moe_mlp_weights* w, const uint16_t*
   const float rsf = c->routed_scaling_factor;
 
   if (decode1_ok(c, T, prefill)) {
-    decode1(c, w, x, out, ids_out, w_out, logits, ids, wts, h, hs, s, ev(0), ev(1), ev(2), ev(3));
+    decode1(c, w, x, out, ids_out, w_out, logits, ids, wts, h, hs, s, ev(0), ev(1), ev(2));
     return launch_status();
   }
   router_logits(x, w->router_w, logits, T, H, E, s, ev(0));
@@ -521,7 +536,7 @@ int moe_mlp_forward_profiled(const moe_mlp_config* cfg, const moe_mlp_weights* w
 const char* moe_mlp_stage_name(const moe_mlp_config* cfg, int64_t T, int prefill, int stage) {
   if (!cfg || stage < 0) return nullptr;
   if (cfg->kind == MOE_MLP_KIND_DENSE) return stage < 2 ? kDenseStages[stage] : nullptr;
-  if (decode1_ok(cfg, T, prefill)) return stage < 4 ? kDecode1Stages[stage] : nullptr;
+  if (decode1_ok(cfg, T, prefill)) return stage < 3 ? kDecode1Stages[stage] : nullptr;
   if (prefill) return stage < 8 ? kPrefillStages[stage] : nullptr;
   return stage < 7 ? kDecodeStages[stage] : nullptr;
 }

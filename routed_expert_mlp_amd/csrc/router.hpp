@@ -143,12 +143,14 @@ __global__ __launch_bounds__(256) void k_logits_gemm(const uint16_t* __restrict_
 // Top-k of one token by one wavefront.  Lane l holds experts l, l+64, ...
 // (NJ per lane, E <= 64 * NJ).  Each of K rounds takes the largest biased
 // score (exact ties: lower expert id), then the weights are the chosen
-// unbiased scores over their sum, times rsf.
+// unbiased scores over their sum, times rsf, and written to ids/wts (and
+// ids2/wts2 when not null).  Returns the id in slot `want`; with ids == null
+// nothing is written and only rounds 0..want run.
 // ---------------------------------------------------------------------------
 template <int NJ>
-__device__ __forceinline__ void topk_wave(const float* __restrict__ lrow, const float* __restrict__ bias,
-                                          int E, int K, float rsf, int32_t* ids, float* wts,
-                                          int32_t* ids2, float* wts2) {
+__device__ __forceinline__ int topk_wave(const float* __restrict__ lrow, const float* __restrict__ bias,
+                                         int E, int K, float rsf, int32_t* ids, float* wts,
+                                         int32_t* ids2, float* wts2, int want = 0) {
   const int lane = threadIdx.x & 63;
   float sel[NJ], sc[NJ];
 #pragma unroll
@@ -164,9 +166,10 @@ __device__ __forceinline__ void topk_wave(const float* __restrict__ lrow, const 
     }
   }
   uint32_t taken = 0;
-  int my_id = 0;
+  int my_id = 0, want_id = 0;
   float my_s = 0.0f, sum = 0.0f;
-  for (int k = 0; k < K; ++k) {
+  const int nr = ids ? K : want + 1;
+  for (int k = 0; k < nr; ++k) {
     float best = -INFINITY, bs = 0.0f;
     int be = 0x7fffffff;
 #pragma unroll
@@ -184,15 +187,17 @@ __device__ __forceinline__ void topk_wave(const float* __restrict__ lrow, const 
       my_id = be;
       my_s = bs;
     }
+    if (k == want) want_id = be;
     sum += bs;
   }
-  if (lane < K) {
+  if (ids && lane < K) {
     const float w = my_s / sum * rsf;
     ids[lane] = my_id;
     wts[lane] = w;
     if (ids2) ids2[lane] = my_id;
     if (wts2) wts2[lane] = w;
   }
+  return want_id;                               // wave-uniform
 }
 
 template <int NJ>

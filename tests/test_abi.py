@@ -182,24 +182,24 @@ def test_profiled_entry_validation():
     L = R.lib()
     c = cfg()
     w = full_weights()
-    n = 4                               # one-token decode stages of this config
+    n = 3                               # one-token decode stages of this config
     names = [L.moe_mlp_stage_name(ctypes.byref(c), 1, 0, i) for i in range(n + 1)]
-    assert [x.decode() for x in names[:n]] == ["logits_shared_gateup", "topk", "routed_gateup", "down_combine"]
+    assert [x.decode() for x in names[:n]] == ["logits_shared_gateup", "topk_routed_gateup", "down_combine"]
     assert names[n] is None
     assert [L.moe_mlp_stage_name(ctypes.byref(c), 2, 0, i).decode() for i in range(7)][3] == "routed_gateup"
     assert L.moe_mlp_stage_name(ctypes.byref(c), 2, 1, 8) is None
     assert L.moe_mlp_stage_name(None, 1, 0, 0) is None
-    ev_t = ctypes.c_void_p * 8
-    evs = ev_t(*[FAKE + 64 * i for i in range(8)])
+    ev_t = ctypes.c_void_p * 6
+    evs = ev_t(*[FAKE + 64 * i for i in range(6)])
     st, need = ws_size(c, 1, 0)
     f = L.moe_mlp_forward_profiled
-    assert f(ctypes.byref(c), ctypes.byref(w), FAKE, 1, FAKE, None, None, FAKE, need, None, 0, None, 8) == \
+    assert f(ctypes.byref(c), ctypes.byref(w), FAKE, 1, FAKE, None, None, FAKE, need, None, 0, None, 6) == \
         capi.ERR_NULL_ARG
-    assert f(ctypes.byref(c), ctypes.byref(w), FAKE, 1, FAKE, None, None, FAKE, need, None, 0, evs, 7) == \
+    assert f(ctypes.byref(c), ctypes.byref(w), FAKE, 1, FAKE, None, None, FAKE, need, None, 0, evs, 5) == \
         capi.ERR_BAD_VALUE
     evs[3] = None
-    assert f(ctypes.byref(c), ctypes.byref(w), FAKE, 1, FAKE, None, None, FAKE, need, None, 0, evs, 8) == \
+    assert f(ctypes.byref(c), ctypes.byref(w), FAKE, 1, FAKE, None, None, FAKE, need, None, 0, evs, 6) == \
         capi.ERR_NULL_ARG
     evs[3] = FAKE
-    assert f(ctypes.byref(c), ctypes.byref(w), FAKE, 1, FAKE, None, None, FAKE, need - 1, None, 0, evs, 8) == \
+    assert f(ctypes.byref(c), ctypes.byref(w), FAKE, 1, FAKE, None, None, FAKE, need - 1, None, 0, evs, 6) == \
         capi.ERR_WORKSPACE_TOO_SMALL
