@@ -5,7 +5,7 @@
 //      BF16 shared expert's gate/up + clamped SwiGLU, both of which only need
 //      x, in one grid;
 //   2. k_dec_gateup: every wavefront first redoes the router top-k from the
-//      E logits (K wavefront argmax rounds over DPP lane permutes; "Traps":
+//      E logits (router.hpp topk_wave, DPP wavefront max rounds; "Traps":
 //      bias steers selection only, weights are the renormalised unbiased
 //      scores times rsf) to learn which expert its block serves, then streams
 //      that expert's NVFP4 gate/up rows + clamped SwiGLU -> h (bf16).  One
@@ -115,7 +115,7 @@ __global__ __launch_bounds__(256) void k_dec_gateup(const uint16_t* __restrict__
   const int j0 = (blockIdx.x * 4 + wv) * RJ;
   if (j0 >= I) return;
   const bool writer = blockIdx.x == 0 && k == 0 && wv == 0;
-  const int sel = topk_wave<NJ>(logits, bias, E, K, rsf, writer ? ids : nullptr, wts, ids_out, w_out, k);
+  const int sel = topk_wave<NJ>(logits, bias, E, K, rsf, k, writer ? ids : nullptr, wts, ids_out, w_out);
   const int e = min(max(sel, 0), E - 1);
   const int64_t rq = H >> 1, rs = H >> 4;                 // code / scale bytes per row
   const uint8_t* qe = q13 + static_cast<int64_t>(e) * 2 * I * rq;

@@ -9,6 +9,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <type_traits>
 
 #include "../../include/moe_mlp.h"
 #include "common.hpp"
@@ -154,38 +155,37 @@ void launch(F kernel, dim3 grid, dim3 block, hipStream_t s, hipEvent_t e0, hipEv
   hipExtLaunchKernelGGL(kernel, grid, block, 0, s, e0, e1, 0, args...);
 }
 
-template <int NJ>
-void launch_topk_bucket(const float* logits, const float* bias, int T, int E, int K, float rsf, int32_t* ids,
-                        float* wts, int32_t* ids_out, float* w_out, Groups g, hipStream_t s, Ev ev) {
-  launch(k_topk_bucket<NJ>, dim3(1), dim3(1024), s, ev.a, ev.b, logits, bias, T, E, K, rsf, ids, wts, ids_out,
-         w_out, g);
+// Calls f(std::integral_constant<int, NJ>) with the smallest supported NJ >= E / 64
+// (the per-lane candidate count of the top-k wavefront).
+template <typename F>
+void with_nj(int E, F&& f) {
+  switch (static_cast<int>(cdiv(E, 64))) {
+    case 1: f(std::integral_constant<int, 1>{}); break;
+    case 2: f(std::integral_constant<int, 2>{}); break;
+    case 3: f(std::integral_constant<int, 3>{}); break;
+    case 4: f(std::integral_constant<int, 4>{}); break;
+    case 5: f(std::integral_constant<int, 5>{}); break;
+    case 6: f(std::integral_constant<int, 6>{}); break;
+    case 7: case 8: f(std::integral_constant<int, 8>{}); break;
+    case 9: case 10: case 11: case 12: f(std::integral_constant<int, 12>{}); break;
+    default: f(std::integral_constant<int, 16>{}); break;
+  }
 }
 
 void topk_bucket(int E, const float* logits, const float* bias, int T, int K, float rsf, int32_t* ids,
                  float* wts, int32_t* ids_out, float* w_out, Groups g, hipStream_t s, Ev ev) {
-  const int nj = static_cast<int>(cdiv(E, 64));
-  if (nj <= 1) launch_topk_bucket<1>(logits, bias, T, E, K, rsf, ids, wts, ids_out, w_out, g, s, ev);
-  else if (nj <= 2) launch_topk_bucket<2>(logits, bias, T, E, K, rsf, ids, wts, ids_out, w_out, g, s, ev);
-  else if (nj <= 4) launch_topk_bucket<4>(logits, bias, T, E, K, rsf, ids, wts, ids_out, w_out, g, s, ev);
-  else if (nj <= 8) launch_topk_bucket<8>(logits, bias, T, E, K, rsf, ids, wts, ids_out, w_out, g, s, ev);
-  else launch_topk_bucket<16>(logits, bias, T, E, K, rsf, ids, wts, ids_out, w_out, g, s, ev);
-}
-
-template <int NJ>
-void launch_topk(const float* logits, const float* bias, int T, int E, int K, float rsf, int32_t* ids, float* wts,
-                 int32_t* ids_out, float* w_out, hipStream_t s, Ev ev) {
-  launch(k_topk<NJ>, dim3(static_cast<unsigned>(cdiv(T, 4))), dim3(256), s, ev.a, ev.b, logits, bias, T, E, K,
-         rsf, ids, wts, ids_out, w_out);
+  with_nj(E, [&](auto nj) {
+    launch(k_topk_bucket<decltype(nj)::value>, dim3(1), dim3(1024), s, ev.a, ev.b, logits, bias, T, E, K, rsf,
+           ids, wts, ids_out, w_out, g);
+  });
 }
 
 void topk_tokens(int E, const float* logits, const float* bias, int T, int K, float rsf, int32_t* ids,
                  float* wts, int32_t* ids_out, float* w_out, hipStream_t s, Ev ev) {
-  const int nj = static_cast<int>(cdiv(E, 64));
-  if (nj <= 1) launch_topk<1>(logits, bias, T, E, K, rsf, ids, wts, ids_out, w_out, s, ev);
-  else if (nj <= 2) launch_topk<2>(logits, bias, T, E, K, rsf, ids, wts, ids_out, w_out, s, ev);
-  else if (nj <= 4) launch_topk<4>(logits, bias, T, E, K, rsf, ids, wts, ids_out, w_out, s, ev);
-  else if (nj <= 8) launch_topk<8>(logits, bias, T, E, K, rsf, ids, wts, ids_out, w_out, s, ev);
-  else launch_topk<16>(logits, bias, T, E, K, rsf, ids, wts, ids_out, w_out, s, ev);
+  with_nj(E, [&](auto nj) {
+    launch(k_topk<decltype(nj)::value>, dim3(static_cast<unsigned>(cdiv(T, 4))), dim3(256), s, ev.a, ev.b, logits,
+           bias, T, E, K, rsf, ids, wts, ids_out, w_out);
+  });
 }
 
 void router_logits(const uint16_t* x, const float* wr, float* logits, int64_t T, int H, int E, hipStream_t s,
@@ -294,26 +294,17 @@ void launch_down_combine_ns(const uint16_t* h, const uint16_t* hs, const moe_mlp
   else launch_down_combine<KW, 4>(h, hs, w, ids, wts, E, K, H, I, Is, out, s, ev);
 }
 
-template <int NC, int NJ>
-void launch_dec_gateup(const moe_mlp_config* c, const moe_mlp_weights* w, const uint16_t* x, const float* logits,
-                       int32_t* ids, float* wts, int32_t* ids_out, float* w_out, uint16_t* h, hipStream_t s, Ev ev) {
+template <int NC>
+void dec_gateup(const moe_mlp_config* c, const moe_mlp_weights* w, const uint16_t* x, const float* logits,
+                int32_t* ids, float* wts, int32_t* ids_out, float* w_out, uint16_t* h, hipStream_t s, Ev ev) {
   constexpr int RJ = 4;
   const int I = c->moe_intermediate, K = c->top_k;
   const dim3 grid(static_cast<unsigned>(cdiv(I, 4 * RJ)), static_cast<unsigned>(K));
-  launch(k_dec_gateup<RJ, NC, NJ>, grid, dim3(256), s, ev.a, ev.b, x, w->w13_q, w->w13_s, w->w13_g, logits,
-         w->router_bias, K, c->routed_scaling_factor, ids, wts, ids_out, w_out, c->num_experts, c->hidden, I,
-         c->swiglu_limit, h);
-}
-
-template <int NC>
-void dec_gateup_nj(const moe_mlp_config* c, const moe_mlp_weights* w, const uint16_t* x, const float* logits,
-                   int32_t* ids, float* wts, int32_t* ids_out, float* w_out, uint16_t* h, hipStream_t s, Ev ev) {
-  const int nj = static_cast<int>(cdiv(c->num_experts, 64));
-  if (nj <= 1) launch_dec_gateup<NC, 1>(c, w, x, logits, ids, wts, ids_out, w_out, h, s, ev);
-  else if (nj <= 2) launch_dec_gateup<NC, 2>(c, w, x, logits, ids, wts, ids_out, w_out, h, s, ev);
-  else if (nj <= 4) launch_dec_gateup<NC, 4>(c, w, x, logits, ids, wts, ids_out, w_out, h, s, ev);
-  else if (nj <= 8) launch_dec_gateup<NC, 8>(c, w, x, logits, ids, wts, ids_out, w_out, h, s, ev);
-  else launch_dec_gateup<NC, 16>(c, w, x, logits, ids, wts, ids_out, w_out, h, s, ev);
+  with_nj(c->num_experts, [&](auto nj) {
+    launch(k_dec_gateup<RJ, NC, decltype(nj)::value>, grid, dim3(256), s, ev.a, ev.b, x, w->w13_q, w->w13_s,
+           w->w13_g, logits, w->router_bias, K, c->routed_scaling_factor, ids, wts, ids_out, w_out, c->num_experts,
+           c->hidden, I, c->swiglu_limit, h);
+  });
 }
 
 // One-token decode: 3 launches (see decode1.hpp).
@@ -326,8 +317,8 @@ void decode1(const moe_mlp_config* c, const moe_mlp_weights* w, const uint16_t* 
   const int nlb = static_cast<int>(cdiv(E, 4)), nsb = static_cast<int>(cdiv(Is, 4));
   launch(k_dec_logits_shared<16, 8>, dim3(nlb + nsb), dim3(256), s, e0.a, e0.b, x, w->router_w, logits, E, H,
          w->shared_w13, Is, hs, L, nlb);
-  if ((H >> 5) <= 64) dec_gateup_nj<1>(c, w, x, logits, ids, wts, ids_out, w_out, h, s, e1);
-  else dec_gateup_nj<2>(c, w, x, logits, ids, wts, ids_out, w_out, h, s, e1);
+  if ((H >> 5) <= 64) dec_gateup<1>(c, w, x, logits, ids, wts, ids_out, w_out, h, s, e1);
+  else dec_gateup<2>(c, w, x, logits, ids, wts, ids_out, w_out, h, s, e1);
   const int kw = dec1_kw(K);
   if (kw == 4) launch_down_combine_ns<4>(h, hs, w, ids, wts, E, K, H, I, Is, out, s, e2);
   else if (kw == 8) launch_down_combine_ns<8>(h, hs, w, ids, wts, E, K, H, I, Is, out, s, e2);

@@ -140,64 +140,103 @@ __global__ __launch_bounds__(256) void k_logits_gemm(const uint16_t* __restrict_
 }
 
 // ---------------------------------------------------------------------------
-// Top-k of one token by one wavefront.  Lane l holds experts l, l+64, ...
-// (NJ per lane, E <= 64 * NJ).  Each of K rounds takes the largest biased
-// score (exact ties: lower expert id), then the weights are the chosen
-// unbiased scores over their sum, times rsf, and written to ids/wts (and
-// ids2/wts2 when not null).  Returns the id in slot `want`; with ids == null
-// nothing is written and only rounds 0..want run.
+// Top-k of one token by one wavefront.  Candidate e's key is
+//     (order-preserving bits of its biased score) << 32 | (0xFFFFFFFF - e),
+// so a larger key is a larger score and, between equal scores, the lower id
+// (keys are distinct).  Each lane sorts its NJ keys (experts lane + 64 j,
+// E <= 64 * NJ) descending once; a round is the wavefront max of the lanes'
+// first keys (DPP within rows of 16, then the 4 row winners) and the owning
+// lane drops its first key.  One 64-bit value per reduction step keeps a
+// round's dependent chain short: the wavefront sits on the decode critical
+// path.  Returns the id in slot `want`.  With ids != null all K rounds run
+// and ids/wts (and ids2/wts2 when not null) are written: the weight of slot k
+// is its unbiased sigmoid score over the sum of the K chosen scores (added in
+// slot order) times rsf.
 // ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t f32_order_bits(float f) {
+  const uint32_t b = __float_as_uint(f + 0.0f);   // -0 -> +0
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+__device__ __forceinline__ uint64_t u64_of(uint32_t lo, uint32_t hi) {
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_max_u64(uint64_t v) {
+  const uint32_t lo = static_cast<uint32_t>(dpp_mov<CTRL>(static_cast<int>(static_cast<uint32_t>(v))));
+  const uint32_t hi = static_cast<uint32_t>(dpp_mov<CTRL>(static_cast<int>(static_cast<uint32_t>(v >> 32))));
+  const uint64_t o = u64_of(lo, hi);
+  return o > v ? o : v;
+}
+
+__device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int l) {
+  const uint32_t lo = __builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(v)), l);
+  const uint32_t hi = __builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(v >> 32)), l);
+  return u64_of(lo, hi);
+}
+
+// Wave-wide max of a 64-bit value; every lane returns it.  All lanes active.
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+  v = dpp_max_u64<DPP_QUAD_1032>(v);
+  v = dpp_max_u64<DPP_QUAD_2301>(v);
+  v = dpp_max_u64<DPP_ROW_HALF_MIRROR>(v);
+  v = dpp_max_u64<DPP_ROW_MIRROR>(v);
+  const uint64_t a = readlane_u64(v, 0), b = readlane_u64(v, 16);
+  const uint64_t c = readlane_u64(v, 32), d = readlane_u64(v, 48);
+  const uint64_t ab = a > b ? a : b, cd = c > d ? c : d;
+  return ab > cd ? ab : cd;
+}
+
 template <int NJ>
-__device__ __forceinline__ int topk_wave(const float* __restrict__ lrow, const float* __restrict__ bias,
-                                         int E, int K, float rsf, int32_t* ids, float* wts,
-                                         int32_t* ids2, float* wts2, int want = 0) {
+__device__ __forceinline__ int topk_wave(const float* __restrict__ lrow, const float* __restrict__ bias, int E,
+                                         int K, float rsf, int want, int32_t* ids, float* wts, int32_t* ids2,
+                                         float* wts2) {
   const int lane = threadIdx.x & 63;
-  float sel[NJ], sc[NJ];
+  uint64_t key[NJ];
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
     const int e = lane + 64 * j;
-    if (e < E) {
-      const float s = 1.0f / (1.0f + expf(-lrow[e]));
-      sc[j] = s;
-      sel[j] = s + bias[e];
-    } else {
-      sc[j] = 0.0f;
-      sel[j] = -INFINITY;
-    }
+    key[j] = e < E ? u64_of(0xFFFFFFFFu - static_cast<uint32_t>(e),
+                            f32_order_bits(1.0f / (1.0f + expf(-lrow[e])) + bias[e]))
+                   : 0;                          // below every real key
   }
-  uint32_t taken = 0;
-  int my_id = 0, want_id = 0;
-  float my_s = 0.0f, sum = 0.0f;
-  const int nr = ids ? K : want + 1;
-  for (int k = 0; k < nr; ++k) {
-    float best = -INFINITY, bs = 0.0f;
-    int be = 0x7fffffff;
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      const int e = lane + 64 * j;
-      if (e < E && !((taken >> j) & 1u) && (sel[j] > best || be == 0x7fffffff)) {
-        best = sel[j];
-        bs = sc[j];
-        be = e;
-      }
+  for (int i = 0; i < NJ - 1; ++i)
+#pragma unroll
+    for (int j = 0; j < NJ - 1 - i; ++j) {
+      const uint64_t a = key[j], b = key[j + 1];
+      const bool sw = b > a;
+      key[j] = sw ? b : a;
+      key[j + 1] = sw ? a : b;
     }
-    wave_argmax(best, be, bs);
-    if ((be & 63) == lane) taken |= 1u << (be >> 6);
-    if (lane == k) {
-      my_id = be;
-      my_s = bs;
+  const int nr = ids ? K : want + 1;
+  int want_id = 0, my_id = 0;
+  for (int k = 0; k < nr; ++k) {
+    const uint64_t w = wave_max_u64(key[0]);
+    const int id = static_cast<int>(0xFFFFFFFFu - static_cast<uint32_t>(w));
+    if (key[0] == w) {
+#pragma unroll
+      for (int j = 0; j < NJ - 1; ++j) key[j] = key[j + 1];
+      key[NJ - 1] = 0;
     }
-    if (k == want) want_id = be;
-    sum += bs;
+    if (k == want) want_id = id;
+    if (lane == k) my_id = id;
   }
-  if (ids && lane < K) {
-    const float w = my_s / sum * rsf;
-    ids[lane] = my_id;
-    wts[lane] = w;
-    if (ids2) ids2[lane] = my_id;
-    if (wts2) wts2[lane] = w;
+  if (ids) {
+    // the same expression as above on the same logit: the same bits
+    const float my_s = lane < K ? 1.0f / (1.0f + expf(-lrow[my_id])) : 0.0f;
+    float sum = 0.0f;
+    for (int k = 0; k < K; ++k) sum += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_s), k));
+    if (lane < K) {
+      const float w = my_s / sum * rsf;
+      ids[lane] = my_id;
+      wts[lane] = w;
+      if (ids2) ids2[lane] = my_id;
+      if (wts2) wts2[lane] = w;
+    }
   }
-  return want_id;                               // wave-uniform
+  return want_id;
 }
 
 template <int NJ>
@@ -207,7 +246,7 @@ __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ logits, 
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
   const int64_t o = static_cast<int64_t>(t) * K;
-  topk_wave<NJ>(logits + static_cast<int64_t>(t) * E, bias, E, K, rsf, ids + o, wts + o,
+  topk_wave<NJ>(logits + static_cast<int64_t>(t) * E, bias, E, K, rsf, 0, ids + o, wts + o,
                 ids_out ? ids_out + o : nullptr, w_out ? w_out + o : nullptr);
 }
 
@@ -238,7 +277,7 @@ __global__ __launch_bounds__(1024) void k_topk_bucket(const float* __restrict__ 
   for (int e = tid; e < E; e += 1024) s_cnt[e] = 0;
   for (int t = wv; t < T; t += 16) {
     const int64_t o = static_cast<int64_t>(t) * K;
-    topk_wave<NJ>(logits + static_cast<int64_t>(t) * E, bias, E, K, rsf, ids + o, wts + o,
+    topk_wave<NJ>(logits + static_cast<int64_t>(t) * E, bias, E, K, rsf, 0, ids + o, wts + o,
                   ids_out ? ids_out + o : nullptr, w_out ? w_out + o : nullptr);
   }
   __threadfence_block();
