@@ -35,7 +35,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "topk_routed_gateup_flash_decode_t1_traffic.txt")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "routed_gateup_shared_down_flash_decode_t1_traffic.txt")
 GEMV_SOURCES = ["routed_expert_mlp_amd/csrc/decode1.hpp", "routed_expert_mlp_amd/csrc/router.hpp",
                 "routed_expert_mlp_amd/csrc/gemv.hpp", "routed_expert_mlp_amd/csrc/common.hpp"]
 
@@ -301,16 +301,17 @@ def main():
     n_prof = max(50, min(args.steps, 500))
     st = stage_times(cfg, wts, xs, outs, False, n_prof, ev, ws)
     prof_step_ms = sum(st.values())
-    gu_ms = st["topk_routed_gateup"]
+    gu_ms = st["routed_gateup_shared_down"]
     # algorithmic bytes of each one-token stage
     exp13 = 2 * w.I * w.H // 2 + 2 * w.I * w.H // 16          # NVFP4 gate/up of one expert
     exp2 = w.H * w.I // 2 + w.H * w.I // 16                    # NVFP4 down of one expert
     stage_bytes = {
         "logits_shared_gateup": 4 * w.E * w.H + 2 * 2 * w.Is * w.H + 2 * w.H + 4 * w.E + 2 * w.Is,
-        "topk_routed_gateup": w.K * exp13 + 2 * w.H + 4 * w.E * 2 + 2 * w.K * w.I + 8 * w.K,
-        "down_combine": w.K * exp2 + 2 * w.H * w.Is + 2 * w.K * w.I + 2 * w.Is + 2 * w.H,
+        "routed_gateup_shared_down": (w.K * exp13 + 2 * w.H * w.Is + 2 * w.H + 4 * w.E * 2 + 2 * w.K * w.I
+                                      + 2 * w.Is + 4 * w.H + 8 * w.K),
+        "routed_down_combine": w.K * exp2 + 2 * w.K * w.I + 4 * w.H + 2 * w.H + 8 * w.K,
     }
-    gu_bytes = stage_bytes["topk_routed_gateup"]
+    gu_bytes = stage_bytes["routed_gateup_shared_down"]
     gu_gbs = gu_bytes / (gu_ms * 1e-3) / 1e9
     traffic = read_traffic()
     extra = {"tokens_per_s": round(1.0 / sec, 1), "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
@@ -393,7 +394,7 @@ def main():
                    "tokens": 1, "hidden": w.H, "moe_intermediate": w.I, "experts": w.E, "top_k": w.K,
                    "weights": "nvfp4 (e2m1 + e4m3/16) routed, bf16 shared, fp32 router",
                    "weight_copies_rotated": R},
-        "roofline": {"bound": "hbm", "kernel": "topk_routed_gateup (k_dec_gateup: router top-k, NVFP4 gate/up, clamped SwiGLU)",
+        "roofline": {"bound": "hbm", "kernel": "routed_gateup_shared_down (k_dec_gateup: BF16 shared down, router top-k, NVFP4 gate/up + clamped SwiGLU)",
                      "achieved": round(gu_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gu_gbs / HBM_PEAK_GBS, 4), "avg_launch_us": round(gu_ms * 1e3, 3),
                      "algorithmic_bytes_per_launch": int(gu_bytes),

@@ -167,7 +167,8 @@ int moe_mlp_prefill(const moe_mlp_config* cfg, const moe_mlp_weights* w, const u
  * `events` is a HOST array of n_events caller-created hipEvent_t handles
  * (none NULL); n_events >= 2 * n_stages, else MOE_MLP_ERR_BAD_VALUE.
  * Stages (moe_mlp_stage_name): ROUTED one-token decode (T == 1, H <= 4096,
- * I and Is <= 2048) logits_shared_gateup, topk_routed_gateup, down_combine;
+ * I and Is <= 2048) logits_shared_gateup, routed_gateup_shared_down,
+ * routed_down_combine;
  * other ROUTED decode router_logits, topk_bucket, shared_gateup,
  * routed_gateup, shared_down, routed_down, combine; ROUTED prefill
  * router_logits, topk, permute, routed_gateup, routed_down, shared_gateup,

@@ -4,16 +4,18 @@
 //   1. k_dec_logits_shared: router logits (fp32 rows of gate.weight) and the
 //      BF16 shared expert's gate/up + clamped SwiGLU, both of which only need
 //      x, in one grid;
-//   2. k_dec_gateup: every wavefront first redoes the router top-k from the
-//      E logits (router.hpp topk_wave, DPP wavefront max rounds; "Traps":
-//      bias steers selection only, weights are the renormalised unbiased
-//      scores times rsf) to learn which expert its block serves, then streams
-//      that expert's NVFP4 gate/up rows + clamped SwiGLU -> h (bf16).  One
-//      wavefront also writes ids and weights.  Recomputing the selection
+//   2. k_dec_gateup: its first blocks stream the shared expert's BF16 down
+//      rows (ys = W2s hs, fp32), which need nothing from the router, while
+//      the other blocks first redo the router top-k from the E logits
+//      (router.hpp topk_wave; "Traps": bias steers selection only, weights
+//      are the renormalised unbiased scores times rsf) to learn which expert
+//      they serve, then stream its NVFP4 gate/up rows + clamped SwiGLU -> h
+//      (bf16).  One wavefront also writes ids and weights.  The shared rows
+//      keep HBM busy while the selection runs, and redoing the selection
 //      (~1 KB of logits per wavefront) is cheaper than a launch of its own;
-//   3. k_dec_down_combine: routed NVFP4 down rows of all K experts, the BF16
-//      shared down rows, and the combine out = bf16(shared + sum_k w_k y_k)
-//      for a block of output rows (fixed k order).
+//   3. k_dec_down_combine: routed NVFP4 down rows of all K experts and the
+//      combine out = bf16(ys + sum_k w_k y_k) for a block of output rows
+//      (fixed k order).
 //
 // Each wavefront issues all loads of its rows before using any of them, so a
 // wavefront has its whole share of the weight stream in flight at once.
@@ -96,25 +98,71 @@ __global__ __launch_bounds__(256) void k_dec_logits_shared(const uint16_t* __res
 }
 
 // -------------------------------------------------------------------------
-// 2. top-k + routed gate/up for one token.  Grid (I / (4*RJ), K): block
-// (jb, k) finds the expert in slot k (topk_wave, NJ >= E / 64) and runs its
-// gate rows j = (jb*4 + wave)*RJ .. +RJ and up rows I + j.  Lane l covers the
-// 16-byte chunks l, l+64, ... (NC of them) of each row, so every load
-// instruction reads 1 KB contiguous.  Wavefront 0 of block (0, 0) runs all K
-// rounds and writes ids/wts (and ids_out/w_out when not null).
+// 2. shared down + top-k + routed gate/up for one token.  1-D grid:
+//  * blocks [0, n_sd): shared down rows r = (b*4 + wave)*RS .. +RS,
+//    ys[r] = sum_j W2s[r, j] hs[j] in fp32 (lane l takes the 16-byte chunks
+//    l, l+64, ... of each row, NSC of them);
+//  * blocks n_sd + a: slot k = a / njb finds its expert (topk_wave,
+//    NJ >= E / 64) and runs gate rows j = ((a % njb)*4 + wave)*RJ .. +RJ and
+//    up rows I + j, njb = ceil(I / (4 RJ)).  Lane l covers the 16-byte chunks
+//    l, l+64, ... (NC of them) of each row, so every load instruction reads
+//    1 KB contiguous.  Wavefront 0 of the first gate/up block runs all K
+//    rounds and writes ids/wts (and ids_out/w_out when not null).
 // -------------------------------------------------------------------------
-template <int RJ, int NC, int NJ>
+template <int RJ, int NC, int NJ, int RS, int NSC>
 __global__ __launch_bounds__(256) void k_dec_gateup(const uint16_t* __restrict__ x, const uint8_t* __restrict__ q13,
                                                     const uint8_t* __restrict__ s13, const float* __restrict__ g13,
                                                     const float* __restrict__ logits, const float* __restrict__ bias,
                                                     int K, float rsf, int32_t* __restrict__ ids,
                                                     float* __restrict__ wts, int32_t* ids_out, float* w_out, int E,
-                                                    int H, int I, float L, uint16_t* __restrict__ h) {
+                                                    int H, int I, float L, uint16_t* __restrict__ h,
+                                                    const uint16_t* __restrict__ sw2, const uint16_t* __restrict__ hs,
+                                                    int Is, float* __restrict__ ys, int n_sd) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int k = blockIdx.y;
-  const int j0 = (blockIdx.x * 4 + wv) * RJ;
+  if (static_cast<int>(blockIdx.x) < n_sd) {
+    const int r0 = (blockIdx.x * 4 + wv) * RS;
+    if (r0 >= H) return;
+    const int nsc = Is >> 3;                     // 8-bf16 chunks per row
+    uint4 w[RS][NSC];
+#pragma unroll
+    for (int r = 0; r < RS; ++r) {
+      const uint4* row = reinterpret_cast<const uint4*>(sw2 + static_cast<int64_t>(min(r0 + r, H - 1)) * Is);
+#pragma unroll
+      for (int i = 0; i < NSC; ++i) {
+        const int c = lane + 64 * i;
+        w[r][i] = c < nsc ? row[c] : make_uint4(0, 0, 0, 0);
+      }
+    }
+    uint32_t hv[NSC][4];
+#pragma unroll
+    for (int i = 0; i < NSC; ++i) {
+      const int c = lane + 64 * i;
+      const uint4 v = c < nsc ? reinterpret_cast<const uint4*>(hs)[c] : make_uint4(0, 0, 0, 0);
+      hv[i][0] = v.x; hv[i][1] = v.y; hv[i][2] = v.z; hv[i][3] = v.w;
+    }
+    float acc[RS];
+#pragma unroll
+    for (int r = 0; r < RS; ++r) {
+      acc[r] = 0.0f;
+#pragma unroll
+      for (int i = 0; i < NSC; ++i) acc[r] = bf16_chunk_dot(w[r][i], hv[i], acc[r]);
+      acc[r] = wave_sum(acc[r]);
+    }
+    if (lane < RS) {
+      float v = acc[0];
+#pragma unroll
+      for (int r = 1; r < RS; ++r)
+        if (lane == r) v = acc[r];
+      if (r0 + lane < H) ys[r0 + lane] = v;
+    }
+    return;
+  }
+  const int a = blockIdx.x - n_sd;
+  const int njb = static_cast<int>(cdiv(I, 4 * RJ));
+  const int k = a / njb;
+  const int j0 = ((a % njb) * 4 + wv) * RJ;
   if (j0 >= I) return;
-  const bool writer = blockIdx.x == 0 && k == 0 && wv == 0;
+  const bool writer = a == 0 && wv == 0;
   const int sel = topk_wave<NJ>(logits, bias, E, K, rsf, k, writer ? ids : nullptr, wts, ids_out, w_out);
   const int e = min(max(sel, 0), E - 1);
   const int64_t rq = H >> 1, rs = H >> 4;                 // code / scale bytes per row
@@ -179,22 +227,19 @@ __global__ __launch_bounds__(256) void k_dec_gateup(const uint16_t* __restrict__
 }
 
 // -------------------------------------------------------------------------
-// 4. down + combine for one token.  Block b owns output rows
+// 3. routed down + combine for one token.  Block b owns output rows
 // r0 = b*R .. +R and has KW >= K wavefronts: wavefront k streams those R rows
 // of expert ids[k]'s NVFP4 down projection against its h_k (one 16-byte
-// chunk per lane, lanes < I/32, h_k chunk in registers), and the shared
-// expert's BF16 down rows r0 + w, r0 + w + KW, ... are spread over all KW
-// wavefronts.  Per-row partials meet in LDS and thread r writes
-// out[r0+r] = bf16(ys + sum_k (w_k * g2_k) * acc_k), k in order.
+// chunk per lane, lanes < I/32, h_k chunk in registers).  Per-row partials
+// meet in LDS and thread r writes out[r0+r] = bf16(ys + sum_k (w_k g2_k)
+// acc_k), k in order (ys = 0 without a shared expert).
 // -------------------------------------------------------------------------
-template <int R, int KW, int NS>
+template <int R, int KW>
 __global__ __launch_bounds__(KW * 64) void k_dec_down_combine(
-    const uint16_t* __restrict__ h, const uint16_t* __restrict__ hs, const uint8_t* __restrict__ q2,
-    const uint8_t* __restrict__ s2, const float* __restrict__ g2, const uint16_t* __restrict__ sw2,
-    const int32_t* __restrict__ ids, const float* __restrict__ wts, int E, int K, int H, int I, int Is,
-    uint16_t* __restrict__ out) {
-  constexpr int SR = (R + KW - 1) / KW;             // shared rows per wavefront
-  __shared__ float part[KW + 1][R];
+    const uint16_t* __restrict__ h, const uint8_t* __restrict__ q2, const uint8_t* __restrict__ s2,
+    const float* __restrict__ g2, const float* __restrict__ ys, const int32_t* __restrict__ ids,
+    const float* __restrict__ wts, int E, int K, int H, int I, uint16_t* __restrict__ out) {
+  __shared__ float part[KW][R];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int r0 = blockIdx.x * R;
   const bool routed = wv < K;
@@ -209,19 +254,6 @@ __global__ __launch_bounds__(KW * 64) void k_dec_down_combine(
     cw[r] = act ? *reinterpret_cast<const uint4*>(q2 + base * rq + 16 * lane) : make_uint4(0, 0, 0, 0);
     sc[r] = act ? *reinterpret_cast<const uint16_t*>(s2 + base * rs + 2 * lane) : 0u;
   }
-  const int nsc = Is >> 3;                           // 8-bf16 chunks per shared row
-  uint4 shw[SR][NS];
-#pragma unroll
-  for (int r = 0; r < SR; ++r) {
-    const int rr = wv + KW * r;                      // row within the block
-    const int row = min(r0 + rr, H - 1);
-#pragma unroll
-    for (int i = 0; i < NS; ++i) {
-      const int c = lane + 64 * i;
-      shw[r][i] = (rr < R && c < nsc) ? reinterpret_cast<const uint4*>(sw2 + static_cast<int64_t>(row) * Is)[c]
-                                      : make_uint4(0, 0, 0, 0);
-    }
-  }
   uint32_t xp[16];
   {
     const uint4* hp = reinterpret_cast<const uint4*>(h + static_cast<int64_t>(wv) * I + 32 * lane);
@@ -231,42 +263,23 @@ __global__ __launch_bounds__(KW * 64) void k_dec_down_combine(
       xp[4 * q] = v.x; xp[4 * q + 1] = v.y; xp[4 * q + 2] = v.z; xp[4 * q + 3] = v.w;
     }
   }
-  uint32_t hsp[NS][4];
-#pragma unroll
-  for (int i = 0; i < NS; ++i) {
-    const int c = lane + 64 * i;
-    const uint4 v = c < nsc ? reinterpret_cast<const uint4*>(hs)[c] : make_uint4(0, 0, 0, 0);
-    hsp[i][0] = v.x; hsp[i][1] = v.y; hsp[i][2] = v.z; hsp[i][3] = v.w;
-  }
   float acc[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     acc[r] = fmaf(e2m1x16_dot(cw[r].x, cw[r].y, xp), e4m3_to_f32<0>(sc[r]), 0.0f);
     acc[r] = fmaf(e2m1x16_dot(cw[r].z, cw[r].w, xp + 8), e4m3_to_f32<1>(sc[r]), acc[r]);
   }
-  float accs[SR];
-#pragma unroll
-  for (int r = 0; r < SR; ++r) {
-    accs[r] = 0.0f;
-#pragma unroll
-    for (int i = 0; i < NS; ++i) accs[r] = bf16_chunk_dot(shw[r][i], hsp[i], accs[r]);
-  }
 #pragma unroll
   for (int r = 0; r < R; ++r) acc[r] = wave_sum(acc[r]);
-#pragma unroll
-  for (int r = 0; r < SR; ++r) accs[r] = wave_sum(accs[r]);
   if (lane == 0) {
     const float wk = routed ? wts[wv] * g2[e] : 0.0f;
 #pragma unroll
     for (int r = 0; r < R; ++r) part[wv][r] = wk * acc[r];
-#pragma unroll
-    for (int r = 0; r < SR; ++r)
-      if (wv + KW * r < R) part[KW][wv + KW * r] = accs[r];
   }
   __syncthreads();
   const int t = threadIdx.x;
   if (t < R && r0 + t < H) {
-    float o = part[KW][t];
+    float o = ys ? ys[r0 + t] : 0.0f;
     for (int k = 0; k < K; ++k) o += part[k][t];
     out[r0 + t] = f32_to_bf16(o);
   }

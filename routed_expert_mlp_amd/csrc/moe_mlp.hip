@@ -253,7 +253,8 @@ GemmArgs bf16_gemm_args(const uint16_t* act, int kdim, const uint16_t* w, int ha
 
 const char* const kDecodeStages[] = {"router_logits", "topk_bucket", "shared_gateup", "routed_gateup",
                                     "shared_down", "routed_down", "combine"};
-const char* const kDecode1Stages[] = {"logits_shared_gateup", "topk_routed_gateup", "down_combine"};
+const char* const kDecode1Stages[] = {"logits_shared_gateup", "routed_gateup_shared_down",
+                                       "routed_down_combine"};
 const char* const kPrefillStages[] = {"router_logits", "topk", "permute", "routed_gateup", "routed_down",
                                      "shared_gateup", "shared_down", "combine"};
 const char* const kDenseStages[] = {"dense_gateup", "dense_down"};
@@ -276,53 +277,50 @@ int n_stages(const moe_mlp_config* c, int64_t T, int prefill) {
   return prefill ? 8 : 7;
 }
 
-template <int KW, int NS>
-void launch_down_combine(const uint16_t* h, const uint16_t* hs, const moe_mlp_weights* w, const int32_t* ids,
-                         const float* wts, int E, int K, int H, int I, int Is, uint16_t* out, hipStream_t s, Ev ev) {
-  constexpr int R = 8;
-  launch(k_dec_down_combine<R, KW, NS>, dim3(static_cast<unsigned>(cdiv(H, R))), dim3(KW * 64), s, ev.a, ev.b, h,
-         hs, w->w2_q, w->w2_s, w->w2_g, w->shared_w2, ids, wts, E, K, H, I, Is, out);
-}
-
-template <int KW>
-void launch_down_combine_ns(const uint16_t* h, const uint16_t* hs, const moe_mlp_weights* w, const int32_t* ids,
-                            const float* wts, int E, int K, int H, int I, int Is, uint16_t* out, hipStream_t s,
-                            Ev ev) {
-  const int ns = static_cast<int>(cdiv(Is / 8, 64));
-  if (ns <= 1) launch_down_combine<KW, 1>(h, hs, w, ids, wts, E, K, H, I, Is, out, s, ev);
-  else if (ns <= 2) launch_down_combine<KW, 2>(h, hs, w, ids, wts, E, K, H, I, Is, out, s, ev);
-  else launch_down_combine<KW, 4>(h, hs, w, ids, wts, E, K, H, I, Is, out, s, ev);
-}
-
-template <int NC>
+// One-token decode: 3 launches (see decode1.hpp).
+template <int NSC>
 void dec_gateup(const moe_mlp_config* c, const moe_mlp_weights* w, const uint16_t* x, const float* logits,
-                int32_t* ids, float* wts, int32_t* ids_out, float* w_out, uint16_t* h, hipStream_t s, Ev ev) {
-  constexpr int RJ = 4;
-  const int I = c->moe_intermediate, K = c->top_k;
-  const dim3 grid(static_cast<unsigned>(cdiv(I, 4 * RJ)), static_cast<unsigned>(K));
+                int32_t* ids, float* wts, int32_t* ids_out, float* w_out, uint16_t* h, const uint16_t* hs,
+                float* ys, hipStream_t s, Ev ev) {
+  constexpr int RJ = 4, NC = 2, RS = 8;
+  const int H = c->hidden, I = c->moe_intermediate, K = c->top_k;
+  const int Is = c->n_shared_experts ? c->shared_intermediate : 0;
+  const int n_sd = Is ? static_cast<int>(cdiv(H, 4 * RS)) : 0;
+  const unsigned grid = static_cast<unsigned>(n_sd + K * cdiv(I, 4 * RJ));
   with_nj(c->num_experts, [&](auto nj) {
-    launch(k_dec_gateup<RJ, NC, decltype(nj)::value>, grid, dim3(256), s, ev.a, ev.b, x, w->w13_q, w->w13_s,
-           w->w13_g, logits, w->router_bias, K, c->routed_scaling_factor, ids, wts, ids_out, w_out, c->num_experts,
-           c->hidden, I, c->swiglu_limit, h);
+    launch(k_dec_gateup<RJ, NC, decltype(nj)::value, RS, NSC>, dim3(grid), dim3(256), s, ev.a, ev.b, x, w->w13_q,
+           w->w13_s, w->w13_g, logits, w->router_bias, K, c->routed_scaling_factor, ids, wts, ids_out, w_out,
+           c->num_experts, H, I, c->swiglu_limit, h, w->shared_w2, hs, Is, ys, n_sd);
   });
 }
 
-// One-token decode: 3 launches (see decode1.hpp).
+template <int KW>
+void launch_down_combine(const moe_mlp_config* c, const moe_mlp_weights* w, const uint16_t* h, const float* ys,
+                         const int32_t* ids, const float* wts, uint16_t* out, hipStream_t s, Ev ev) {
+  constexpr int R = 4;
+  const int H = c->hidden;
+  launch(k_dec_down_combine<R, KW>, dim3(static_cast<unsigned>(cdiv(H, R))), dim3(KW * 64), s, ev.a, ev.b, h,
+         w->w2_q, w->w2_s, w->w2_g, ys, ids, wts, c->num_experts, c->top_k, H, c->moe_intermediate, out);
+}
+
 void decode1(const moe_mlp_config* c, const moe_mlp_weights* w, const uint16_t* x, uint16_t* out,
              int32_t* ids_out, float* w_out, float* logits, int32_t* ids, float* wts, uint16_t* h, uint16_t* hs,
-             hipStream_t s, Ev e0, Ev e1, Ev e2) {
-  const int H = c->hidden, E = c->num_experts, K = c->top_k, I = c->moe_intermediate;
+             float* ys, hipStream_t s, Ev e0, Ev e1, Ev e2) {
+  const int H = c->hidden, E = c->num_experts, K = c->top_k;
   const int Is = c->n_shared_experts ? c->shared_intermediate : 0;
-  const float L = c->swiglu_limit;
   const int nlb = static_cast<int>(cdiv(E, 4)), nsb = static_cast<int>(cdiv(Is, 4));
   launch(k_dec_logits_shared<16, 8>, dim3(nlb + nsb), dim3(256), s, e0.a, e0.b, x, w->router_w, logits, E, H,
-         w->shared_w13, Is, hs, L, nlb);
-  if ((H >> 5) <= 64) dec_gateup<1>(c, w, x, logits, ids, wts, ids_out, w_out, h, s, e1);
-  else dec_gateup<2>(c, w, x, logits, ids, wts, ids_out, w_out, h, s, e1);
+         w->shared_w13, Is, hs, c->swiglu_limit, nlb);
+  const int nsc = static_cast<int>(cdiv(Is / 8, 64));
+  if (nsc <= 1) dec_gateup<1>(c, w, x, logits, ids, wts, ids_out, w_out, h, hs, ys, s, e1);
+  else if (nsc == 2) dec_gateup<2>(c, w, x, logits, ids, wts, ids_out, w_out, h, hs, ys, s, e1);
+  else if (nsc == 3) dec_gateup<3>(c, w, x, logits, ids, wts, ids_out, w_out, h, hs, ys, s, e1);
+  else dec_gateup<4>(c, w, x, logits, ids, wts, ids_out, w_out, h, hs, ys, s, e1);
+  const float* ysr = Is ? ys : nullptr;
   const int kw = dec1_kw(K);
-  if (kw == 4) launch_down_combine_ns<4>(h, hs, w, ids, wts, E, K, H, I, Is, out, s, e2);
-  else if (kw == 8) launch_down_combine_ns<8>(h, hs, w, ids, wts, E, K, H, I, Is, out, s, e2);
-  else launch_down_combine_ns<16>(h, hs, w, ids, wts, E, K, H, I, Is, out, s, e2);
+  if (kw == 4) launch_down_combine<4>(c, w, h, ysr, ids, wts, out, s, e2);
+  else if (kw == 8) launch_down_combine<8>(c, w, h, ysr, ids, wts, out, s, e2);
+  else launch_down_combine<16>(c, w, h, ysr, ids, wts, out, s, e2);
 }
 
 int run_layer(const moe_mlp_config* c, const moe_mlp_weights* w, const uint16_t* x, int64_t T, uint16_t* out,
@@ -386,7 +384,7 @@ int run_layer(const moe_mlp_config* c, const moe_mlp_weights* w, const uint16_t*
   const float rsf = c->routed_scaling_factor;
 
   if (decode1_ok(c, T, prefill)) {
-    decode1(c, w, x, out, ids_out, w_out, logits, ids, wts, h, hs, s, ev(0), ev(1), ev(2));
+    decode1(c, w, x, out, ids_out, w_out, logits, ids, wts, h, hs, ys, s, ev(0), ev(1), ev(2));
     return launch_status();
   }
   router_logits(x, w->router_w, logits, T, H, E, s, ev(0));

@@ -184,7 +184,8 @@ def test_profiled_entry_validation():
     w = full_weights()
     n = 3                               # one-token decode stages of this config
     names = [L.moe_mlp_stage_name(ctypes.byref(c), 1, 0, i) for i in range(n + 1)]
-    assert [x.decode() for x in names[:n]] == ["logits_shared_gateup", "topk_routed_gateup", "down_combine"]
+    assert [x.decode() for x in names[:n]] == ["logits_shared_gateup", "routed_gateup_shared_down",
+                                                   "routed_down_combine"]
     assert names[n] is None
     assert [L.moe_mlp_stage_name(ctypes.byref(c), 2, 0, i).decode() for i in range(7)][3] == "routed_gateup"
     assert L.moe_mlp_stage_name(ctypes.byref(c), 2, 1, 8) is None

@@ -200,6 +200,33 @@ def test_dense_decode_full_width():
     _dense("dense_prefill_t4096", False, 4, T=4)
 
 
+ONE_TOKEN = [dict(K=16), dict(E=1, K=1), dict(Is=0), dict(H=32, I=32, Is=32), dict(K=2),
+             dict(I=96, Is=224), dict(H=4096, I=2048, Is=2048, E=12, K=8)]
+
+
+@pytest.mark.parametrize("overrides", ONE_TOKEN, ids=[str(o) for o in ONE_TOKEN])
+def test_one_token_path_edge_cases(overrides):
+    """T=1 runs the three-launch one-token kernels: block shapes for K up to 16, no shared
+    expert, the smallest hidden size, ragged row counts, and the largest H / I / Is it takes."""
+    _fresh("tiny_decode", False, T=1, **overrides)
+
+
+def test_one_token_path_repeated_calls():
+    """Many calls in a row on one workspace (which starts as garbage) give the same bits."""
+    d = device_workload("flash_decode_t1")
+    ws = capi.workspace(d.cfg, 1, False, DEV)
+    ws.fill_(0xFF)
+    ref = d.run(False)[0]
+    outs = []
+    for _ in range(20):
+        o = torch.empty_like(ref)
+        capi.moe_mlp_decode(d.cfg, d.weights, d.x, o, ws=ws)
+        outs.append(o)
+    torch.cuda.synchronize()
+    for o in outs:
+        assert torch.equal(o.view(torch.int16), ref.view(torch.int16))
+
+
 def test_single_token_general_path():
     """I > 2048 takes the general decode kernels at T=1 (not the one-token path)."""
     _fresh("tiny_decode", False, T=1, I=2080)
