@@ -34,6 +34,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E
+CALIB_BYTES = 512 << 20         # the counter-calibration copy
 BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "routed_gateup_shared_down_flash_decode_t1_traffic.txt")
 GEMV_SOURCES = ["routed_expert_mlp_amd/csrc/decode1.hpp", "routed_expert_mlp_amd/csrc/router.hpp",
@@ -54,6 +55,10 @@ def parse():
     p.add_argument("--no-extra-decode", action="store_true")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle CPU time")
+    p.add_argument("--calibrate-copy", action="store_true",
+                   help="end the decode part with 3 device copies of 512 MiB (counter calibration)")
+    p.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                   help="write the traffic summary from two rocprofv3 --pmc counter_collection.csv files and exit")
     return p.parse_args()
 
 
@@ -174,6 +179,53 @@ def read_traffic():
         return None
 
 
+def summarize_traffic(fetch_csv, write_csv):
+    """HBM bytes per launch of the one-token decode kernels from two rocprofv3 --pmc runs of
+    `bench.py --calibrate-copy` (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch).  Each counter is
+    scaled by what it reads for the 512 MiB device copies the run ends its decode part with."""
+    import csv
+    import numpy as np
+
+    def per_kernel(path):
+        rows = list(csv.DictReader(open(path)))
+        vals = {}
+        order = []
+        for r in rows:
+            v = float(r["Counter_Value"])
+            name = r["Kernel_Name"]
+            vals.setdefault(name, []).append(v)
+            order.append((name, v))
+        return vals, order
+
+    out = []
+    scale = {}
+    per = {}
+    for label, path in (("fetch", fetch_csv), ("write", write_csv)):
+        vals, order = per_kernel(path)
+        copies = [v for n, v in order if "copyBuffer" in n][-3:]
+        if len(copies) < 3:
+            raise SystemExit(f"{path}: the calibration copies are missing")
+        scale[label] = CALIB_BYTES / (float(np.mean(copies)) * 1024.0)
+        for name, v in vals.items():
+            if "k_dec_" in name:
+                short = name.split("(")[0].replace("void ", "")
+                per.setdefault(short, {})[label] = float(np.mean(v)) * 1024.0 * scale[label]
+                per[short]["n"] = len(v)
+    out.append(f"fetch_scale = {scale['fetch']:.5f}")
+    out.append(f"write_scale = {scale['write']:.5f}")
+    main_kernel = None
+    for short, d in sorted(per.items()):
+        out.append(f"# {short}: {d['n']} dispatches, fetch {d.get('fetch', 0):.0f} B, write {d.get('write', 0):.0f} B "
+                   f"per launch (scaled)")
+        if short.startswith("moe::k_dec_gateup"):
+            main_kernel = d
+    if main_kernel is None:
+        raise SystemExit("no k_dec_gateup dispatches in the counter files")
+    out.append(f"source_sha256_16 = {source_hash(GEMV_SOURCES)}")
+    out.append(f"hbm_bytes_per_launch = {main_kernel.get('fetch', 0) + main_kernel.get('write', 0):.0f}")
+    return out
+
+
 def run_decode_steps(fn, n):
     import torch
     torch.cuda.synchronize()
@@ -184,9 +236,10 @@ def run_decode_steps(fn, n):
     return (time.perf_counter() - t0) / max(n, 1)
 
 
-def stage_times(cfg, wts, xs, out, prefill, n, ev, ws):
+def stage_times(cfg, wts, xs, out, prefill, n, ev, ws, per_step=None):
     """Average per-stage milliseconds over n profiled steps: HIP events attached to the
-    stages' first and last kernel dispatches on the launch stream."""
+    stages' first and last kernel dispatches on the launch stream.  per_step, when a
+    list, receives each step's first-kernel-start to last-kernel-end milliseconds."""
     import torch
     from routed_expert_mlp_amd import capi
     names = capi.stage_names(cfg, xs[0].shape[0], prefill)
@@ -199,6 +252,8 @@ def stage_times(cfg, wts, xs, out, prefill, n, ev, ws):
             ev.sync(evs[-1])
             for j in range(len(names)):
                 sums[j] += ev.elapsed_ms(evs[2 * j], evs[2 * j + 1])
+            if per_step is not None:
+                per_step.append(ev.elapsed_ms(evs[0], evs[-1]))
     finally:
         torch.cuda.synchronize()
         ev.destroy(evs)
@@ -257,6 +312,21 @@ def cpu_baseline(w, budget_s):
 
 def main():
     args = parse()
+    if args.summarize_traffic:
+        lines = summarize_traffic(*args.summarize_traffic)
+        head = ["# HBM traffic of the one-token decode kernels, flash_decode_t1 (T=1, H=4096, I=1536, E=288, K=8,",
+                "# Is=1536), from two rocprofv3 counter runs on one MI355X (from the repository root):",
+                "#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch -o run -- \\",
+                "#       python3 bench.py --steps 20 --warmup 5 --no-prefill --no-extra-decode --no-cpu-baseline --calibrate-copy",
+                "#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write -o run -- (same)",
+                "#   python3 bench.py --summarize-traffic <fetch counter_collection.csv> <write counter_collection.csv>",
+                "# FETCH_SIZE / WRITE_SIZE are KiB per dispatch; each is scaled so that the run's 512 MiB device",
+                "# copies read and write 512 MiB.  bench.py reports hbm_bytes_per_launch as roofline.traffic while",
+                "# source_sha256_16 matches the kernel sources."]
+        with open(TRAFFIC_FILE, "w") as f:
+            f.write("\n".join(head + lines) + "\n")
+        print("\n".join(lines))
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on one GPU only (the layer holds all 288 experts on "
                                    "one MI355X); --gpus N>1 is not supported"}))
@@ -299,8 +369,24 @@ def main():
     gbs = step_bytes / sec / 1e9
 
     n_prof = max(50, min(args.steps, 500))
-    st = stage_times(cfg, wts, xs, outs, False, n_prof, ev, ws)
+    step_ms = []
+    st = stage_times(cfg, wts, xs, outs, False, n_prof, ev, ws, step_ms)
     prof_step_ms = sum(st.values())
+    p10, p50, p90 = (float(v) for v in np.percentile(np.asarray(step_ms) * 1e3, [10, 50, 90]))
+    # warm: one weight copy, so the 8 experts + shared + router (~128 MB) stay in the 256 MB MALL
+    for i in range(20):
+        capi.moe_mlp_decode(cfg, wts[0], xs[0], outs[0], ids[0], ws=ws)
+    sec_warm = run_decode_steps(lambda i: capi.moe_mlp_decode(cfg, wts[0], xs[0], outs[0], ids[0], ws=ws),
+                                args.steps)
+    if args.calibrate_copy:
+        # a plain device copy of known size, for scaling the FETCH_SIZE / WRITE_SIZE counters
+        src = torch.empty(CALIB_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     gu_ms = st["routed_gateup_shared_down"]
     # algorithmic bytes of each one-token stage
     exp13 = 2 * w.I * w.H // 2 + 2 * w.I * w.H // 16          # NVFP4 gate/up of one expert
@@ -319,7 +405,12 @@ def main():
              "decode_stage_us": {k: round(v * 1e3, 2) for k, v in st.items()},
              "decode_stage_gbs": {k: round(stage_bytes[k] / (v * 1e-3) / 1e9, 1)
                                   for k, v in st.items() if k in stage_bytes and v > 0},
-             "profiled_step_us": round(prof_step_ms * 1e3, 2)}
+             "profiled_step_us": round(prof_step_ms * 1e3, 2),
+             "profiled_step_us_p10_p50_p90": [round(p10, 2), round(p50, 2), round(p90, 2)],
+             "decode_warm": {"us_per_step": round(sec_warm * 1e6, 2),
+                             "gbs": round(decode_bytes(w, uniq[0], 1) / sec_warm / 1e9, 1),
+                             "tokens_per_s": round(1.0 / sec_warm, 1),
+                             "note": "one weight copy, resident in the 256 MB last-level cache"}}
 
     # ---------------- decode T=16 / T=64 (same weights, more tokens) ----------------
     if not args.no_extra_decode:
