@@ -55,6 +55,8 @@ struct Plan {
   size_t g_n = 0, g_expert = 0, g_count = 0, g_offset = 0, g_slots = 0;          // decode groups
   size_t count = 0, offset = 0, perm = 0, n_tiles = 0, tile_e = 0, tile_m0 = 0;  // prefill permutation
   size_t h = 0, hs = 0, y = 0, ys = 0;
+  size_t wsplit = 0;                                                             // router weight, 3 bf16 planes
+  int logit_planes = 1;
   size_t total = 0;
   int64_t max_tiles = 0;
 };
@@ -68,6 +70,12 @@ struct Alloc {
   }
 };
 
+// Prefill router logits on the matrix cores (split fp32 weight, see router.hpp)
+// when there are enough tokens and the reduction length suits the fast GEMM.
+bool mfma_logits(const moe_mlp_config* c, int64_t T, int prefill) {
+  return prefill && T >= 64 && c->hidden % 64 == 0;
+}
+
 Plan make_plan(const moe_mlp_config* c, int64_t T, int prefill) {
   Plan p;
   Alloc a;
@@ -79,7 +87,11 @@ Plan make_plan(const moe_mlp_config* c, int64_t T, int prefill) {
   const int64_t E = c->num_experts, K = c->top_k, H = c->hidden, I = c->moe_intermediate;
   const int64_t Is = c->n_shared_experts ? c->shared_intermediate : 0;
   const int64_t S = T * K;
-  p.logits = a.take(size_t(T * E) * 4);
+  if (mfma_logits(c, T, prefill)) {
+    p.logit_planes = 3;
+    p.wsplit = a.take(size_t(3 * E * H) * 2);
+  }
+  p.logits = a.take(size_t(T * E * p.logit_planes) * 4);
   p.ids = a.take(size_t(S) * 4);
   p.wts = a.take(size_t(S) * 4);
   if (prefill) {
@@ -181,10 +193,10 @@ void topk_bucket(int E, const float* logits, const float* bias, int T, int K, fl
 }
 
 void topk_tokens(int E, const float* logits, const float* bias, int T, int K, float rsf, int32_t* ids,
-                 float* wts, int32_t* ids_out, float* w_out, hipStream_t s, Ev ev) {
+                 float* wts, int32_t* ids_out, float* w_out, hipStream_t s, Ev ev, int planes = 1) {
   with_nj(E, [&](auto nj) {
     launch(k_topk<decltype(nj)::value>, dim3(static_cast<unsigned>(cdiv(T, 4))), dim3(256), s, ev.a, ev.b, logits,
-           bias, T, E, K, rsf, ids, wts, ids_out, w_out);
+           bias, T, E, K, rsf, ids, wts, ids_out, w_out, planes);
   });
 }
 
@@ -249,6 +261,22 @@ GemmArgs bf16_gemm_args(const uint16_t* act, int kdim, const uint16_t* w, int ha
   a.ldo = ldo;
   a.limit = limit;
   return a;
+}
+
+// Router logits [T][3][E] against the three bf16 parts of the router weight
+// (k_split_bf16x3 into the workspace, then the bf16 MFMA GEMM over the stacked
+// [3E, H] parts); the top-k adds the parts.  Plain fp32 otherwise.
+void router_logits_plan(const Plan& p, void* ws, const uint16_t* x, const float* wr, float* logits, int64_t T,
+                        int H, int E, hipStream_t s, Ev ev) {
+  if (p.logit_planes == 1) {
+    router_logits(x, wr, logits, T, H, E, s, ev);
+    return;
+  }
+  uint16_t* planes = at<uint16_t>(ws, p.wsplit);
+  const int64_t n = static_cast<int64_t>(E) * H;
+  launch(k_split_bf16x3, dim3(static_cast<unsigned>(cdiv(n / 8, 256))), dim3(256), s, ev.a, nullptr, wr, planes, n);
+  gemm<false, GEMM_DOWN_F32, false>(bf16_gemm_args(x, H, planes, 3 * E, static_cast<int>(T), logits, 3 * E, 1.0f),
+                                    cdiv(T, GM_BM), s, Ev{nullptr, ev.b});
 }
 
 const char* const kDecodeStages[] = {"router_logits", "topk_bucket", "shared_gateup", "routed_gateup",
@@ -387,9 +415,9 @@ int run_layer(const moe_mlp_config* c, const moe_mlp_weights* w, const uint16_t*
     decode1(c, w, x, out, ids_out, w_out, logits, ids, wts, h, hs, ys, s, ev(0), ev(1), ev(2));
     return launch_status();
   }
-  router_logits(x, w->router_w, logits, T, H, E, s, ev(0));
+  router_logits_plan(p, ws, x, w->router_w, logits, T, H, E, s, ev(0));
   if (prefill) {
-    topk_tokens(E, logits, w->router_bias, Ti, K, rsf, ids, wts, ids_out, w_out, s, ev(1));
+    topk_tokens(E, logits, w->router_bias, Ti, K, rsf, ids, wts, ids_out, w_out, s, ev(1), p.logit_planes);
     Perm pm{at<int32_t>(ws, p.count), at<int32_t>(ws, p.offset), at<int32_t>(ws, p.perm),
             at<int32_t>(ws, p.n_tiles), at<int32_t>(ws, p.tile_e), at<int32_t>(ws, p.tile_m0)};
     const Ev pe = ev(2);
@@ -545,9 +573,9 @@ int moe_router_topk(const moe_mlp_config* cfg, const float* router_w, const floa
   if (ws_bytes < p.total) return MOE_MLP_ERR_WORKSPACE_TOO_SMALL;
   hipStream_t s = static_cast<hipStream_t>(stream);
   float* logits = at<float>(workspace, p.logits);
-  router_logits(x, router_w, logits, T, cfg->hidden, cfg->num_experts, s, Ev{});
+  router_logits_plan(p, workspace, x, router_w, logits, T, cfg->hidden, cfg->num_experts, s, Ev{});
   topk_tokens(cfg->num_experts, logits, router_bias, static_cast<int>(T), cfg->top_k,
-              cfg->routed_scaling_factor, ids, w, nullptr, nullptr, s, Ev{});
+              cfg->routed_scaling_factor, ids, w, nullptr, nullptr, s, Ev{}, p.logit_planes);
   return launch_status();
 }
 

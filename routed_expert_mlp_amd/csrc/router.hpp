@@ -188,17 +188,24 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
   return ab > cd ? ab : cd;
 }
 
+// Logit e of a row: one fp32 value, or (planes == 3, the split-weight router
+// GEMM) the sum of the three partial logits against the hi, mid and lo bf16
+// parts of the router weight, added as (lo + mid) + hi.
+__device__ __forceinline__ float logit_of(const float* __restrict__ lrow, int E, int planes, int e) {
+  return planes == 3 ? (lrow[2 * E + e] + lrow[E + e]) + lrow[e] : lrow[e];
+}
+
 template <int NJ>
 __device__ __forceinline__ int topk_wave(const float* __restrict__ lrow, const float* __restrict__ bias, int E,
                                          int K, float rsf, int want, int32_t* ids, float* wts, int32_t* ids2,
-                                         float* wts2) {
+                                         float* wts2, int planes = 1) {
   const int lane = threadIdx.x & 63;
   uint64_t key[NJ];
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
     const int e = lane + 64 * j;
     key[j] = e < E ? u64_of(0xFFFFFFFFu - static_cast<uint32_t>(e),
-                            f32_order_bits(1.0f / (1.0f + expf(-lrow[e])) + bias[e]))
+                            f32_order_bits(1.0f / (1.0f + expf(-logit_of(lrow, E, planes, e))) + bias[e]))
                    : 0;                          // below every real key
   }
 #pragma unroll
@@ -225,7 +232,7 @@ __device__ __forceinline__ int topk_wave(const float* __restrict__ lrow, const f
   }
   if (ids) {
     // the same expression as above on the same logit: the same bits
-    const float my_s = lane < K ? 1.0f / (1.0f + expf(-lrow[my_id])) : 0.0f;
+    const float my_s = lane < K ? 1.0f / (1.0f + expf(-logit_of(lrow, E, planes, my_id))) : 0.0f;
     float sum = 0.0f;
     for (int k = 0; k < K; ++k) sum += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_s), k));
     if (lane < K) {
@@ -242,12 +249,49 @@ __device__ __forceinline__ int topk_wave(const float* __restrict__ lrow, const f
 template <int NJ>
 __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ logits, const float* __restrict__ bias,
                                               int T, int E, int K, float rsf, int32_t* __restrict__ ids,
-                                              float* __restrict__ wts, int32_t* ids_out, float* w_out) {
+                                              float* __restrict__ wts, int32_t* ids_out, float* w_out,
+                                              int planes) {
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
   const int64_t o = static_cast<int64_t>(t) * K;
-  topk_wave<NJ>(logits + static_cast<int64_t>(t) * E, bias, E, K, rsf, 0, ids + o, wts + o,
-                ids_out ? ids_out + o : nullptr, w_out ? w_out + o : nullptr);
+  topk_wave<NJ>(logits + static_cast<int64_t>(t) * E * planes, bias, E, K, rsf, 0, ids + o, wts + o,
+                ids_out ? ids_out + o : nullptr, w_out ? w_out + o : nullptr, planes);
+}
+
+// ---------------------------------------------------------------------------
+// Router weight for the matrix cores: each fp32 w splits exactly into three
+// bf16 parts, hi = bf16(w), mid = bf16(w - hi), lo = bf16(w - hi - mid) (each
+// difference is exact in fp32 and the last part has at most 8 significant
+// bits left), so x . w = x . hi + x . mid + x . lo with every bf16 x bf16
+// product exact in fp32.  Planes [3][n] (hi, mid, lo); 8 values per thread.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_split_bf16x3(const float* __restrict__ w, uint16_t* __restrict__ planes,
+                                                      int64_t n) {
+  const int64_t i = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) * 8;
+  if (i >= n) return;
+  const float4 a = *reinterpret_cast<const float4*>(w + i);
+  const float4 b = *reinterpret_cast<const float4*>(w + i + 4);
+  const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+  uint32_t hi[4], mid[4], lo[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    float r0[2], r1[2], r2[2];
+    uint16_t h[2], m[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      r0[u] = v[2 * q + u];
+      h[u] = f32_to_bf16(r0[u]);
+      r1[u] = r0[u] - bf16_to_f32(h[u]);
+      m[u] = f32_to_bf16(r1[u]);
+      r2[u] = r1[u] - bf16_to_f32(m[u]);
+    }
+    hi[q] = static_cast<uint32_t>(h[0]) | (static_cast<uint32_t>(h[1]) << 16);
+    mid[q] = static_cast<uint32_t>(m[0]) | (static_cast<uint32_t>(m[1]) << 16);
+    lo[q] = pack_bf16x2(r2[0], r2[1]);
+  }
+  *reinterpret_cast<uint4*>(planes + i) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+  *reinterpret_cast<uint4*>(planes + n + i) = make_uint4(mid[0], mid[1], mid[2], mid[3]);
+  *reinterpret_cast<uint4*>(planes + 2 * n + i) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
 }
 
 // ---------------------------------------------------------------------------
