@@ -360,12 +360,160 @@ __device__ __forceinline__ void gemm_fast_mainloop(const GemmArgs& a, uint4 (&L0
   }
 }
 
+// The MTV A fragments of one k-step from LDS: ds_read_b128 at base +
+// mt * 4096 bytes, in one asm statement that also waits for them, so the
+// compiler adds no wait of its own for LDS DMA (see gemm_dma_mainloop).
+// Early-clobber outputs: every read of the block uses the address register.
+template <int MTV>
+__device__ __forceinline__ void lds_a_frags(uint32_t base, bf16x8 (&af)[MTV]) {
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  u32x4 v0, v1, v2, v3;
+  if constexpr (MTV == 1) {
+    asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=&v"(v0) : "v"(base) : "memory");
+  } else if constexpr (MTV == 2) {
+    asm volatile("ds_read_b128 %0, %2\n\tds_read_b128 %1, %2 offset:4096\n\ts_waitcnt lgkmcnt(0)"
+                 : "=&v"(v0), "=&v"(v1) : "v"(base) : "memory");
+  } else if constexpr (MTV == 3) {
+    asm volatile("ds_read_b128 %0, %3\n\tds_read_b128 %1, %3 offset:4096\n\tds_read_b128 %2, %3 offset:8192\n\t"
+                 "s_waitcnt lgkmcnt(0)"
+                 : "=&v"(v0), "=&v"(v1), "=&v"(v2) : "v"(base) : "memory");
+  } else {
+    asm volatile("ds_read_b128 %0, %4\n\tds_read_b128 %1, %4 offset:4096\n\tds_read_b128 %2, %4 offset:8192\n\t"
+                 "ds_read_b128 %3, %4 offset:12288\n\ts_waitcnt lgkmcnt(0)"
+                 : "=&v"(v0), "=&v"(v1), "=&v"(v2), "=&v"(v3) : "v"(base) : "memory");
+  }
+  af[0] = __builtin_bit_cast(bf16x8, v0);
+  if constexpr (MTV > 1) af[1] = __builtin_bit_cast(bf16x8, v1);
+  if constexpr (MTV > 2) af[2] = __builtin_bit_cast(bf16x8, v2);
+  if constexpr (MTV > 3) af[3] = __builtin_bit_cast(bf16x8, v3);
+}
+
+// This lane's NVFP4 operand of one stage from LDS: the 16-byte code chunks of
+// its two columns (n-tile stride 4096 bytes) and the E4M3 scale words (stride
+// 1024 bytes), in one asm statement that waits for them.
+__device__ __forceinline__ void lds_b_stage(uint32_t cbase, uint32_t sbase, uint4 (&c)[2], uint32_t (&sc)[2]) {
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  u32x4 c0, c1;
+  uint32_t s0, s1;
+  asm volatile("ds_read_b128 %0, %4\n\tds_read_b128 %1, %4 offset:4096\n\tds_read_b32 %2, %5\n\t"
+               "ds_read_b32 %3, %5 offset:1024\n\ts_waitcnt lgkmcnt(0)"
+               : "=&v"(c0), "=&v"(c1), "=&v"(s0), "=&v"(s1) : "v"(cbase), "v"(sbase) : "memory");
+  c[0] = make_uint4(c0.x, c0.y, c0.z, c0.w);
+  c[1] = make_uint4(c1.x, c1.y, c1.z, c1.w);
+  sc[0] = s0;
+  sc[1] = s1;
+}
+
+template <typename T>
+__device__ __forceinline__ uint32_t lds_addr(T* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) T*)p));
+}
+
+// NVFP4 main loop with every operand staged by LDS DMA (global_load_lds):
+// per 64-wide k stage a lane issues 4 x 16 B of A (as above), the 16-byte
+// code chunk of each of its two weight rows, and the 4-byte scale word of
+// each row that holds both of its 16-column blocks' E4M3 scales.  The only
+// vector memory operations in flight in the loop are these DMAs, which
+// complete in issue order, so the explicit vmcnt waits (at most one later
+// stage in flight) plus a bare barrier order each stage; every LDS read is
+// an asm statement (lds_a_frags, lds_b_stage), so the compiler adds no wait
+// for all outstanding loads.  Three-stage ring, 26 KB per stage.
+template <int MTV>
+__device__ __forceinline__ void gemm_dma_mainloop(uint4 (&A0)[1024], uint4 (&A1)[1024], uint4 (&A2)[1024],
+                                                  uint4 (&C0)[512], uint4 (&C1)[512], uint4 (&C2)[512],
+                                                  uint32_t (&S0)[512], uint32_t (&S1)[512], uint32_t (&S2)[512],
+                                                  const uint16_t* arow, const uint8_t* bq, const uint8_t* bs,
+                                                  const int (&brow)[2], int wv, int lane, int g, int kdim,
+                                                  f32x16 (&acc)[4][2]) {
+  constexpr int BK = 64, LOADS = 8;
+  const int nkb = kdim / BK;
+  const uint8_t* qrow[2];
+  const uint8_t* srow[2];
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    qrow[nt] = bq + static_cast<int64_t>(brow[nt]) * (kdim >> 1);
+    srow[nt] = bs + static_cast<int64_t>(brow[nt]) * (kdim >> 4);
+  }
+  auto slotA = [&](auto c) -> uint4* {
+    constexpr int SL = decltype(c)::value;
+    if constexpr (SL == 0) return A0; else if constexpr (SL == 1) return A1; else return A2;
+  };
+  auto slotC = [&](auto c) -> uint4* {
+    constexpr int SL = decltype(c)::value;
+    if constexpr (SL == 0) return C0; else if constexpr (SL == 1) return C1; else return C2;
+  };
+  auto slotS = [&](auto c) -> uint32_t* {
+    constexpr int SL = decltype(c)::value;
+    if constexpr (SL == 0) return S0; else if constexpr (SL == 1) return S1; else return S2;
+  };
+  auto issue = [&](int k, auto slot_c) {
+    const int kg = k * BK + 32 * g;
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(arow + kg + 8 * s),
+                                       (void __attribute__((address_space(3)))*)&slotA(slot_c)[(wv * 4 + s) * 64],
+                                       16, 0, 0);
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(qrow[nt] + (kg >> 1)),
+                                       (void __attribute__((address_space(3)))*)&slotC(slot_c)[(nt * 4 + wv) * 64],
+                                       16, 0, 0);
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(srow[nt] + 4 * k),
+                                       (void __attribute__((address_space(3)))*)&slotS(slot_c)[(nt * 4 + wv) * 64],
+                                       4, 0, 0);
+    }
+  };
+  auto compute = [&](auto slot_c) {
+    uint4 cw[2];
+    uint32_t sw[2];
+    lds_b_stage(lds_addr(&slotC(slot_c)[wv * 64 + lane]), lds_addr(&slotS(slot_c)[wv * 64 + lane]), cw, sw);
+    // this lane's two scale bytes (its 32 columns = two 16-blocks) sit at bytes 2g, 2g+1
+    const uint32_t s0 = sw[0] >> (16 * g), s1 = sw[1] >> (16 * g);
+    const uint32_t abase = lds_addr(&slotA(slot_c)[lane]);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      bf16x8 af[MTV];
+      lds_a_frags<MTV>(abase + s * 1024, af);
+      bf16x8 bfrag[2];
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        const uint4 c = cw[nt];
+        const uint32_t word = s == 0 ? c.x : s == 1 ? c.y : s == 2 ? c.z : c.w;
+        const uint32_t sb = nt == 0 ? s0 : s1;
+        const float scale = (s < 2) ? e4m3_to_f32<0>(sb) : e4m3_to_f32<1>(sb);
+        uint32_t o[4];
+        e2m1x8_scaled_bf16(word, scale, o);
+        bfrag[nt] = __builtin_bit_cast(bf16x8, make_uint4(o[0], o[1], o[2], o[3]));
+      }
+#pragma unroll
+      for (int mt = 0; mt < MTV; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+          acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mt], bfrag[nt], acc[mt][nt], 0, 0, 0);
+    }
+  };
+  issue(0, std::integral_constant<int, 0>{});
+  if (1 < nkb) issue(1, std::integral_constant<int, 1>{});
+  auto step = [&](int k, auto slot_c) {
+    constexpr int SL = decltype(slot_c)::value;
+    if (k >= nkb) return;
+    if (k + 1 < nkb) __builtin_amdgcn_s_waitcnt(waitcnt_vm(LOADS));   // stage k+1 may stay in flight
+    else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (k + 2 < nkb) issue(k + 2, std::integral_constant<int, (SL + 2) % 3>{});
+    compute(slot_c);
+  };
+  for (int k = 0; k < nkb; k += 3) {
+    step(k, std::integral_constant<int, 0>{});
+    step(k + 1, std::integral_constant<int, 1>{});
+    step(k + 2, std::integral_constant<int, 2>{});
+  }
+}
+
 template <bool NVFP4, int MODE, bool ROUTED, int NST>
 __global__ __launch_bounds__(256, 2) void k_gemm_fast(GemmArgs a) {
-  __shared__ uint4 L0[1024];
-  __shared__ uint4 L1[1024];
-  __shared__ uint4 L2[NST > 2 ? 1024 : 1];
-  __shared__ uint4 L3[NST > 3 ? 1024 : 1];
   // work item -> (tile, column block), XCD-aware (see above)
   const int nbn = a.n_blocks;
   const int ntl = ROUTED ? *a.n_tiles : static_cast<int>(cdiv(a.T, GM_BM));
@@ -420,11 +568,27 @@ __global__ __launch_bounds__(256, 2) void k_gemm_fast(GemmArgs a) {
     for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
       for (int j = 0; j < 16; ++j) acc[mt][nt][j] = 0.0f;
+  if constexpr (NVFP4) {
+    __shared__ uint4 A0[1024], A1[1024], A2[1024];
+    __shared__ uint4 C0[512], C1[512], C2[512];
+    __shared__ uint32_t S0[512], S1[512], S2[512];
+    switch (mt_valid) {
+      case 1: gemm_dma_mainloop<1>(A0, A1, A2, C0, C1, C2, S0, S1, S2, arow, bq, bs, brow, wv, lane, g, kdim, acc); break;
+      case 2: gemm_dma_mainloop<2>(A0, A1, A2, C0, C1, C2, S0, S1, S2, arow, bq, bs, brow, wv, lane, g, kdim, acc); break;
+      case 3: gemm_dma_mainloop<3>(A0, A1, A2, C0, C1, C2, S0, S1, S2, arow, bq, bs, brow, wv, lane, g, kdim, acc); break;
+      default: gemm_dma_mainloop<4>(A0, A1, A2, C0, C1, C2, S0, S1, S2, arow, bq, bs, brow, wv, lane, g, kdim, acc); break;
+    }
+  } else {
+  __shared__ uint4 L0[1024];
+  __shared__ uint4 L1[1024];
+  __shared__ uint4 L2[NST > 2 ? 1024 : 1];
+  __shared__ uint4 L3[NST > 3 ? 1024 : 1];
   switch (mt_valid) {
     case 1: gemm_fast_mainloop<NVFP4, NST, 1>(a, L0, L1, *reinterpret_cast<uint4(*)[1024]>(&L2[0]), *reinterpret_cast<uint4(*)[1024]>(&L3[0]), arow, bq, bs, brow, wv, lane, g, kdim, acc); break;
     case 2: gemm_fast_mainloop<NVFP4, NST, 2>(a, L0, L1, *reinterpret_cast<uint4(*)[1024]>(&L2[0]), *reinterpret_cast<uint4(*)[1024]>(&L3[0]), arow, bq, bs, brow, wv, lane, g, kdim, acc); break;
     case 3: gemm_fast_mainloop<NVFP4, NST, 3>(a, L0, L1, *reinterpret_cast<uint4(*)[1024]>(&L2[0]), *reinterpret_cast<uint4(*)[1024]>(&L3[0]), arow, bq, bs, brow, wv, lane, g, kdim, acc); break;
     default: gemm_fast_mainloop<NVFP4, NST, 4>(a, L0, L1, *reinterpret_cast<uint4(*)[1024]>(&L2[0]), *reinterpret_cast<uint4(*)[1024]>(&L3[0]), arow, bq, bs, brow, wv, lane, g, kdim, acc); break;
+  }
   }
   float g0 = 1.0f, g1 = 1.0f;
   if (ROUTED && a.gscale) {
