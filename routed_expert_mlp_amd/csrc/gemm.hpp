@@ -415,9 +415,9 @@ __device__ __forceinline__ uint32_t lds_addr(T* p) {
 // each row that holds both of its 16-column blocks' E4M3 scales.  The only
 // vector memory operations in flight in the loop are these DMAs, which
 // complete in issue order, so the explicit vmcnt waits (at most one later
-// stage in flight) plus a bare barrier order each stage; every LDS read is
-// an asm statement (lds_a_frags, lds_b_stage), so the compiler adds no wait
-// for all outstanding loads.  Three-stage ring, 26 KB per stage.
+// stage in flight) plus a bare barrier order each stage, and the compiler
+// adds no wait for all outstanding loads (see compute() for which LDS reads
+// are asm statements).  Three-stage ring, 26 KB per stage.
 template <int MTV>
 __device__ __forceinline__ void gemm_dma_mainloop(uint4 (&A0)[1024], uint4 (&A1)[1024], uint4 (&A2)[1024],
                                                   uint4 (&C0)[512], uint4 (&C1)[512], uint4 (&C2)[512],
@@ -464,16 +464,33 @@ __device__ __forceinline__ void gemm_dma_mainloop(uint4 (&A0)[1024], uint4 (&A1)
     }
   };
   auto compute = [&](auto slot_c) {
+    // Slot 0 is read first after the loop back-edge, where the compiler
+    // cannot tell which ring slots still have DMA in flight and would wait
+    // for all of them: its reads are asm.  Slots 1 and 2 use plain LDS reads,
+    // which the compiler interleaves with the MFMAs.
+    constexpr bool ASM_READS = decltype(slot_c)::value == 0;
     uint4 cw[2];
     uint32_t sw[2];
-    lds_b_stage(lds_addr(&slotC(slot_c)[wv * 64 + lane]), lds_addr(&slotS(slot_c)[wv * 64 + lane]), cw, sw);
+    if constexpr (ASM_READS) {
+      lds_b_stage(lds_addr(&slotC(slot_c)[wv * 64 + lane]), lds_addr(&slotS(slot_c)[wv * 64 + lane]), cw, sw);
+    } else {
+      cw[0] = slotC(slot_c)[wv * 64 + lane];
+      cw[1] = slotC(slot_c)[256 + wv * 64 + lane];
+      sw[0] = slotS(slot_c)[wv * 64 + lane];
+      sw[1] = slotS(slot_c)[256 + wv * 64 + lane];
+    }
     // this lane's two scale bytes (its 32 columns = two 16-blocks) sit at bytes 2g, 2g+1
     const uint32_t s0 = sw[0] >> (16 * g), s1 = sw[1] >> (16 * g);
     const uint32_t abase = lds_addr(&slotA(slot_c)[lane]);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       bf16x8 af[MTV];
-      lds_a_frags<MTV>(abase + s * 1024, af);
+      if constexpr (ASM_READS) {
+        lds_a_frags<MTV>(abase + s * 1024, af);
+      } else {
+#pragma unroll
+        for (int mt = 0; mt < MTV; ++mt) af[mt] = __builtin_bit_cast(bf16x8, slotA(slot_c)[(mt * 4 + s) * 64 + lane]);
+      }
       bf16x8 bfrag[2];
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) {
