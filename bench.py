@@ -414,7 +414,7 @@ def main():
 
     # ---------------- decode T=16 / T=64 (same weights, more tokens) ----------------
     if not args.no_extra_decode:
-        for T in (16, 64):
+        for T in (2, 4, 16, 64):
             xs_t = [x_dev(w, range(100 + r * T, 100 + (r + 1) * T), dev) for r in range(R)]
             out_t = [torch.empty((T, w.H), dtype=torch.bfloat16, device=dev) for _ in range(R)]
             ids_t = [torch.empty((T, w.K), dtype=torch.int32, device=dev) for _ in range(R)]

@@ -65,7 +65,11 @@ __device__ __forceinline__ float bf16_chunk_dot(uint4 w, const uint32_t* xp, flo
 }
 
 // Grid: x = row blocks of 4*RW (gate/up: gate rows), y = token groups.
-template <bool NVFP4, int MODE, int RW>
+// NC > 0: every row has at most 64*NC chunks; a wavefront loads all of its
+// rows' chunks (NC per lane) before any arithmetic and keeps them in
+// registers for every token pass, so it waits for memory once.  NC == 0:
+// rows of any length, one chunk per lane per loop iteration.
+template <bool NVFP4, int MODE, int RW, int NC = 0>
 __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
   constexpr int NR = (MODE == GEMV_GATEUP) ? 2 * RW : RW;   // weight rows per wavefront
   constexpr int XW = NVFP4 ? 16 : 4;                        // activation words per chunk
@@ -102,6 +106,27 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
       g0 = a.gscale[e];
     }
   }
+  constexpr int NCW = NC > 0 ? NC : 1;
+  uint4 wr[NR][NCW];
+  uint32_t scr[NR][NCW];
+  if constexpr (NC > 0) {
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
+      const int c = lane + 64 * i;
+      const bool ok = c < nch;
+#pragma unroll
+      for (int r = 0; r < NR; ++r) {
+        if (NVFP4) {
+          wr[r][i] = ok ? *reinterpret_cast<const uint4*>(wq + rows[r] * row_q + 16 * c) : make_uint4(0, 0, 0, 0);
+          scr[r][i] = ok ? *reinterpret_cast<const uint16_t*>(wsc + rows[r] * row_s + 2 * c) : 0u;
+        } else {
+          wr[r][i] = ok ? *reinterpret_cast<const uint4*>(a.wb + static_cast<int64_t>(rows[r]) * a.cols + 8 * c)
+                        : make_uint4(0, 0, 0, 0);
+          scr[r][i] = 0u;
+        }
+      }
+    }
+  }
   for (int t0 = 0; t0 < n_tok; t0 += GEMV_TC) {
     const int nt = min(GEMV_TC, n_tok - t0);
     int in_row[GEMV_TC], out_row[GEMV_TC];
@@ -117,18 +142,7 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
     for (int r = 0; r < NR; ++r)
 #pragma unroll
       for (int t = 0; t < GEMV_TC; ++t) acc[r][t] = 0.0f;
-    for (int c = lane; c < nch; c += 64) {
-      uint4 w[NR];
-      uint32_t sc[NR];
-#pragma unroll
-      for (int r = 0; r < NR; ++r) {
-        if (NVFP4) {
-          w[r] = *reinterpret_cast<const uint4*>(wq + rows[r] * row_q + 16 * c);
-          sc[r] = *reinterpret_cast<const uint16_t*>(wsc + rows[r] * row_s + 2 * c);
-        } else {
-          w[r] = *reinterpret_cast<const uint4*>(a.wb + static_cast<int64_t>(rows[r]) * a.cols + 8 * c);
-        }
-      }
+    auto chunk = [&](int c, const uint4 (&w)[NR], const uint32_t (&sc)[NR]) {
 #pragma unroll
       for (int t = 0; t < GEMV_TC; ++t) {
         if (t < nt) {
@@ -144,6 +158,38 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
           for (int r = 0; r < NR; ++r)
             acc[r][t] = NVFP4 ? nvfp4_chunk_dot(w[r], sc[r], xp, acc[r][t]) : bf16_chunk_dot(w[r], xp, acc[r][t]);
         }
+      }
+    };
+    if constexpr (NC > 0) {
+#pragma unroll
+      for (int i = 0; i < NC; ++i) {
+        const int c = lane + 64 * i;
+        if (c < nch) {
+          uint4 w[NR];
+          uint32_t sc[NR];
+#pragma unroll
+          for (int r = 0; r < NR; ++r) {
+            w[r] = wr[r][i];
+            sc[r] = scr[r][i];
+          }
+          chunk(c, w, sc);
+        }
+      }
+    } else {
+      for (int c = lane; c < nch; c += 64) {
+        uint4 w[NR];
+        uint32_t sc[NR];
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+          if (NVFP4) {
+            w[r] = *reinterpret_cast<const uint4*>(wq + rows[r] * row_q + 16 * c);
+            sc[r] = *reinterpret_cast<const uint16_t*>(wsc + rows[r] * row_s + 2 * c);
+          } else {
+            w[r] = *reinterpret_cast<const uint4*>(a.wb + static_cast<int64_t>(rows[r]) * a.cols + 8 * c);
+            sc[r] = 0u;
+          }
+        }
+        chunk(c, w, sc);
       }
     }
 #pragma unroll

@@ -210,10 +210,28 @@ void router_logits(const uint16_t* x, const float* wr, float* logits, int64_t T,
   }
 }
 
+// BF16 rows of up to 8 chunks per lane (the shared expert, one grid of few
+// row blocks) take the all-loads-first kernel (NC = chunks per lane).  The
+// routed NVFP4 GEMVs run thousands of blocks, hide latency by occupancy, and
+// keep the looping kernel: holding their chunks would double the registers.
 template <bool NVFP4, int MODE, int RW>
 void gemv(const GemvArgs& a, int groups, hipStream_t s, Ev ev) {
   const dim3 grid(static_cast<unsigned>(cdiv(a.half_rows, 4 * RW)), static_cast<unsigned>(groups));
-  launch(k_gemv<NVFP4, MODE, RW>, grid, dim3(256), s, ev.a, ev.b, a);
+  const int nch = NVFP4 ? (a.cols >> 5) : (a.cols >> 3);
+  if constexpr (NVFP4) {
+    launch(k_gemv<NVFP4, MODE, RW, 0>, grid, dim3(256), s, ev.a, ev.b, a);
+    return;
+  } else {
+  switch (static_cast<int>(cdiv(nch, 64))) {
+    case 1: launch(k_gemv<NVFP4, MODE, RW, 1>, grid, dim3(256), s, ev.a, ev.b, a); break;
+    case 2: launch(k_gemv<NVFP4, MODE, RW, 2>, grid, dim3(256), s, ev.a, ev.b, a); break;
+    case 3: launch(k_gemv<NVFP4, MODE, RW, 3>, grid, dim3(256), s, ev.a, ev.b, a); break;
+    case 4: launch(k_gemv<NVFP4, MODE, RW, 4>, grid, dim3(256), s, ev.a, ev.b, a); break;
+    case 5: case 6: launch(k_gemv<NVFP4, MODE, RW, 6>, grid, dim3(256), s, ev.a, ev.b, a); break;
+    case 7: case 8: launch(k_gemv<NVFP4, MODE, RW, 8>, grid, dim3(256), s, ev.a, ev.b, a); break;
+    default: launch(k_gemv<NVFP4, MODE, RW, 0>, grid, dim3(256), s, ev.a, ev.b, a); break;
+  }
+  }
 }
 
 // Reduction lengths that are a multiple of 64 take the 32x32x16-MFMA kernel
