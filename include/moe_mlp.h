@@ -173,7 +173,9 @@ int moe_mlp_prefill(const moe_mlp_config* cfg, const moe_mlp_weights* w, const u
  * routed_gateup, shared_down, routed_down, combine; ROUTED prefill
  * router_logits, topk, permute, routed_gateup, routed_down, shared_gateup,
  * shared_down, combine; DENSE dense_gateup, dense_down.  A stage with
- * nothing to run (no shared expert) records both events back to back.
+ * nothing to run records both events back to back: no shared expert, or
+ * (decode of T <= 16 tokens, H <= 4096, Is <= 2048) shared_gateup, whose
+ * work runs inside router_logits.
  */
 int moe_mlp_forward_profiled(const moe_mlp_config* cfg, const moe_mlp_weights* w, const uint16_t* x,
                              int64_t T, uint16_t* out, int32_t* ids_out, float* w_out, void* workspace,

@@ -98,6 +98,85 @@ __global__ __launch_bounds__(256) void k_dec_logits_shared(const uint16_t* __res
 }
 
 // -------------------------------------------------------------------------
+// 1'. The same grid for T <= 16 tokens (general decode): each wavefront
+// loads its router row (or shared gate/up row pair) once, then runs every
+// token's dot product against it; x rows are re-read per token (they stay in
+// the caches).  Per token the arithmetic and reduction order are those of
+// k_dec_logits_shared.  Writes logits [T][E] and hs [T][Is].
+// -------------------------------------------------------------------------
+template <int NR, int NS>
+__global__ __launch_bounds__(256) void k_dec_logits_shared_t(const uint16_t* __restrict__ x,
+                                                             const float* __restrict__ wr,
+                                                             float* __restrict__ logits, int E, int H,
+                                                             const uint16_t* __restrict__ sw13, int Is,
+                                                             uint16_t* __restrict__ hs, float L, int n_logit_blocks,
+                                                             int T) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  if (static_cast<int>(blockIdx.x) < n_logit_blocks) {
+    const int e = blockIdx.x * 4 + wv;
+    if (e >= E) return;
+    const float4* row = reinterpret_cast<const float4*>(wr + static_cast<int64_t>(e) * H);
+    float4 w[NR];
+    const int nch = H >> 2;
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+      const int c = lane + 64 * i;
+      w[i] = c < nch ? row[c] : make_float4(0, 0, 0, 0);
+    }
+    for (int t = 0; t < T; ++t) {
+      const uint2* xv = reinterpret_cast<const uint2*>(x + static_cast<int64_t>(t) * H);
+      uint2 xs[NR];
+#pragma unroll
+      for (int i = 0; i < NR; ++i) {
+        const int c = lane + 64 * i;
+        xs[i] = c < nch ? xv[c] : make_uint2(0, 0);
+      }
+      float acc = 0.0f;
+#pragma unroll
+      for (int i = 0; i < NR; ++i) {
+        acc = fmaf(__uint_as_float(xs[i].x << 16), w[i].x, acc);
+        acc = fmaf(__uint_as_float(xs[i].x & 0xffff0000u), w[i].y, acc);
+        acc = fmaf(__uint_as_float(xs[i].y << 16), w[i].z, acc);
+        acc = fmaf(__uint_as_float(xs[i].y & 0xffff0000u), w[i].w, acc);
+      }
+      acc = wave_sum(acc);
+      if (lane == 0) logits[static_cast<int64_t>(t) * E + e] = acc;
+    }
+  } else {
+    const int j = (blockIdx.x - n_logit_blocks) * 4 + wv;
+    if (j >= Is) return;
+    const uint4* g = reinterpret_cast<const uint4*>(sw13 + static_cast<int64_t>(j) * H);
+    const uint4* u = reinterpret_cast<const uint4*>(sw13 + static_cast<int64_t>(Is + j) * H);
+    const int nch = H >> 3;
+    uint4 wg[NS], wu[NS];
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+      const int c = lane + 64 * i;
+      const bool ok = c < nch;
+      wg[i] = ok ? g[c] : make_uint4(0, 0, 0, 0);
+      wu[i] = ok ? u[c] : make_uint4(0, 0, 0, 0);
+    }
+    for (int t = 0; t < T; ++t) {
+      const uint4* xv = reinterpret_cast<const uint4*>(x + static_cast<int64_t>(t) * H);
+      float ag = 0.0f, au = 0.0f;
+#pragma unroll
+      for (int i = 0; i < NS; ++i) {
+        const int c = lane + 64 * i;
+        const uint4 xs = c < nch ? xv[c] : make_uint4(0, 0, 0, 0);
+        const uint32_t xp[4] = {xs.x, xs.y, xs.z, xs.w};
+        ag = dot2_bf16(wg[i].x, xp[0], ag); ag = dot2_bf16(wg[i].y, xp[1], ag);
+        ag = dot2_bf16(wg[i].z, xp[2], ag); ag = dot2_bf16(wg[i].w, xp[3], ag);
+        au = dot2_bf16(wu[i].x, xp[0], au); au = dot2_bf16(wu[i].y, xp[1], au);
+        au = dot2_bf16(wu[i].z, xp[2], au); au = dot2_bf16(wu[i].w, xp[3], au);
+      }
+      ag = wave_sum(ag);
+      au = wave_sum(au);
+      if (lane == 0) hs[static_cast<int64_t>(t) * Is + j] = f32_to_bf16(swiglu_clamped(ag, au, L));
+    }
+  }
+}
+
+// -------------------------------------------------------------------------
 // 2. shared down + top-k + routed gate/up for one token.  1-D grid:
 //  * blocks [0, n_sd): shared down rows r = (b*4 + wave)*RS .. +RS,
 //    ys[r] = sum_j W2s[r, j] hs[j] in fp32 (lane l takes the 16-byte chunks

@@ -210,10 +210,11 @@ void router_logits(const uint16_t* x, const float* wr, float* logits, int64_t T,
   }
 }
 
-// BF16 rows of up to 8 chunks per lane (the shared expert, one grid of few
-// row blocks) take the all-loads-first kernel (NC = chunks per lane).  The
-// routed NVFP4 GEMVs run thousands of blocks, hide latency by occupancy, and
-// keep the looping kernel: holding their chunks would double the registers.
+// BF16 rows of up to 8 chunks per lane (the shared expert and dense FFN) take
+// the all-loads-first kernel (NC = chunks per lane).  The routed NVFP4 GEMVs
+// keep the looping kernel: they run thousands of blocks and hide latency by
+// occupancy, and holding their chunks (with 16 activation words per chunk
+// and token) costs more registers than it saves in waits (measured).
 template <bool NVFP4, int MODE, int RW>
 void gemv(const GemvArgs& a, int groups, hipStream_t s, Ev ev) {
   const dim3 grid(static_cast<unsigned>(cdiv(a.half_rows, 4 * RW)), static_cast<unsigned>(groups));
@@ -433,7 +434,17 @@ int run_layer(const moe_mlp_config* c, const moe_mlp_weights* w, const uint16_t*
     decode1(c, w, x, out, ids_out, w_out, logits, ids, wts, h, hs, ys, s, ev(0), ev(1), ev(2));
     return launch_status();
   }
-  router_logits_plan(p, ws, x, w->router_w, logits, T, H, E, s, ev(0));
+  // decode of up to 16 tokens with H <= 4096: router logits and the shared
+  // expert's gate/up share one launch (stage router_logits; shared_gateup
+  // then records an empty stage)
+  const bool fused_k1 = !prefill && T <= 16 && H <= kDec1MaxH && Is <= 2048;
+  if (fused_k1) {
+    const int nlb = static_cast<int>(cdiv(E, 4)), nsb = static_cast<int>(cdiv(Is, 4));
+    launch(k_dec_logits_shared_t<16, 8>, dim3(nlb + nsb), dim3(256), s, ev(0).a, ev(0).b, x, w->router_w, logits,
+           E, H, w->shared_w13, Is, hs, L, nlb, Ti);
+  } else {
+    router_logits_plan(p, ws, x, w->router_w, logits, T, H, E, s, ev(0));
+  }
   if (prefill) {
     topk_tokens(E, logits, w->router_bias, Ti, K, rsf, ids, wts, ids_out, w_out, s, ev(1), p.logit_planes);
     Perm pm{at<int32_t>(ws, p.count), at<int32_t>(ws, p.offset), at<int32_t>(ws, p.perm),
@@ -490,7 +501,7 @@ int run_layer(const moe_mlp_config* c, const moe_mlp_weights* w, const uint16_t*
               at<int32_t>(ws, p.g_offset), at<int32_t>(ws, p.g_slots)};
     topk_bucket(E, logits, w->router_bias, Ti, K, rsf, ids, wts, ids_out, w_out, gr, s, ev(1));
     const int groups = static_cast<int>(S < E ? S : E);
-    if (Is) gemv<false, GEMV_GATEUP, 1>(bf16_gemv_args(w->shared_w13, Is, H, Ti, x, hs, L), 1, s, ev(2));
+    if (Is && !fused_k1) gemv<false, GEMV_GATEUP, 1>(bf16_gemv_args(w->shared_w13, Is, H, Ti, x, hs, L), 1, s, ev(2));
     else empty_stage(ev(2));
     GemvArgs r{};
     r.n_groups = gr.n_groups;
