@@ -378,6 +378,31 @@ def main():
         capi.moe_mlp_decode(cfg, wts[0], xs[0], outs[0], ids[0], ws=ws)
     sec_warm = run_decode_steps(lambda i: capi.moe_mlp_decode(cfg, wts[0], xs[0], outs[0], ids[0], ws=ws),
                                 args.steps)
+    # the same steps replayed from HIP graphs of 16 steps each (one graph per starting copy)
+    graph_us = None
+    try:
+        gs = []
+        gsm = torch.cuda.Stream()
+        gsm.wait_stream(torch.cuda.current_stream())
+        for r in range(R):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=gsm):
+                for j in range(16):
+                    q = (r + j) % R
+                    capi.moe_mlp_decode(cfg, wts[q], xs[q], outs[q], ids[q], ws=ws)
+            gs.append(g)
+        for i in range(2 * R):
+            gs[i % R].replay()
+        n_rep = max(4, args.steps // 16)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(n_rep):
+            gs[i % R].replay()
+        torch.cuda.synchronize()
+        graph_us = (time.perf_counter() - t0) / (n_rep * 16) * 1e6
+        del gs
+    except RuntimeError as exc:                       # capture unsupported: report, do not fail the run
+        log(f"[bench] graph capture failed: {exc}")
     if args.calibrate_copy:
         # a plain device copy of known size, for scaling the FETCH_SIZE / WRITE_SIZE counters
         src = torch.empty(CALIB_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
@@ -407,6 +432,7 @@ def main():
                                   for k, v in st.items() if k in stage_bytes and v > 0},
              "profiled_step_us": round(prof_step_ms * 1e3, 2),
              "profiled_step_us_p10_p50_p90": [round(p10, 2), round(p50, 2), round(p90, 2)],
+             "decode_graph_us_per_step": None if graph_us is None else round(graph_us, 2),
              "decode_warm": {"us_per_step": round(sec_warm * 1e6, 2),
                              "gbs": round(decode_bytes(w, uniq[0], 1) / sec_warm / 1e9, 1),
                              "tokens_per_s": round(1.0 / sec_warm, 1),

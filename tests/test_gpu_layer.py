@@ -259,3 +259,51 @@ def test_profiled_entry_matches_plain_call(name, prefill):
         hip.hipEventDestroy(ctypes.c_void_p(evs[2 * i + 1]))
     say(f"[stages] {name}: " + ", ".join(f"{n}={t * 1e3:.1f}us" for n, t in zip(names, times)))
     assert all(t >= 0 for t in times) and sum(times) > 0
+
+
+# ---------------------------------------------------------------------------
+# HIP graph capture (hipGraph through torch.cuda.CUDAGraph): the layer's
+# launches replay from a graph.  Every replay, with eager work and a new input
+# copied into the captured input buffer in between, equals an eager call on
+# the same input bitwise.
+# ---------------------------------------------------------------------------
+
+GRAPH_CASES = [("flash_decode_t1", 1, False), ("flash_decode_t16", 4, False), ("ragged_prefill", 300, True)]
+
+
+@pytest.mark.parametrize("name,T,prefill", GRAPH_CASES, ids=[f"{c[0]}_T{c[1]}" for c in GRAPH_CASES])
+def test_hip_graph_replays_equal_eager(name, T, prefill):
+    d = device_workload(name)
+    say(f"[case] graph {name} T={T} {'prefill' if prefill else 'decode'}")
+    fn = capi.moe_mlp_prefill if prefill else capi.moe_mlp_decode
+    H, K = d.w.H, d.w.K
+    xs = [d.x[:T].clone(), d.x[T:2 * T].clone() if d.x.shape[0] >= 2 * T else d.x[:T].flip(0).contiguous()]
+    x_in = xs[0].clone()
+    out = torch.empty((T, H), dtype=torch.bfloat16, device=DEV)
+    ids = torch.empty((T, K), dtype=torch.int32, device=DEV)
+    wts = torch.empty((T, K), dtype=torch.float32, device=DEV)
+    ws = capi.workspace(d.cfg, T, prefill, DEV)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn(d.cfg, d.weights, x_in, out, ids, wts, ws=ws)          # warm-up outside capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        fn(d.cfg, d.weights, x_in, out, ids, wts, ws=ws)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        xr = xs[rep % 2]
+        ref_out = torch.empty_like(out)
+        ref_ids = torch.empty_like(ids)
+        ref_w = torch.empty_like(wts)
+        fn(d.cfg, d.weights, xr, ref_out, ref_ids, ref_w)       # eager, own workspace
+        x_in.copy_(xr)
+        out.fill_(0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), ref_out.view(torch.int16)), f"replay {rep}: output differs"
+        assert torch.equal(ids, ref_ids), f"replay {rep}: ids differ"
+        assert torch.equal(wts, ref_w), f"replay {rep}: weights differ"
+    say(f"[parity] graph {name}: 4 replays equal eager bitwise")
