@@ -85,8 +85,8 @@ extern "C" {
 
 /*
  * Layer geometry and constants.  Every field is read from the caller; none
- * has a default ("Glm5NextMlpConfig: read from the checkpoint config --
- * never defaulted", Module glm5next_mlp, Structs).
+ * has a default (Module glm5next_mlp, Structs: the config comes from the
+ * checkpoint's own config and is never filled in by the library).
  */
 typedef struct moe_mlp_config {
   int32_t kind;                  /* MOE_MLP_KIND_ROUTED or MOE_MLP_KIND_DENSE */
@@ -131,8 +131,11 @@ int moe_mlp_workspace_size(const moe_mlp_config* cfg, int64_t T, int prefill, si
 
 /*
  * Decode form ("forward": the page's one-token decode), for 1..MOE_MLP_DECODE_MAX_T
- * tokens.  Routed experts run as W4A16 GEMVs that stream the NVFP4 codes
- * once per touched expert; the BF16 shared expert as a GEMV.
+ * tokens.  Up to 63 tokens the routed experts run as W4A16 GEMVs that stream
+ * the NVFP4 codes once per touched expert (T == 1: three fused launches), and
+ * the BF16 shared expert as a GEMV.  From 64 tokens on, the call runs the
+ * grouped-GEMM kernels of moe_mlp_prefill (faster there; the workspace size
+ * and stage list follow).
  *   x        [T, H] bf16 input.
  *   out      [T, H] bf16 output.
  *   ids_out  [T, K] int32 chosen expert ids, descending biased score
@@ -168,11 +171,11 @@ int moe_mlp_prefill(const moe_mlp_config* cfg, const moe_mlp_weights* w, const u
  * (none NULL); n_events >= 2 * n_stages, else MOE_MLP_ERR_BAD_VALUE.
  * Stages (moe_mlp_stage_name): ROUTED one-token decode (T == 1, H <= 4096,
  * I and Is <= 2048) logits_shared_gateup, routed_gateup_shared_down,
- * routed_down_combine;
- * other ROUTED decode router_logits, topk_bucket, shared_gateup,
- * routed_gateup, shared_down, routed_down, combine; ROUTED prefill
- * router_logits, topk, permute, routed_gateup, routed_down, shared_gateup,
- * shared_down, combine; DENSE dense_gateup, dense_down.  A stage with
+ * routed_down_combine; other ROUTED decode below 64 tokens router_logits,
+ * topk_bucket, shared_gateup, routed_gateup, shared_down, routed_down,
+ * combine; ROUTED prefill (and decode from 64 tokens) router_logits, topk,
+ * permute, routed_gateup, routed_down, shared_gateup, shared_down, combine;
+ * DENSE dense_gateup, dense_down.  A stage with
  * nothing to run records both events back to back: no shared expert, or
  * (decode of T <= 16 tokens, H <= 4096, Is <= 2048) shared_gateup, whose
  * work runs inside router_logits.

@@ -70,6 +70,16 @@ struct Alloc {
   }
 };
 
+// The grouped-GEMM form runs prefill, and decode from this many tokens on
+// (measured: the expert GEMVs re-stream each touched expert's rows once per
+// pass of 4 of its tokens; the GEMM streams them once per 128-row tile and
+// overtakes the GEMVs from T = 64, by 2.2x at T = 256).
+constexpr int64_t kDecodeGemmMinT = 64;
+
+int gemm_form(const moe_mlp_config* c, int64_t T, int prefill) {
+  return (prefill || T >= kDecodeGemmMinT) ? 1 : 0;
+}
+
 // Prefill router logits on the matrix cores (split fp32 weight, see router.hpp)
 // when there are enough tokens and the reduction length suits the fast GEMM.
 bool mfma_logits(const moe_mlp_config* c, int64_t T, int prefill) {
@@ -202,7 +212,9 @@ void topk_tokens(int E, const float* logits, const float* bias, int T, int K, fl
 
 void router_logits(const uint16_t* x, const float* wr, float* logits, int64_t T, int H, int E, hipStream_t s,
                    Ev ev) {
-  if (T <= 16) {
+  // one workgroup per expert row up to the decode limit (the tile GEMM below
+  // has only ceil(T/64) x ceil(E/64) workgroups, too few for small T)
+  if (T <= MOE_MLP_DECODE_MAX_T) {
     launch(k_logits_gemv, dim3(E), dim3(256), s, ev.a, ev.b, x, wr, logits, static_cast<int>(T), H, E);
   } else {
     const dim3 grid(static_cast<unsigned>(cdiv(T, 64)), static_cast<unsigned>(cdiv(E, 64)));
@@ -321,7 +333,7 @@ bool decode1_ok(const moe_mlp_config* c, int64_t T, int prefill) {
 int n_stages(const moe_mlp_config* c, int64_t T, int prefill) {
   if (c->kind == MOE_MLP_KIND_DENSE) return 2;
   if (decode1_ok(c, T, prefill)) return 3;
-  return prefill ? 8 : 7;
+  return gemm_form(c, T, prefill) ? 8 : 7;
 }
 
 // One-token decode: 3 launches (see decode1.hpp).
@@ -382,6 +394,7 @@ int run_layer(const moe_mlp_config* c, const moe_mlp_weights* w, const uint16_t*
   if (!aligned(x) || !aligned(out) || !aligned(ws)) return MOE_MLP_ERR_MISALIGNED;
   if (c->kind == MOE_MLP_KIND_ROUTED && ((ids_out && !aligned(ids_out)) || (w_out && !aligned(w_out))))
     return MOE_MLP_ERR_MISALIGNED;
+  if (!decode1_ok(c, T, prefill)) prefill = gemm_form(c, T, prefill);   // from here on: the form that runs
   const Plan p = make_plan(c, T, prefill);
   if (ws_bytes < p.total) return MOE_MLP_ERR_WORKSPACE_TOO_SMALL;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -553,7 +566,7 @@ int moe_mlp_workspace_size(const moe_mlp_config* cfg, int64_t T, int prefill, si
   const int st = validate_cfg(cfg, T, prefill);
   if (st) return st;
   if (!bytes) return MOE_MLP_ERR_NULL_ARG;
-  *bytes = make_plan(cfg, T, prefill).total;
+  *bytes = make_plan(cfg, T, gemm_form(cfg, T, prefill)).total;
   return MOE_MLP_OK;
 }
 
@@ -583,7 +596,7 @@ const char* moe_mlp_stage_name(const moe_mlp_config* cfg, int64_t T, int prefill
   if (!cfg || stage < 0) return nullptr;
   if (cfg->kind == MOE_MLP_KIND_DENSE) return stage < 2 ? kDenseStages[stage] : nullptr;
   if (decode1_ok(cfg, T, prefill)) return stage < 3 ? kDecode1Stages[stage] : nullptr;
-  if (prefill) return stage < 8 ? kPrefillStages[stage] : nullptr;
+  if (gemm_form(cfg, T, prefill)) return stage < 8 ? kPrefillStages[stage] : nullptr;
   return stage < 7 ? kDecodeStages[stage] : nullptr;
 }
 

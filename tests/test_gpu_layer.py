@@ -62,28 +62,31 @@ def test_prefill_parity(name, n_sample):
 
 
 def test_decode_and_prefill_agree_on_every_token():
-    """Two different kernel paths (GEMV vs MFMA grouped GEMM) on the same 64 tokens."""
+    """Two different kernel paths (expert GEMVs below 64 tokens vs the MFMA grouped GEMM)
+    on the same 48 tokens."""
     d = device_workload("flash_decode_t64")
-    a, ida, wa = d.run(False)
-    b, idb, wb = d.run(True)
+    x = d.x[:48].contiguous()
+    a, ida, wa = d.run(False, x=x)
+    b, idb, wb = d.run(True, x=x)
     torch.cuda.synchronize()
     assert torch.equal(ida, idb)
     assert torch.allclose(wa, wb, rtol=1e-6, atol=0)
     r = rel_l2(a.float().cpu().numpy(), b.float().cpu().numpy())
-    say(f"[parity] decode vs prefill (64 tokens): rel_l2={r:.3e}")
+    say(f"[parity] decode vs prefill (48 tokens): rel_l2={r:.3e}")
     assert r < 5e-3
 
 
 def test_prefill_matches_decode_on_a_token_subset():
-    """Tokens are independent: prefill over 4096 tokens equals decode of any subset (within tolerance)."""
+    """Tokens are independent: prefill over 4096 tokens equals decode (expert GEMVs) of a
+    48-token subset (within tolerance)."""
     d = device_workload("prefill_t4096")
     out, ids, _ = d.run(True)
-    sub = torch.arange(0, 4096, 16, device=DEV)[:256]
+    sub = torch.arange(0, 4096, 85, device=DEV)[:48]
     o2, ids2, _ = d.run(False, x=d.x[sub].contiguous())
     torch.cuda.synchronize()
     assert torch.equal(ids[sub], ids2)
     r = rel_l2(out[sub].float().cpu().numpy(), o2.float().cpu().numpy())
-    say(f"[parity] prefill vs decode on 256 sampled tokens: rel_l2={r:.3e}")
+    say(f"[parity] prefill vs decode on 48 sampled tokens: rel_l2={r:.3e}")
     assert r < 5e-3
 
 
@@ -153,6 +156,14 @@ def test_minimum_hidden_size(prefill):
 
 def test_decode_maximum_tokens():
     _fresh("ragged_decode", False, n_sample=256, T=capi.DECODE_MAX_T)
+
+
+@pytest.mark.parametrize("overrides", [dict(T=63), dict(T=48, K=8, E=8), dict(T=33, K=2)],
+                         ids=["T63", "T48_E8_K8", "T33_K2"])
+def test_decode_gemv_path_below_the_gemm_switch(overrides):
+    """Ragged shapes on the expert-GEMV decode path (fewer than 64 tokens): many token
+    groups per expert, every expert touched (E=8, K=8), and K=2."""
+    _fresh("ragged_decode", False, n_sample=64, **overrides)
 
 
 def test_prefill_one_token():
