@@ -3,22 +3,22 @@
  *
  * The layer is the GLM-5.3-Flash MLP of the "Module glm5next_mlp" API page
  * (GLM-5.3-Flash MLP production surface), section "The stack this layer
- * runs":
+ * runs".  In a ROUTED layer the token's hidden vector goes through an fp32
+ * router projection; the top-k of the router scores picks K experts, each an
+ * NVFP4 gate/up projection, clamped SwiGLU and NVFP4 down projection; a BF16
+ * shared expert of the same shape runs for every token; the routed outputs,
+ * weighted, and the shared output are summed.  A DENSE layer is a single BF16
+ * gate/up, clamped SwiGLU, down FFN.
  *
- *   ROUTED:  x -> gate.weight -> logits (f32) -> router_topk -> ids[K], weights[K]
- *            x -> experts[id]: NVFP4 gate/up -> clamped SwiGLU -> NVFP4 down
- *            x -> shared expert: BF16 gate/up -> clamped SwiGLU -> BF16 down
- *            -> combine -> out
- *   DENSE:   x -> gate/up -> clamped SwiGLU -> down -> out
- *
- * with the rules of that page's section "Traps this module exists to hold":
- * the SwiGLU clamp is asymmetric (gate bounded above only, up bounded both
- * ways, limit swiglu_limit, never defaulted); the router's correction bias
- * steers selection only and the emitted weight is the unbiased sigmoid score
- * renormalised over the chosen experts of the FULL expert count, then
- * multiplied by routed_scaling_factor; the shared expert is not scaled by
- * routed_scaling_factor.  "Constants, KERNEL_MAX_TOP_K": at most 16 experts
- * per token.  The page's "forward" (decode, one token) and
+ * The rules of that page's section "Traps this module exists to hold", as
+ * implemented here: the SwiGLU clamp is asymmetric (the gate has only an
+ * upper bound, the up projection both; the limit is swiglu_limit and is never
+ * defaulted); the router's correction bias affects which experts are chosen
+ * and nothing else, the weight of a chosen expert being its plain sigmoid
+ * score divided by the sum of the chosen plain scores over the full expert
+ * count, times routed_scaling_factor; routed_scaling_factor does not touch
+ * the shared expert.  Section Constants, KERNEL_MAX_TOP_K: at most 16 experts
+ * per token.  The page's "forward" (one-token decode) and
  * "forward_prefill_gemm" (grouped-GEMM prefill) are moe_mlp_decode and
  * moe_mlp_prefill here.
  *

@@ -9,18 +9,18 @@ This is the plain definition of what the layer computes, written out in
 float64 with NumPy, one step per function, in the order the pages give:
 
   Module glm5next_mlp (GLM-5.3-Flash MLP production surface), section
-  "The stack this layer runs":
-      x -> gate.weight -> logits (f32) -> router_topk -> ids[K], weights[K]
-      x -> experts[id]: NVFP4 gate/up -> clamped SwiGLU -> NVFP4 down
-      x -> shared_experts: BF16 gate/up -> clamped SwiGLU -> BF16 down
-      -> moe_combine -> partial
-  DENSE layers: x -> gate_proj/up_proj -> clamped SwiGLU -> down_proj
+  "The stack this layer runs": a ROUTED layer projects the token onto fp32
+  router logits, picks K experts by top-k, runs each chosen expert's NVFP4
+  gate/up projection, clamped SwiGLU and NVFP4 down projection, runs the BF16
+  shared expert (same shape) on every token, and sums the weighted routed
+  outputs with the shared output; a DENSE layer is one BF16 gate/up, clamped
+  SwiGLU, down FFN;
 
 and, same page, section "Traps this module exists to hold":
-  * the SwiGLU clamp is asymmetric: gate bounded above only, up bounded both
-    ways, by swiglu_limit (never defaulted);
-  * the correction bias steers selection only; the emitted weight is the
-    unbiased sigmoid score of the chosen expert;
+  * the SwiGLU clamp is asymmetric: the gate has an upper bound only, the up
+    projection both, at swiglu_limit (never defaulted);
+  * the correction bias only changes which experts are chosen; a chosen
+    expert's weight uses its plain sigmoid score;
   * routed_scaling_factor multiplies the top-k weights; the shared expert is
     not scaled by it;
   * num_experts is the full expert count, and the weights are renormalised
@@ -36,7 +36,7 @@ Number formats (not on the pages; public specifications):
   * one fp32 global scale per (expert, projection), multiplied after the
     dot product.
 
-Readings where the pages are silent (each is listed in the design doc):
+Readings where the pages are silent:
   * the correction bias is added to the sigmoid score (score space);
   * no expert groups: one flat top-K over all E experts;
   * ids are in descending biased-score order, exact ties to the lower index;

@@ -3,7 +3,7 @@
 // "Module glm5next_mlp", forward_prefill_gemm / MOE_GROUPED_MODULE: routed
 // prefill runs each expert's sorted rows through a grouped W4A16 GEMM.  The
 // same kernel, with BF16 weights and identity rows, runs the shared expert and
-// the dense FFN ("DENSE: gate_proj/up_proj -> clamped SwiGLU -> down_proj").
+// the dense FFN (the page's DENSE layer: BF16 gate/up, clamped SwiGLU, down).
 //
 // Tiling (one workgroup = 4 wavefronts, 128 rows of A):
 //   * A (activations, bf16) is staged through LDS in MFMA-fragment order, two

@@ -1,9 +1,9 @@
-// Sigmoid router top-k of the GLM-5.3-Flash routed MLP ("Module glm5next_mlp":
-// "The stack this layer runs": gate.weight -> logits (f32) -> router_topk ->
-// ids[K], weights[K]; "Traps this module exists to hold": the correction bias
-// steers selection only, the weight is the unbiased sigmoid score
-// renormalised over the chosen experts of the full count, then multiplied by
-// routed_scaling_factor; Constants, KERNEL_MAX_TOP_K: K <= 16).
+// Sigmoid router top-k of the GLM-5.3-Flash routed MLP ("Module glm5next_mlp",
+// sections "The stack this layer runs" and "Traps this module exists to
+// hold", Constants KERNEL_MAX_TOP_K).  fp32 logits from the router weight; the
+// correction bias only changes which experts are chosen; a chosen expert's
+// weight is its plain sigmoid score over the sum of the chosen plain scores
+// (full expert count), times routed_scaling_factor; K <= 16.
 //
 // Logits are fp32 with a blocked accumulation order (short sequential runs,
 // then a tree or a sum of partials) so the emitted weights stay within 1e-6

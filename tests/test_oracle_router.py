@@ -1,10 +1,10 @@
 """Pins of the oracle's sigmoid router top-k.
 
-Module glm5next_mlp: "The stack this layer runs" (gate.weight -> logits(f32)
--> router_topk -> ids[K], weights[K]); "Traps this module exists to hold"
-(bias steers selection only, unbiased sigmoid weights, routed_scaling_factor
-on the weights, renormalise over the chosen experts of the full count);
-Constants, KERNEL_MAX_TOP_K (K <= 16).
+Module glm5next_mlp: "The stack this layer runs" (fp32 router logits, then a
+top-k that emits K ids and K weights); "Traps this module exists to hold" (the
+bias changes only the choice, weights from the plain sigmoid scores,
+routed_scaling_factor on the weights, renormalised over the chosen experts of
+the full count); Constants, KERNEL_MAX_TOP_K (K <= 16).
 """
 import itertools
 import math
