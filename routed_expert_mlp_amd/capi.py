@@ -218,6 +218,37 @@ def _layer(fn_name: str, cfg: Config, w: Weights, x: torch.Tensor, out: torch.Te
     _check(st, fn_name)
 
 
+def bind_layer(cfg: Config, w: Weights, x: torch.Tensor, out: torch.Tensor, ids_out=None, w_out=None,
+               ws: Optional[torch.Tensor] = None, stream=None, prefill=False):
+    """Check and marshal the arguments of one moe_mlp_decode / moe_mlp_prefill call once and return
+    a zero-argument callable that issues it again on the same buffers (for tight loops: the C call
+    with prebuilt ctypes arguments).  The callable raises MoeMlpError on a non-zero status."""
+    T = x.shape[0] if x.dim() == 2 else -1
+    _check_tensor(x, "x", (T, cfg.hidden), torch.bfloat16)
+    _check_tensor(out, "out", (T, cfg.hidden), torch.bfloat16)
+    if ids_out is not None:
+        _check_tensor(ids_out, "ids_out", (T, cfg.top_k), torch.int32)
+    if w_out is not None:
+        _check_tensor(w_out, "w_out", (T, cfg.top_k), torch.float32)
+    w.check(cfg)
+    if ws is None:
+        ws = workspace(cfg, T, prefill, x.device)
+    _check_tensor(ws, "workspace", None, torch.uint8)
+    name = "moe_mlp_prefill" if prefill else "moe_mlp_decode"
+    fn = getattr(lib(), name)
+    c_cfg, c_w = cfg.c(), w.c()
+    args = (ctypes.byref(c_cfg), ctypes.byref(c_w), x.data_ptr(), T, out.data_ptr(), _ptr(ids_out), _ptr(w_out),
+            ws.data_ptr(), ws.numel(), _stream(stream))
+    keep = (c_cfg, c_w, x, out, ids_out, w_out, ws, w)     # the buffers outlive the callable
+
+    def call():
+        st = fn(*args)
+        if st:
+            _check(st, name)
+    call.keep = keep
+    return call
+
+
 def moe_mlp_decode(cfg: Config, w: Weights, x: torch.Tensor, out: torch.Tensor, ids_out=None, w_out=None,
                    ws: Optional[torch.Tensor] = None, stream=None) -> None:
     _layer("moe_mlp_decode", cfg, w, x, out, ids_out, w_out, ws, stream, prefill=False)

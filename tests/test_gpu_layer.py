@@ -318,3 +318,16 @@ def test_hip_graph_replays_equal_eager(name, T, prefill):
         assert torch.equal(ids, ref_ids), f"replay {rep}: ids differ"
         assert torch.equal(wts, ref_w), f"replay {rep}: weights differ"
     say(f"[parity] graph {name}: 4 replays equal eager bitwise")
+
+
+def test_bound_call_equals_plain_call():
+    """capi.bind_layer (arguments marshalled once) issues the same call as moe_mlp_decode."""
+    d = device_workload("flash_decode_t16")
+    ref = d.run(False)[0]
+    out = torch.empty_like(ref)
+    call = capi.bind_layer(d.cfg, d.weights, d.x, out)
+    for _ in range(3):
+        out.fill_(0)
+        call()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
