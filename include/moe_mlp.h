@@ -132,8 +132,8 @@ int moe_mlp_workspace_size(const moe_mlp_config* cfg, int64_t T, int prefill, si
 /*
  * Decode form ("forward": the page's one-token decode), for 1..MOE_MLP_DECODE_MAX_T
  * tokens.  Up to 63 tokens the routed experts run as W4A16 GEMVs that stream
- * the NVFP4 codes once per touched expert (T == 1: three fused launches), and
- * the BF16 shared expert as a GEMV.  From 64 tokens on, the call runs the
+ * the NVFP4 codes once per touched expert (1..4 tokens, the MTP verify
+ * shapes: three fused launches), and the BF16 shared expert as a GEMV.  From 64 tokens on, the call runs the
  * grouped-GEMM kernels of moe_mlp_prefill (faster there; the workspace size
  * and stage list follow).
  *   x        [T, H] bf16 input.
@@ -169,8 +169,8 @@ int moe_mlp_prefill(const moe_mlp_config* cfg, const moe_mlp_weights* w, const u
  * is the stage's kernel execution time as a kernel trace reports it.
  * `events` is a HOST array of n_events caller-created hipEvent_t handles
  * (none NULL); n_events >= 2 * n_stages, else MOE_MLP_ERR_BAD_VALUE.
- * Stages (moe_mlp_stage_name): ROUTED one-token decode (T == 1, H <= 4096,
- * I and Is <= 2048) logits_shared_gateup, routed_gateup_shared_down,
+ * Stages (moe_mlp_stage_name): ROUTED decode of 1..4 tokens (T*K <= 64,
+ * H <= 4096, I and Is <= 2048) logits_shared_gateup, routed_gateup_shared_down,
  * routed_down_combine; other ROUTED decode below 64 tokens router_logits,
  * topk_bucket, shared_gateup, routed_gateup, shared_down, routed_down,
  * combine; ROUTED prefill (and decode from 64 tokens) router_logits, topk,

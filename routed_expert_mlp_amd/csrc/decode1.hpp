@@ -196,7 +196,7 @@ __global__ __launch_bounds__(256) void k_dec_gateup(const uint16_t* __restrict__
                                                     float* __restrict__ wts, int32_t* ids_out, float* w_out, int E,
                                                     int H, int I, float L, uint16_t* __restrict__ h,
                                                     const uint16_t* __restrict__ sw2, const uint16_t* __restrict__ hs,
-                                                    int Is, float* __restrict__ ys, int n_sd) {
+                                                    int Is, float* __restrict__ ys, int n_sd, int T) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   if (static_cast<int>(blockIdx.x) < n_sd) {
     const int r0 = (blockIdx.x * 4 + wv) * RS;
@@ -212,37 +212,45 @@ __global__ __launch_bounds__(256) void k_dec_gateup(const uint16_t* __restrict__
         w[r][i] = c < nsc ? row[c] : make_uint4(0, 0, 0, 0);
       }
     }
-    uint32_t hv[NSC][4];
+    for (int t = 0; t < T; ++t) {
+      uint32_t hv[NSC][4];
 #pragma unroll
-    for (int i = 0; i < NSC; ++i) {
-      const int c = lane + 64 * i;
-      const uint4 v = c < nsc ? reinterpret_cast<const uint4*>(hs)[c] : make_uint4(0, 0, 0, 0);
-      hv[i][0] = v.x; hv[i][1] = v.y; hv[i][2] = v.z; hv[i][3] = v.w;
-    }
-    float acc[RS];
+      for (int i = 0; i < NSC; ++i) {
+        const int c = lane + 64 * i;
+        const uint4 v = c < nsc ? reinterpret_cast<const uint4*>(hs + static_cast<int64_t>(t) * Is)[c]
+                                : make_uint4(0, 0, 0, 0);
+        hv[i][0] = v.x; hv[i][1] = v.y; hv[i][2] = v.z; hv[i][3] = v.w;
+      }
+      float acc[RS];
 #pragma unroll
-    for (int r = 0; r < RS; ++r) {
-      acc[r] = 0.0f;
+      for (int r = 0; r < RS; ++r) {
+        acc[r] = 0.0f;
 #pragma unroll
-      for (int i = 0; i < NSC; ++i) acc[r] = bf16_chunk_dot(w[r][i], hv[i], acc[r]);
-      acc[r] = wave_sum(acc[r]);
-    }
-    if (lane < RS) {
-      float v = acc[0];
+        for (int i = 0; i < NSC; ++i) acc[r] = bf16_chunk_dot(w[r][i], hv[i], acc[r]);
+        acc[r] = wave_sum(acc[r]);
+      }
+      if (lane < RS) {
+        float v = acc[0];
 #pragma unroll
-      for (int r = 1; r < RS; ++r)
-        if (lane == r) v = acc[r];
-      if (r0 + lane < H) ys[r0 + lane] = v;
+        for (int r = 1; r < RS; ++r)
+          if (lane == r) v = acc[r];
+        if (r0 + lane < H) ys[static_cast<int64_t>(t) * H + r0 + lane] = v;
+      }
     }
     return;
   }
   const int a = blockIdx.x - n_sd;
   const int njb = static_cast<int>(cdiv(I, 4 * RJ));
-  const int k = a / njb;
-  const int j0 = ((a % njb) * 4 + wv) * RJ;
+  const int slot = a / njb;                          // t * K + k
+  const int t = slot / K, k = slot - t * K;
+  const int jb = a - slot * njb;
+  const int j0 = (jb * 4 + wv) * RJ;
   if (j0 >= I) return;
-  const bool writer = a == 0 && wv == 0;
-  const int sel = topk_wave<NJ>(logits, bias, E, K, rsf, k, writer ? ids : nullptr, wts, ids_out, w_out);
+  const bool writer = jb == 0 && k == 0 && wv == 0;
+  const int64_t o = static_cast<int64_t>(t) * K;
+  const int sel = topk_wave<NJ>(logits + static_cast<int64_t>(t) * E, bias, E, K, rsf, k, writer ? ids + o : nullptr,
+                                wts + o, ids_out ? ids_out + o : nullptr, w_out ? w_out + o : nullptr);
+  x += static_cast<int64_t>(t) * H;
   const int e = min(max(sel, 0), E - 1);
   const int64_t rq = H >> 1, rs = H >> 4;                 // code / scale bytes per row
   const uint8_t* qe = q13 + static_cast<int64_t>(e) * 2 * I * rq;
@@ -300,67 +308,82 @@ __global__ __launch_bounds__(256) void k_dec_gateup(const uint16_t* __restrict__
       }
     const int j = j0 + lane;
     if (j < I)
-      h[static_cast<int64_t>(k) * I + j] =
+      h[static_cast<int64_t>(slot) * I + j] =
           f32_to_bf16(swiglu_clamped(g13[2 * e] * gg, g13[2 * e + 1] * uu, L));
   }
 }
 
 // -------------------------------------------------------------------------
-// 3. routed down + combine for one token.  Block b owns output rows
-// r0 = b*R .. +R and has KW >= K wavefronts: wavefront k streams those R rows
-// of expert ids[k]'s NVFP4 down projection against its h_k (one 16-byte
-// chunk per lane, lanes < I/32, h_k chunk in registers).  Per-row partials
-// meet in LDS and thread r writes out[r0+r] = bf16(ys + sum_k (w_k g2_k)
-// acc_k), k in order (ys = 0 without a shared expert).
+// 3. routed down + combine for T tokens (T*K slots, slot = t*K + k).  Block
+// b owns output rows r0 = b*R .. +R and has KW wavefronts; wavefront w
+// streams those R rows of expert ids[s]'s NVFP4 down projection against h_s
+// for its slots s = w, w + KW, ... (NP of them; one 16-byte chunk per lane,
+// lanes < I/32, the h_s chunk in registers), every load issued before any
+// arithmetic.  Per-(slot, row) partials meet in LDS and thread (t, r) writes
+// out[t][r0+r] = bf16(ys[t] + sum_k (w_{tK+k} g2) acc_{tK+k}), k in order
+// (ys = 0 without a shared expert).
 // -------------------------------------------------------------------------
-template <int R, int KW>
+template <int R, int KW, int NP>
 __global__ __launch_bounds__(KW * 64) void k_dec_down_combine(
     const uint16_t* __restrict__ h, const uint8_t* __restrict__ q2, const uint8_t* __restrict__ s2,
     const float* __restrict__ g2, const float* __restrict__ ys, const int32_t* __restrict__ ids,
-    const float* __restrict__ wts, int E, int K, int H, int I, uint16_t* __restrict__ out) {
-  __shared__ float part[KW][R];
+    const float* __restrict__ wts, int E, int K, int H, int I, uint16_t* __restrict__ out, int T) {
+  __shared__ float part[KW * NP][R];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int r0 = blockIdx.x * R;
-  const bool routed = wv < K;
-  const int e = routed ? min(max(ids[wv], 0), E - 1) : 0;
+  const int S = T * K;
   const int64_t rq = I >> 1, rs = I >> 4;
-  const bool act = routed && lane < (I >> 5);
-  uint4 cw[R];
-  uint32_t sc[R];
+  int e[NP];
+  bool act[NP];
+  uint4 cw[NP][R];
+  uint32_t sc[NP][R];
 #pragma unroll
-  for (int r = 0; r < R; ++r) {
-    const int64_t base = static_cast<int64_t>(e) * H + min(r0 + r, H - 1);
-    cw[r] = act ? *reinterpret_cast<const uint4*>(q2 + base * rq + 16 * lane) : make_uint4(0, 0, 0, 0);
-    sc[r] = act ? *reinterpret_cast<const uint16_t*>(s2 + base * rs + 2 * lane) : 0u;
-  }
-  uint32_t xp[16];
-  {
-    const uint4* hp = reinterpret_cast<const uint4*>(h + static_cast<int64_t>(wv) * I + 32 * lane);
+  for (int p = 0; p < NP; ++p) {
+    const int sl = wv + KW * p;
+    const bool routed = sl < S;
+    e[p] = routed ? min(max(ids[sl], 0), E - 1) : 0;
+    act[p] = routed && lane < (I >> 5);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint4 v = act ? hp[q] : make_uint4(0, 0, 0, 0);
-      xp[4 * q] = v.x; xp[4 * q + 1] = v.y; xp[4 * q + 2] = v.z; xp[4 * q + 3] = v.w;
+    for (int r = 0; r < R; ++r) {
+      const int64_t base = static_cast<int64_t>(e[p]) * H + min(r0 + r, H - 1);
+      cw[p][r] = act[p] ? *reinterpret_cast<const uint4*>(q2 + base * rq + 16 * lane) : make_uint4(0, 0, 0, 0);
+      sc[p][r] = act[p] ? *reinterpret_cast<const uint16_t*>(s2 + base * rs + 2 * lane) : 0u;
     }
   }
-  float acc[R];
 #pragma unroll
-  for (int r = 0; r < R; ++r) {
-    acc[r] = fmaf(e2m1x16_dot(cw[r].x, cw[r].y, xp), e4m3_to_f32<0>(sc[r]), 0.0f);
-    acc[r] = fmaf(e2m1x16_dot(cw[r].z, cw[r].w, xp + 8), e4m3_to_f32<1>(sc[r]), acc[r]);
-  }
+  for (int p = 0; p < NP; ++p) {
+    const int sl = wv + KW * p;
+    uint32_t xp[16];
+    const uint4* hp = reinterpret_cast<const uint4*>(h + static_cast<int64_t>(sl) * I + 32 * lane);
 #pragma unroll
-  for (int r = 0; r < R; ++r) acc[r] = wave_sum(acc[r]);
-  if (lane == 0) {
-    const float wk = routed ? wts[wv] * g2[e] : 0.0f;
+    for (int q = 0; q < 4; ++q) {
+      const uint4 v = act[p] ? hp[q] : make_uint4(0, 0, 0, 0);
+      xp[4 * q] = v.x; xp[4 * q + 1] = v.y; xp[4 * q + 2] = v.z; xp[4 * q + 3] = v.w;
+    }
+    float acc[R];
 #pragma unroll
-    for (int r = 0; r < R; ++r) part[wv][r] = wk * acc[r];
+    for (int r = 0; r < R; ++r) {
+      acc[r] = fmaf(e2m1x16_dot(cw[p][r].x, cw[p][r].y, xp), e4m3_to_f32<0>(sc[p][r]), 0.0f);
+      acc[r] = fmaf(e2m1x16_dot(cw[p][r].z, cw[p][r].w, xp + 8), e4m3_to_f32<1>(sc[p][r]), acc[r]);
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) acc[r] = wave_sum(acc[r]);
+    if (lane == 0) {
+      const float wk = sl < S ? wts[sl] * g2[e[p]] : 0.0f;
+#pragma unroll
+      for (int r = 0; r < R; ++r) part[sl][r] = wk * acc[r];
+    }
   }
   __syncthreads();
-  const int t = threadIdx.x;
-  if (t < R && r0 + t < H) {
-    float o = ys ? ys[r0 + t] : 0.0f;
-    for (int k = 0; k < K; ++k) o += part[k][t];
-    out[r0 + t] = f32_to_bf16(o);
+  const int tid = threadIdx.x;
+  if (tid < T * R) {
+    const int t = tid / R, r = tid - t * R;
+    if (r0 + r < H) {
+      const int64_t oi = static_cast<int64_t>(t) * H + r0 + r;
+      float o = ys ? ys[oi] : 0.0f;
+      for (int k = 0; k < K; ++k) o += part[t * K + k][r];
+      out[oi] = f32_to_bf16(o);
+    }
   }
 }
 

@@ -324,8 +324,13 @@ constexpr int kDec1MaxH = 4096;
 
 int dec1_kw(int K) { return K <= 4 ? 4 : K <= 8 ? 8 : 16; }
 
+// The few-token decode kernels (decode1.hpp) take up to 4 tokens (the MTP
+// verify shapes: one token plus up to three drafted ones), T*K <= 64 slots.
+constexpr int64_t kDecFewMaxT = 4;
+
 bool decode1_ok(const moe_mlp_config* c, int64_t T, int prefill) {
-  if (prefill || T != 1 || c->kind != MOE_MLP_KIND_ROUTED) return false;
+  if (prefill || T < 1 || T > kDecFewMaxT || c->kind != MOE_MLP_KIND_ROUTED) return false;
+  if (T * c->top_k > 64) return false;
   const int Is = c->n_shared_experts ? c->shared_intermediate : 0;
   return c->hidden <= kDec1MaxH && c->moe_intermediate <= 2048 && Is <= 2048;
 }
@@ -336,50 +341,58 @@ int n_stages(const moe_mlp_config* c, int64_t T, int prefill) {
   return gemm_form(c, T, prefill) ? 8 : 7;
 }
 
-// One-token decode: 3 launches (see decode1.hpp).
+// Few-token decode (1..4 tokens): 3 launches (see decode1.hpp).
 template <int NSC>
 void dec_gateup(const moe_mlp_config* c, const moe_mlp_weights* w, const uint16_t* x, const float* logits,
                 int32_t* ids, float* wts, int32_t* ids_out, float* w_out, uint16_t* h, const uint16_t* hs,
-                float* ys, hipStream_t s, Ev ev) {
+                float* ys, int T, hipStream_t s, Ev ev) {
   constexpr int RJ = 4, NC = 2, RS = 8;
   const int H = c->hidden, I = c->moe_intermediate, K = c->top_k;
   const int Is = c->n_shared_experts ? c->shared_intermediate : 0;
   const int n_sd = Is ? static_cast<int>(cdiv(H, 4 * RS)) : 0;
-  const unsigned grid = static_cast<unsigned>(n_sd + K * cdiv(I, 4 * RJ));
+  const unsigned grid = static_cast<unsigned>(n_sd + T * K * cdiv(I, 4 * RJ));
   with_nj(c->num_experts, [&](auto nj) {
     launch(k_dec_gateup<RJ, NC, decltype(nj)::value, RS, NSC>, dim3(grid), dim3(256), s, ev.a, ev.b, x, w->w13_q,
            w->w13_s, w->w13_g, logits, w->router_bias, K, c->routed_scaling_factor, ids, wts, ids_out, w_out,
-           c->num_experts, H, I, c->swiglu_limit, h, w->shared_w2, hs, Is, ys, n_sd);
+           c->num_experts, H, I, c->swiglu_limit, h, w->shared_w2, hs, Is, ys, n_sd, T);
   });
 }
 
-template <int KW>
+template <int KW, int NP>
 void launch_down_combine(const moe_mlp_config* c, const moe_mlp_weights* w, const uint16_t* h, const float* ys,
-                         const int32_t* ids, const float* wts, uint16_t* out, hipStream_t s, Ev ev) {
+                         const int32_t* ids, const float* wts, uint16_t* out, int T, hipStream_t s, Ev ev) {
   constexpr int R = 4;
   const int H = c->hidden;
-  launch(k_dec_down_combine<R, KW>, dim3(static_cast<unsigned>(cdiv(H, R))), dim3(KW * 64), s, ev.a, ev.b, h,
-         w->w2_q, w->w2_s, w->w2_g, ys, ids, wts, c->num_experts, c->top_k, H, c->moe_intermediate, out);
+  launch(k_dec_down_combine<R, KW, NP>, dim3(static_cast<unsigned>(cdiv(H, R))), dim3(KW * 64), s, ev.a, ev.b, h,
+         w->w2_q, w->w2_s, w->w2_g, ys, ids, wts, c->num_experts, c->top_k, H, c->moe_intermediate, out, T);
 }
 
-void decode1(const moe_mlp_config* c, const moe_mlp_weights* w, const uint16_t* x, uint16_t* out,
+void decode1(const moe_mlp_config* c, const moe_mlp_weights* w, const uint16_t* x, int T, uint16_t* out,
              int32_t* ids_out, float* w_out, float* logits, int32_t* ids, float* wts, uint16_t* h, uint16_t* hs,
              float* ys, hipStream_t s, Ev e0, Ev e1, Ev e2) {
   const int H = c->hidden, E = c->num_experts, K = c->top_k;
   const int Is = c->n_shared_experts ? c->shared_intermediate : 0;
   const int nlb = static_cast<int>(cdiv(E, 4)), nsb = static_cast<int>(cdiv(Is, 4));
-  launch(k_dec_logits_shared<16, 8>, dim3(nlb + nsb), dim3(256), s, e0.a, e0.b, x, w->router_w, logits, E, H,
-         w->shared_w13, Is, hs, c->swiglu_limit, nlb);
+  if (T == 1)
+    launch(k_dec_logits_shared<16, 8>, dim3(nlb + nsb), dim3(256), s, e0.a, e0.b, x, w->router_w, logits, E, H,
+           w->shared_w13, Is, hs, c->swiglu_limit, nlb);
+  else
+    launch(k_dec_logits_shared_t<16, 8>, dim3(nlb + nsb), dim3(256), s, e0.a, e0.b, x, w->router_w, logits, E, H,
+           w->shared_w13, Is, hs, c->swiglu_limit, nlb, T);
   const int nsc = static_cast<int>(cdiv(Is / 8, 64));
-  if (nsc <= 1) dec_gateup<1>(c, w, x, logits, ids, wts, ids_out, w_out, h, hs, ys, s, e1);
-  else if (nsc == 2) dec_gateup<2>(c, w, x, logits, ids, wts, ids_out, w_out, h, hs, ys, s, e1);
-  else if (nsc == 3) dec_gateup<3>(c, w, x, logits, ids, wts, ids_out, w_out, h, hs, ys, s, e1);
-  else dec_gateup<4>(c, w, x, logits, ids, wts, ids_out, w_out, h, hs, ys, s, e1);
+  if (nsc <= 1) dec_gateup<1>(c, w, x, logits, ids, wts, ids_out, w_out, h, hs, ys, T, s, e1);
+  else if (nsc == 2) dec_gateup<2>(c, w, x, logits, ids, wts, ids_out, w_out, h, hs, ys, T, s, e1);
+  else if (nsc == 3) dec_gateup<3>(c, w, x, logits, ids, wts, ids_out, w_out, h, hs, ys, T, s, e1);
+  else dec_gateup<4>(c, w, x, logits, ids, wts, ids_out, w_out, h, hs, ys, T, s, e1);
   const float* ysr = Is ? ys : nullptr;
-  const int kw = dec1_kw(K);
-  if (kw == 4) launch_down_combine<4>(c, w, h, ysr, ids, wts, out, s, e2);
-  else if (kw == 8) launch_down_combine<8>(c, w, h, ysr, ids, wts, out, s, e2);
-  else launch_down_combine<16>(c, w, h, ysr, ids, wts, out, s, e2);
+  // one wavefront per slot at one token (K <= 16), else 16 wavefronts looping over the T*K slots
+  const int S = T * K;
+  if (T == 1 && dec1_kw(K) == 4) launch_down_combine<4, 1>(c, w, h, ysr, ids, wts, out, T, s, e2);
+  else if (T == 1 && dec1_kw(K) == 8) launch_down_combine<8, 1>(c, w, h, ysr, ids, wts, out, T, s, e2);
+  else if (S <= 16) launch_down_combine<16, 1>(c, w, h, ysr, ids, wts, out, T, s, e2);
+  else if (S <= 32) launch_down_combine<16, 2>(c, w, h, ysr, ids, wts, out, T, s, e2);
+  else if (S <= 48) launch_down_combine<16, 3>(c, w, h, ysr, ids, wts, out, T, s, e2);
+  else launch_down_combine<16, 4>(c, w, h, ysr, ids, wts, out, T, s, e2);
 }
 
 int run_layer(const moe_mlp_config* c, const moe_mlp_weights* w, const uint16_t* x, int64_t T, uint16_t* out,
@@ -444,7 +457,7 @@ int run_layer(const moe_mlp_config* c, const moe_mlp_weights* w, const uint16_t*
   const float rsf = c->routed_scaling_factor;
 
   if (decode1_ok(c, T, prefill)) {
-    decode1(c, w, x, out, ids_out, w_out, logits, ids, wts, h, hs, ys, s, ev(0), ev(1), ev(2));
+    decode1(c, w, x, Ti, out, ids_out, w_out, logits, ids, wts, h, hs, ys, s, ev(0), ev(1), ev(2));
     return launch_status();
   }
   // decode of up to 16 tokens with H <= 4096: router logits and the shared

@@ -187,7 +187,9 @@ def test_profiled_entry_validation():
     assert [x.decode() for x in names[:n]] == ["logits_shared_gateup", "routed_gateup_shared_down",
                                                    "routed_down_combine"]
     assert names[n] is None
-    assert [L.moe_mlp_stage_name(ctypes.byref(c), 2, 0, i).decode() for i in range(7)][3] == "routed_gateup"
+    assert [L.moe_mlp_stage_name(ctypes.byref(c), 8, 0, i).decode() for i in range(7)][3] == "routed_gateup"
+    assert L.moe_mlp_stage_name(ctypes.byref(c), 4, 0, 1).decode() == "routed_gateup_shared_down"
+    assert L.moe_mlp_stage_name(ctypes.byref(c), 64, 0, 2).decode() == "permute"
     assert L.moe_mlp_stage_name(ctypes.byref(c), 2, 1, 8) is None
     assert L.moe_mlp_stage_name(None, 1, 0, 0) is None
     ev_t = ctypes.c_void_p * 6
