@@ -489,6 +489,44 @@ def main():
             "stage_us": {k: round(v * 1e3, 1) for k, v in stp.items()}}
         del wtp, xp, outp, wsp
 
+        # ---------------- dense FFN variant: prefill T=4096 and one-token decode ----------------
+        wd = synth.workload("dense_prefill_t4096")
+        cfgd = capi.Config(kind=capi.KIND_DENSE, hidden=wd.H, moe_intermediate=0, num_experts=0, top_k=0,
+                           n_shared_experts=0, shared_intermediate=0, dense_intermediate=wd.Id,
+                           routed_scaling_factor=wd.rsf, swiglu_limit=wd.swiglu_limit)
+
+        def bf(bits):
+            return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+        log(f"[bench] generating + uploading {wd.name}")
+        wtd = capi.Weights(dense_w13=bf(synth.dense_w13(wd)), dense_w2=bf(synth.dense_w2(wd)))
+        xd = bf(synth.x_rows(wd))
+        outd = torch.empty((wd.T, wd.H), dtype=torch.bfloat16, device=dev)
+        wsd = capi.workspace(cfgd, wd.T, True, dev)
+        call_d = capi.bind_layer(cfgd, wtd, xd, outd, ws=wsd, prefill=True)
+        for _ in range(3):
+            call_d()
+        s_d = run_decode_steps(lambda i: call_d(), 10)
+        std = stage_times(cfgd, [wtd], [xd], [outd], True, 5, ev, wsd)
+        fl_d = 2.0 * wd.T * 3 * wd.H * wd.Id
+        x1 = xd[:1].contiguous()
+        out1 = torch.empty((1, wd.H), dtype=torch.bfloat16, device=dev)
+        ws1 = capi.workspace(cfgd, 1, False, dev)
+        call_d1 = capi.bind_layer(cfgd, wtd, x1, out1, ws=ws1)
+        for _ in range(10):
+            call_d1()
+        s_d1 = run_decode_steps(lambda i: call_d1(), 200)
+        dense_bytes = 2 * 3 * wd.H * wd.Id
+        extra["dense_prefill_t4096"] = {
+            "ms_per_step": round(s_d * 1e3, 3), "tflops": round(fl_d / s_d / 1e12, 1),
+            "frac_bf16_peak": round(fl_d / s_d / 1e12 / BF16_PEAK_TFLOPS, 4),
+            "stage_us": {k: round(v * 1e3, 1) for k, v in std.items()},
+            "decode_t1_us": round(s_d1 * 1e6, 2),
+            "decode_t1_gbs_warm": round(dense_bytes / s_d1 / 1e9, 1),
+            "note": "dense FFN H=4096, Id=12288, bf16 weights (302 MB: the T=1 decode line reads them "
+                    "from the 256 MB last-level cache only in part)"}
+        del call_d, call_d1, wtd, xd, outd, wsd
+
     # ---------------- CPU oracle baseline ----------------
     cpu = None
     if not args.no_cpu_baseline:
