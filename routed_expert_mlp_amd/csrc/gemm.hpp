@@ -55,7 +55,7 @@ struct GemmArgs {
   const int32_t* count;
   const int32_t* offset;
   const int32_t* perm;
-  int T;                     // dense rows
+  int T;                     // dense rows (routed NVFP4 GEMM: activation rows)
   int K;                     // slot -> token = slot / K (routed gate/up gather)
   void* out;
   int ldo;

@@ -1,0 +1,330 @@
+// Routed NVFP4 grouped GEMM for prefill (gate/up with the clamped SwiGLU, and
+// down), v_mfma_f32_32x32x16_bf16 with the weights dequantised in registers.
+//
+// "Module glm5next_mlp", forward_prefill_gemm / MOE_GROUPED_MODULE: every
+// expert's sorted rows run through one W4A16 GEMM against that expert's NVFP4
+// weights (E2M1 codes, one E4M3 scale per 16 columns of a row, an fp32 global
+// per expert and projection applied after the sum).
+//
+// Why this kernel looks the way it does (measured on gfx950):
+//   * A global->LDS DMA instruction costs the texture path about two cycles
+//     per distinct 128-byte line its 64 lanes touch.  Loads where each lane
+//     reads 16 bytes of a different weight or activation row therefore run at
+//     a quarter (or less) of the rate of loads where eight lanes cover one
+//     128-byte line.  Every DMA here is laid out for whole lines: activations
+//     8 lanes per row (one 64-column stage = 128 bytes), codes 4 lanes per
+//     row (two stages = 64 bytes), scales one lane per row (four stages = 16
+//     bytes, the scale array being the smallest stream).
+//   * The lane -> (row, 16-byte piece) assignment of each DMA is free (the
+//     LDS side is always lane-contiguous), so the XOR swizzle that keeps the
+//     MFMA operand reads free of bank conflicts is applied on the global side.
+//   * One workgroup of 8 wavefronts per CU, tile = 128 rows x 512 weight rows
+//     (gate/up: 256 gate + the matching 256 up rows; down: 512 output
+//     columns).  Each wavefront owns all 128 rows x 64 weight rows (4 x 2
+//     MFMA tiles), so every weight element is dequantised once per tile and
+//     each activation stage in LDS feeds 512 output columns.
+//   * LDS rings: activations 4 stages (16 KB each), codes 2 units of two
+//     stages (32 KB each), scales 2 groups of four stages (8 KB each): 144 KB.
+//     The DMA schedule is static (a prologue, a first, middle and last block
+//     of four stages), so every wait is a compile-time count; activation and
+//     code slots are separate LDS arrays whose reads the compiler schedules
+//     (the next k-step's activation fragments are read during the current
+//     k-step's MFMAs); scale words are read by asm.
+//
+// Rows past the tile's valid count load row 0 again (outputs dropped); weight
+// rows past the matrix edge load row 0 again (outputs not stored).  Requires
+// kdim % 256 == 0 and kdim >= 512.
+#pragma once
+
+#include "common.hpp"
+#include "gemm.hpp"
+
+#include <type_traits>
+
+namespace moe {
+
+constexpr int F4_WROWS = 512;      // weight rows per workgroup
+constexpr int F4_THREADS = 512;    // 8 wavefronts
+
+// 16-byte position of activation chunk c (0..7) of tile row r: c ^ f4_swz_a(r).
+// Conflict-free MFMA operand reads whether a ds_read_b128 phase serves 8 or 16
+// lanes (rows r..r+7 get distinct positions, and so do the even and the odd
+// rows among r..r+15).
+__device__ __forceinline__ int f4_swz_a(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+// 16-byte position of code piece q (0..3) of weight row p: q ^ f4_swz_c(p).
+__device__ __forceinline__ int f4_swz_c(int p) { return ((p >> 1) & 3) ^ ((p >> 3) & 1); }
+
+// This lane's two scale words of one stage (n-tile stride NT_S bytes): one asm
+// statement that waits for them (the scale ring alternates slots at run time,
+// so a compiler-visible read could not be told apart from the DMA in flight).
+template <int NT_S>
+__device__ __forceinline__ void f4_read_scales(uint32_t saddr, uint32_t (&sc)[2]) {
+  uint32_t s0, s1;
+  asm volatile("ds_read_b32 %0, %2\n\tds_read_b32 %1, %2 offset:%3\n\ts_waitcnt lgkmcnt(0)"
+               : "=&v"(s0), "=&v"(s1)
+               : "v"(saddr), "i"(NT_S)
+               : "memory");
+  sc[0] = s0;
+  sc[1] = s1;
+}
+
+// LDS of one workgroup: the activation ring as four arrays and the code ring
+// as two, so that the compiler's wait insertion can tell a read of one slot
+// from the DMA into another; the scale ring (read by asm only) is one array.
+struct F4Lds {
+  uint4* a[4];
+  uint4* c[2];
+  uint8_t* s;
+};
+
+// DMA sources: wave-uniform bases and this lane's 32-bit byte offsets
+// (activations: its two rows' first chunk; codes: its four rows' first piece;
+// scales: its row).  The host keeps every offset below 2^31.
+struct F4Src {
+  const uint8_t* a;
+  uint32_t ao[2];
+  const uint8_t* c;
+  uint32_t co[4];
+  const uint8_t* s;
+  uint32_t so;
+};
+
+template <int MODE, int MTV>
+__device__ __forceinline__ void f4_mainloop(const F4Lds& L, const F4Src& src, int wv, int lane, int kdim,
+                                            f32x16 (&acc)[4][2]) {
+  constexpr int S_BYTES = F4_WROWS * 16;       // one scale group (four stages)
+  // weight-row stride between this lane's two n-tiles
+  constexpr int NT_ROWS = MODE == GEMM_GATEUP ? 256 : 32;
+  const int g = lane >> 5, ln = lane & 31;
+  const int nkb = kdim >> 6;                   // stages; a multiple of 4, at least 8
+  const int nblk4 = nkb >> 2;                  // blocks of four stages
+
+  // ---- DMA issue (per wave: A = 2, C = 4, S = 1 instructions)
+  auto issue_a = [&](int k, auto slot_c) {
+    constexpr int SL = decltype(slot_c)::value;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(src.a + (src.ao[i] + 128u * k)),
+                                       (void __attribute__((address_space(3)))*)(L.a[SL] + wv * 128 + i * 64),
+                                       16, 0, 0);
+  };
+  auto issue_c = [&](int u, auto slot_c) {
+    constexpr int SL = decltype(slot_c)::value;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(src.c + (src.co[i] + 64u * u)),
+                                       (void __attribute__((address_space(3)))*)(L.c[SL] + wv * 256 + i * 64),
+                                       16, 0, 0);
+  };
+  auto issue_s = [&](int v) {
+    __builtin_amdgcn_global_load_lds(static_cast<const void*>(src.s + (src.so + 16u * v)),
+                                     (void __attribute__((address_space(3)))*)(L.s + (v & 1) * S_BYTES + wv * 1024),
+                                     16, 0, 0);
+  };
+
+  // ---- consumer offsets (uint4 units within a ring entry)
+  const int prow = (MODE == GEMM_GATEUP ? 32 * wv : 64 * wv) + ln;   // weight row of n-tile 0
+  const int sc = f4_swz_c(prow), sa = f4_swz_a(ln);
+  int aidx[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) aidx[s] = ln * 8 + ((4 * g + s) ^ sa);
+  int cidx[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) cidx[t] = prow * 4 + ((2 * t + g) ^ sc);
+  const uint32_t sbase = lds_addr(L.s) + static_cast<uint32_t>(prow * 16);
+
+  // ---- one stage: wait for its data (VM = DMA instructions allowed to stay in
+  // flight), barrier, issue the next loads, then 4 k-steps of 8 MFMAs with the
+  // next k-step's activation fragments read during the current one
+  auto stage = [&](int k, auto slot_c, auto vm_c, auto issue) {
+    constexpr int SL = decltype(slot_c)::value;
+    constexpr int VM = decltype(vm_c)::value;
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(VM));
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    issue();
+    const uint4* As = L.a[SL];
+    const uint4* Cs = L.c[SL >> 1];
+    uint32_t sw[2];
+    f4_read_scales<NT_ROWS * 16>(sbase + ((k >> 2) & 1) * S_BYTES + 4 * SL, sw);
+    uint4 cw[2];
+    cw[0] = Cs[cidx[SL & 1]];
+    cw[1] = Cs[cidx[SL & 1] + NT_ROWS * 4];
+    // this lane's two scale bytes (its 32 columns = two 16-blocks) sit at bytes 2g, 2g+1
+    const uint32_t s0 = sw[0] >> (16 * g), s1 = sw[1] >> (16 * g);
+    // activation fragments: each is re-read for the next k-step right after
+    // its last MFMA of this one, so the reads overlap the remaining MFMAs
+    bf16x8 af[MTV];
+#pragma unroll
+    for (int mt = 0; mt < MTV; ++mt) af[mt] = __builtin_bit_cast(bf16x8, As[aidx[0] + mt * 256]);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      bf16x8 bfrag[2];
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        const uint4 c = cw[nt];
+        const uint32_t word = s == 0 ? c.x : s == 1 ? c.y : s == 2 ? c.z : c.w;
+        const uint32_t sb = nt == 0 ? s0 : s1;
+        const float scale = (s < 2) ? e4m3_to_f32<0>(sb) : e4m3_to_f32<1>(sb);
+        uint32_t o[4];
+        e2m1x8_scaled_bf16(word, scale, o);
+        bfrag[nt] = __builtin_bit_cast(bf16x8, make_uint4(o[0], o[1], o[2], o[3]));
+      }
+#pragma unroll
+      for (int mt = 0; mt < MTV; ++mt) {
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+          acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mt], bfrag[nt], acc[mt][nt], 0, 0, 0);
+        if (s < 3) af[mt] = __builtin_bit_cast(bf16x8, As[aidx[(s + 1) & 3] + mt * 256]);
+      }
+    }
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
+
+  // Issue schedule (A(k) = activation stage k into slot k%4, C(u) = code unit u
+  // into slot u%2, S(v) = scale group v into slot v%2).  Prologue: S0 C0 A0 C1
+  // A1 A2 S1.  Stage k of a middle block issues, after its barrier:
+  //   k%4 == 0: S(k/4+1) C(k/2+1) A(k+3); 1: A(k+3); 2: C(k/2+1) A(k+3); 3: A(k+3)
+  // The first block skips S and C at k = 0; the last block issues only
+  // C(k/2+1) A(k+3) at its first stage.  Counting the DMA instructions issued
+  // after the last one each stage needs gives the waits below.
+  issue_s(0);
+  issue_c(0, I0{});
+  issue_a(0, I0{});
+  issue_c(1, I1{});
+  issue_a(1, I1{});
+  issue_a(2, I2{});
+  issue_s(1);
+  // first block
+  stage(0, I0{}, std::integral_constant<int, 9>{}, [&] { issue_a(3, I3{}); });
+  stage(1, I1{}, std::integral_constant<int, 5>{}, [&] { issue_a(4, I0{}); });
+  stage(2, I2{}, std::integral_constant<int, 5>{}, [&] { issue_c(2, I0{}); issue_a(5, I1{}); });
+  stage(3, I3{}, std::integral_constant<int, 8>{}, [&] { issue_a(6, I2{}); });
+  // middle blocks
+  for (int j = 1; j < nblk4 - 1; ++j) {
+    const int k = 4 * j;
+    stage(k, I0{}, std::integral_constant<int, 4>{}, [&] { issue_s(j + 1); issue_c(2 * j + 1, I1{}); issue_a(k + 3, I3{}); });
+    stage(k + 1, I1{}, std::integral_constant<int, 9>{}, [&] { issue_a(k + 4, I0{}); });
+    stage(k + 2, I2{}, std::integral_constant<int, 4>{}, [&] { issue_c(2 * j + 2, I0{}); issue_a(k + 5, I1{}); });
+    stage(k + 3, I3{}, std::integral_constant<int, 8>{}, [&] { issue_a(k + 6, I2{}); });
+  }
+  // last block
+  {
+    const int j = nblk4 - 1, k = 4 * j;
+    stage(k, I0{}, std::integral_constant<int, 4>{}, [&] { issue_c(2 * j + 1, I1{}); issue_a(k + 3, I3{}); });
+    stage(k + 1, I1{}, std::integral_constant<int, 8>{}, [] {});
+    stage(k + 2, I2{}, std::integral_constant<int, 2>{}, [] {});
+    stage(k + 3, I3{}, std::integral_constant<int, 0>{}, [] {});
+  }
+}
+
+// Grid: 1-D, XCD-aware as in k_gemm_fast (block b runs on XCD b % 8; each XCD
+// takes a contiguous run of (tile, column block) work, column blocks of a
+// tile back to back).  n_blocks = column blocks of F4_WROWS weight rows
+// (gate/up: 256 gate columns each).
+template <int MODE>
+__global__ __launch_bounds__(F4_THREADS, 1) void k_gemm_nvfp4(GemmArgs a) {
+  const int nbn = a.n_blocks;
+  const int ntl = *a.n_tiles;
+  const int total = ntl * nbn, chunk = (total + 7) >> 3;
+  const int kk = blockIdx.x >> 3;
+  if (kk >= chunk) return;
+  const int w = (blockIdx.x & 7) * chunk + kk;
+  if (w >= total) return;
+  const int tile = w / nbn, nblk = w - tile * nbn;
+  const int e = a.tile_expert[tile];
+  const int m0 = a.tile_m0[tile];
+  const int valid = min(GM_BM, a.count[e] - m0);
+  const int p0 = a.offset[e] + m0;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int kdim = a.kdim;
+
+  // activation DMA: instruction i of wave wv covers tile rows 16 wv + 8 i .. +7,
+  // 8 lanes per row, lane -> 16-byte chunk (lane & 7) ^ swizzle
+  F4Src src;
+  src.a = reinterpret_cast<const uint8_t*>(a.a);
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int r = 16 * wv + 8 * i + (lane >> 3);
+    const int rr = r < valid ? r : 0;
+    const int64_t row = (MODE == GEMM_GATEUP) ? a.perm[p0 + rr] / a.K : p0 + rr;
+    src.ao[i] = static_cast<uint32_t>((row * kdim + 8 * ((lane & 7) ^ f4_swz_a(r))) * 2);
+  }
+  // weight row of workgroup row p (0..511); rows past the edge reload row 0
+  auto wrow = [&](int p) -> int64_t {
+    if (MODE == GEMM_GATEUP) {
+      const int j = nblk * 256 + (p & 255);
+      return j < a.half_n ? (p < 256 ? j : a.half_n + j) : 0;
+    } else {
+      const int n = nblk * F4_WROWS + p;
+      return n < a.half_n ? n : 0;
+    }
+  };
+  // code DMA: instruction i of wave wv covers workgroup rows 16 (4 wv + i) .. +15,
+  // 4 lanes per row, lane -> 16-byte piece (lane & 3) ^ swizzle of a 64-byte unit
+  src.c = a.bq + e * a.stride_q;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int p = 16 * (4 * wv + i) + (lane >> 2);
+    src.co[i] = static_cast<uint32_t>(wrow(p) * (kdim >> 1) + 16 * ((lane & 3) ^ f4_swz_c(p)));
+  }
+  // scale DMA: workgroup row 64 wv + lane, 16 bytes (four stages) per group
+  src.s = a.bs + e * a.stride_s;
+  src.so = static_cast<uint32_t>(wrow(64 * wv + lane) * (kdim >> 4));
+
+  __shared__ uint4 la0[1024], la1[1024], la2[1024], la3[1024];   // activation ring (16 KB each)
+  __shared__ uint4 lc0[2048], lc1[2048];                          // code ring (32 KB each)
+  __shared__ __attribute__((aligned(16))) uint8_t ls[2 * F4_WROWS * 16];   // scale ring
+  const F4Lds L{{la0, la1, la2, la3}, {lc0, lc1}, ls};
+  f32x16 acc[4][2];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) acc[mt][nt][j] = 0.0f;
+  switch ((valid + 31) >> 5) {
+    case 1: f4_mainloop<MODE, 1>(L, src, wv, lane, kdim, acc); break;
+    case 2: f4_mainloop<MODE, 2>(L, src, wv, lane, kdim, acc); break;
+    case 3: f4_mainloop<MODE, 3>(L, src, wv, lane, kdim, acc); break;
+    default: f4_mainloop<MODE, 4>(L, src, wv, lane, kdim, acc); break;
+  }
+
+  const int mt_valid = (valid + 31) >> 5;
+  const int ln = lane & 31;
+  float g0, g1 = 1.0f;
+  if (MODE == GEMM_GATEUP) {
+    g0 = a.gscale ? a.gscale[2 * e] : 1.0f;
+    g1 = a.gscale ? a.gscale[2 * e + 1] : 1.0f;
+  } else {
+    g0 = a.gscale ? a.gscale[e] : 1.0f;
+  }
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+    if (mt >= mt_valid) continue;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int row = mt * 32 + c32_row(lane, j);
+      if (row >= valid) continue;
+      if (MODE == GEMM_GATEUP) {
+        const int jc = nblk * 256 + 32 * wv + ln;
+        if (jc >= a.half_n) continue;
+        static_cast<uint16_t*>(a.out)[static_cast<int64_t>(p0 + row) * a.ldo + jc] =
+            f32_to_bf16(swiglu_clamped(g0 * acc[mt][0][j], g1 * acc[mt][1][j], a.limit));
+      } else {
+        const int64_t orow = a.perm[p0 + row];
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+          const int n = nblk * F4_WROWS + 64 * wv + 32 * nt + ln;
+          if (n < a.half_n) static_cast<float*>(a.out)[orow * a.ldo + n] = g0 * acc[mt][nt][j];
+        }
+      }
+    }
+  }
+}
+
+}  // namespace moe

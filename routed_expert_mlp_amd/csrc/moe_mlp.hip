@@ -15,6 +15,7 @@
 #include "common.hpp"
 #include "decode1.hpp"
 #include "gemm.hpp"
+#include "gemm_fp4.hpp"
 #include "gemv.hpp"
 #include "permute.hpp"
 #include "router.hpp"
@@ -247,11 +248,24 @@ void gemv(const GemvArgs& a, int groups, hipStream_t s, Ev ev) {
   }
 }
 
-// Reduction lengths that are a multiple of 64 take the 32x32x16-MFMA kernel
-// (k_gemm_fast); others the general 16x16x32 kernel.
+// Routed NVFP4 projections with a reduction length that is a multiple of 256
+// and at least 512 take k_gemm_nvfp4; other reduction lengths that are a multiple of 64 the
+// 32x32x16-MFMA kernel (k_gemm_fast); the rest the general 16x16x32 kernel.
 template <bool NVFP4, int MODE, bool ROUTED>
 void gemm(const GemmArgs& a0, int64_t m_tiles, hipStream_t s, Ev ev) {
   GemmArgs a = a0;
+  if constexpr (NVFP4 && ROUTED && (MODE == GEMM_GATEUP || MODE == GEMM_DOWN_SLOT_F32)) {
+    // its DMA offsets are 32-bit: activation rows (T here) and weight rows
+    // times the row length must stay below 2^31 bytes
+    const int64_t w_rows = MODE == GEMM_GATEUP ? 2 * int64_t(a.half_n) : int64_t(a.half_n);
+    if (a.kdim % 256 == 0 && a.kdim >= 512 && int64_t(a.T) * a.kdim * 2 < (int64_t(1) << 31) &&
+        w_rows * a.kdim / 2 < (int64_t(1) << 31)) {
+      a.n_blocks = static_cast<int>(cdiv(a.half_n, MODE == GEMM_GATEUP ? F4_WROWS / 2 : F4_WROWS));
+      const int64_t work = m_tiles * a.n_blocks;
+      launch(k_gemm_nvfp4<MODE>, dim3(static_cast<unsigned>(8 * cdiv(work, 8))), dim3(F4_THREADS), s, ev.a, ev.b, a);
+      return;
+    }
+  }
   if (a.kdim % 64 == 0) {
     a.n_blocks = static_cast<int>(cdiv(a.half_n, MODE == GEMM_GATEUP ? 128 : 256));
     const int64_t work = m_tiles * a.n_blocks;
@@ -498,6 +512,7 @@ int run_layer(const moe_mlp_config* c, const moe_mlp_weights* w, const uint16_t*
     gu.stride_s = int64_t(2) * I * H / 16;
     gu.gscale = w->w13_g;
     gu.half_n = I;
+    gu.T = static_cast<int>(T);              // activation rows (tokens)
     gu.out = h;
     gu.ldo = I;
     gemm<true, GEMM_GATEUP, true>(gu, p.max_tiles, s, ev(3));
@@ -511,6 +526,7 @@ int run_layer(const moe_mlp_config* c, const moe_mlp_weights* w, const uint16_t*
     gd.stride_s = int64_t(H) * I / 16;
     gd.gscale = w->w2_g;
     gd.half_n = H;
+    gd.T = static_cast<int>(S);              // activation rows (slots)
     gd.out = y;
     gd.ldo = H;
     gemm<true, GEMM_DOWN_SLOT_F32, true>(gd, p.max_tiles, s, ev(4));

@@ -126,6 +126,23 @@ def _fresh(name, prefill, n_sample=64, w13_g=None, w2_g=None, **overrides):
     return _check_layer(d, prefill, n_sample, f"{name} {overrides or ''}")
 
 
+# Routed NVFP4 grouped GEMM (reduction lengths that are multiples of 256, at
+# least 512): experts with two and three 128-row tiles, column blocks cut by
+# the matrix edge in gate/up and in down, reductions of 8, 12 and 16 stages
+# (no, one and two middle blocks of the DMA schedule), and a 256-long
+# reduction (the other grouped GEMM kernel); every token checked.
+FP4_TILES = [dict(T=600, H=512, I=512, E=16, K=4, Is=256),
+             dict(T=300, H=768, I=512, E=8, K=2, Is=96),
+             dict(T=200, H=1024, I=160, E=8, K=2, Is=96),
+             dict(T=700, H=512, I=768, E=4, K=2, Is=0),
+             dict(T=100, H=256, I=256, E=4, K=2, Is=64)]
+
+
+@pytest.mark.parametrize("overrides", FP4_TILES, ids=[f"T{o['T']}_H{o['H']}_I{o['I']}_E{o['E']}" for o in FP4_TILES])
+def test_grouped_gemm_nvfp4_tiles(overrides):
+    _fresh("ragged_prefill", True, n_sample=100000, **overrides)
+
+
 @pytest.mark.parametrize("prefill", [False, True])
 def test_top_k_equals_e_at_the_kernel_limit(prefill):
     _fresh("tiny_decode", prefill, T=8, K=16)
