@@ -20,6 +20,8 @@
 #include "permute.hpp"
 #include "router.hpp"
 
+static_assert(MOE_MLP_MAX_EXPERTS <= moe::PERM_MAX_E, "k_perm_hist keeps one LDS counter per expert");
+
 namespace {
 
 using namespace moe;
@@ -55,6 +57,7 @@ struct Plan {
   size_t logits = 0, ids = 0, wts = 0;
   size_t g_n = 0, g_expert = 0, g_count = 0, g_offset = 0, g_slots = 0;          // decode groups
   size_t count = 0, offset = 0, perm = 0, n_tiles = 0, tile_e = 0, tile_m0 = 0;  // prefill permutation
+  size_t phist = 0, pbase = 0, prank = 0;                                        // permutation scratch
   size_t h = 0, hs = 0, y = 0, ys = 0;
   size_t wsplit = 0;                                                             // router weight, 3 bf16 planes
   int logit_planes = 1;
@@ -113,6 +116,9 @@ Plan make_plan(const moe_mlp_config* c, int64_t T, int prefill) {
     p.n_tiles = a.take(4);
     p.tile_e = a.take(size_t(p.max_tiles) * 4);
     p.tile_m0 = a.take(size_t(p.max_tiles) * 4);
+    p.phist = a.take(size_t(cdiv(S, PERM_CHUNK)) * E * 4);
+    p.pbase = a.take(size_t(cdiv(S, PERM_CHUNK)) * E * 4);
+    p.prank = a.take(size_t(S) * 4);
   } else {
     p.g_n = a.take(4);
     p.g_expert = a.take(size_t(E) * 4);
@@ -490,9 +496,14 @@ int run_layer(const moe_mlp_config* c, const moe_mlp_weights* w, const uint16_t*
     Perm pm{at<int32_t>(ws, p.count), at<int32_t>(ws, p.offset), at<int32_t>(ws, p.perm),
             at<int32_t>(ws, p.n_tiles), at<int32_t>(ws, p.tile_e), at<int32_t>(ws, p.tile_m0)};
     const Ev pe = ev(2);
-    launch(k_expert_count, dim3(E), dim3(256), s, pe.a, nullptr, ids, static_cast<int>(S), pm);
-    launch(k_schedule, dim3(1), dim3(1024), s, nullptr, nullptr, E, GM_BM, pm);
-    launch(k_expert_scatter, dim3(E), dim3(256), s, nullptr, pe.b, ids, static_cast<int>(S), pm);
+    const int nchunk = static_cast<int>(cdiv(S, PERM_CHUNK));
+    int32_t* phist = at<int32_t>(ws, p.phist);
+    int32_t* prank = at<int32_t>(ws, p.prank);
+    launch(k_perm_hist, dim3(nchunk), dim3(PERM_CHUNK), s, pe.a, nullptr, ids, static_cast<int>(S), E, phist, prank);
+    int32_t* pbase = at<int32_t>(ws, p.pbase);
+    launch(k_perm_schedule, dim3(1), dim3(1024), s, nullptr, nullptr, E, nchunk, GM_BM, phist, pbase, pm);
+    launch(k_perm_scatter, dim3(static_cast<unsigned>(cdiv(S, 256))), dim3(256), s, nullptr, pe.b, ids,
+           static_cast<int>(S), E, pbase, prank, pm);
     GemmArgs g{};
     g.n_tiles = pm.n_tiles;
     g.tile_expert = pm.tile_expert;

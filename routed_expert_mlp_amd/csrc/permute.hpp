@@ -1,11 +1,15 @@
 // Token permutation by expert id for the grouped-GEMM prefill ("Module
 // glm5next_mlp", Constants, MOE_MODULE: the token sort / permute / unpermute
 // family).  The T*K routing slots (slot = t*K + k) are sorted by expert id,
-// stably (ascending slot within an expert), with no global atomics:
-//   1. k_expert_count:   one workgroup per expert counts its slots;
-//   2. k_schedule:       one workgroup scans the counts into offsets and cuts
-//                        each expert's rows into BM-row GEMM tiles;
-//   3. k_expert_scatter: one workgroup per expert writes its slots in order.
+// stably (ascending slot within an expert), with no global atomics, in
+// chunks of 256 slots:
+//   1. k_perm_hist:     per chunk, a histogram over experts (LDS) and each
+//                       slot's rank among the chunk's slots of its expert;
+//   2. k_perm_schedule: one workgroup sums the histograms into expert counts,
+//                       scans them into offsets, cuts each expert's rows into
+//                       BM-row GEMM tiles and turns the histograms into the
+//                       sorted position of each (chunk, expert) run;
+//   3. k_perm_scatter:  one thread per slot writes it at run start + rank.
 #pragma once
 
 #include "common.hpp"
@@ -21,30 +25,53 @@ struct Perm {
   int32_t* tile_m0;      // [max_tiles] first row of the tile within its expert
 };
 
-__global__ __launch_bounds__(256) void k_expert_count(const int32_t* __restrict__ ids, int nslot, Perm p) {
-  const int e = blockIdx.x;
-  int c = 0;
-  for (int i = threadIdx.x; i < nslot; i += 256) c += ids[i] == e;
-  __shared__ int red[4];
-  for (int m = 32; m >= 1; m >>= 1) c += __shfl_xor(c, m, 64);
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = c;
+// Slots are taken in chunks of PERM_CHUNK (one per thread of a workgroup).
+constexpr int PERM_CHUNK = 256;
+constexpr int PERM_MAX_E = 1024;
+
+// 1. One workgroup per chunk b: hist[b][e] = the chunk's slots routed to
+// expert e, and rank[i] = how many earlier slots of the same chunk go to the
+// same expert as slot i.
+__global__ __launch_bounds__(PERM_CHUNK) void k_perm_hist(const int32_t* __restrict__ ids, int nslot, int E,
+                                                          int32_t* __restrict__ hist, int32_t* __restrict__ rank) {
+  __shared__ int s_id[PERM_CHUNK];
+  __shared__ int s_h[PERM_MAX_E];
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const int i = b * PERM_CHUNK + tid;
+  const int e = i < nslot ? ids[i] : -1;
+  s_id[tid] = e;
+  for (int x = tid; x < E; x += PERM_CHUNK) s_h[x] = 0;
   __syncthreads();
-  if (threadIdx.x == 0) p.count[e] = red[0] + red[1] + red[2] + red[3];
+  if (e >= 0) atomicAdd(&s_h[e], 1);
+  int r = 0;
+  for (int j = 0; j < tid; ++j) r += s_id[j] == e;
+  if (i < nslot) rank[i] = r;
+  __syncthreads();
+  for (int x = tid; x < E; x += PERM_CHUNK) hist[static_cast<int64_t>(b) * E + x] = s_h[x];
 }
 
-// One workgroup of 1024 threads; E <= 1024.
-__global__ __launch_bounds__(1024) void k_schedule(int E, int bm, Perm p) {
+// 2. One workgroup of 1024 threads (E <= 1024): expert counts (sums over the
+// chunks), their exclusive scan into offsets, the cut of each expert's rows
+// into bm-row GEMM tiles, and base[b][e] = the sorted position of chunk b's
+// first slot of expert e (a separate array, so the loads of both passes over
+// the chunks stay in flight together).
+__global__ __launch_bounds__(1024) void k_perm_schedule(int E, int nblk, int bm, const int32_t* __restrict__ hist,
+                                                        int32_t* __restrict__ base, Perm p) {
   __shared__ int s_w[2][16];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int c = tid < E ? p.count[tid] : 0;
+  int c = 0;
+  if (tid < E) {
+#pragma unroll 16
+    for (int b = 0; b < nblk; ++b) c += hist[static_cast<int64_t>(b) * E + tid];
+  }
   const int nt = static_cast<int>(cdiv(c, bm));
   int ic = c, it = nt;
 #pragma unroll
   for (int m = 1; m < 64; m <<= 1) {
-    const int a = __shfl_up(ic, m, 64), b = __shfl_up(it, m, 64);
+    const int a = __shfl_up(ic, m, 64), t = __shfl_up(it, m, 64);
     if (lane >= m) {
       ic += a;
-      it += b;
+      it += t;
     }
   }
   if (lane == 63) {
@@ -59,6 +86,7 @@ __global__ __launch_bounds__(1024) void k_schedule(int E, int bm, Perm p) {
   }
   const int off = bc + ic - c, toff = bt + it - nt;
   if (tid < E) {
+    p.count[tid] = c;
     p.offset[tid] = off;
     for (int j = 0; j < nt; ++j) {
       p.tile_expert[toff + j] = tid;
@@ -68,31 +96,24 @@ __global__ __launch_bounds__(1024) void k_schedule(int E, int bm, Perm p) {
       p.offset[E] = off + c;
       *p.n_tiles = toff + nt;
     }
+    int run = off;
+#pragma unroll 16
+    for (int b = 0; b < nblk; ++b) {
+      const int64_t q = static_cast<int64_t>(b) * E + tid;
+      base[q] = run;
+      run += hist[q];
+    }
   }
 }
 
-__global__ __launch_bounds__(256) void k_expert_scatter(const int32_t* __restrict__ ids, int nslot, Perm p) {
-  const int e = blockIdx.x;
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int per = static_cast<int>(cdiv(cdiv(nslot, 4), 64) * 64);   // slots per wave, multiple of 64
-  const int beg = wv * per, end = min(nslot, beg + per);
-  int cnt = 0;
-  for (int i = beg; i < end; i += 64) {
-    const bool hit = (i + lane < end) && ids[i + lane] == e;
-    cnt += __popcll(__ballot(hit));
-  }
-  __shared__ int s_c[4];
-  if (lane == 0) s_c[wv] = cnt;
-  __syncthreads();
-  int base = p.offset[e];
-  for (int w = 0; w < wv; ++w) base += s_c[w];
-  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int i = beg; i < end; i += 64) {
-    const bool hit = (i + lane < end) && ids[i + lane] == e;
-    const uint64_t m = __ballot(hit);
-    if (hit) p.perm[base + __popcll(m & below)] = i + lane;
-    base += __popcll(m);
-  }
+// 3. One thread per slot: perm[base(chunk, expert) + rank] = slot.
+__global__ __launch_bounds__(256) void k_perm_scatter(const int32_t* __restrict__ ids, int nslot, int E,
+                                                      const int32_t* __restrict__ base,
+                                                      const int32_t* __restrict__ rank, Perm p) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= nslot) return;
+  const int e = ids[i];
+  p.perm[base[static_cast<int64_t>(i / PERM_CHUNK) * E + e] + rank[i]] = i;
 }
 
 }  // namespace moe
