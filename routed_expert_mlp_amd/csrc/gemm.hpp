@@ -61,6 +61,13 @@ struct GemmArgs {
   int ldo;
   float limit;
   int n_blocks;              // output-column blocks (fast kernel's 1-D work mapping)
+  // BF16 fast kernel only: row strides of A and B (0 = kdim), and a split of
+  // the reduction into ksplit parts of kdim each (A and B columns advance by
+  // kdim per part, part q writes its fp32 result split_out elements after part
+  // q-1; GEMM_DOWN_F32 only)
+  int lda, ldb;
+  int ksplit;
+  int64_t split_out;
 };
 
 template <bool NVFP4, int MODE, bool ROUTED>
@@ -288,6 +295,7 @@ __device__ __forceinline__ void gemm_fast_mainloop(const GemmArgs& a, uint4 (&L0
     else if constexpr (SL == 2) return L2;
     else return L3;
   };
+  const int64_t ldb = a.ldb ? a.ldb : kdim;
   auto issue = [&](int k, auto slot_c) {
     constexpr int SL = decltype(slot_c)::value;
     const int kg = k * BK + 32 * g;
@@ -304,7 +312,7 @@ __device__ __forceinline__ void gemm_fast_mainloop(const GemmArgs& a, uint4 (&L0
       } else {
 #pragma unroll
         for (int q = 0; q < BW; ++q)
-          r.b[SL][nt][q] = *reinterpret_cast<const uint4*>(a.bb + static_cast<int64_t>(brow[nt]) * kdim + kg + 8 * q);
+          r.b[SL][nt][q] = *reinterpret_cast<const uint4*>(a.bb + static_cast<int64_t>(brow[nt]) * ldb + kg + 8 * q);
       }
     }
   };
@@ -534,11 +542,13 @@ __global__ __launch_bounds__(256, 2) void k_gemm_fast(GemmArgs a) {
   // work item -> (tile, column block), XCD-aware (see above)
   const int nbn = a.n_blocks;
   const int ntl = ROUTED ? *a.n_tiles : static_cast<int>(cdiv(a.T, GM_BM));
-  const int total = ntl * nbn, chunk = (total + 7) >> 3;
+  const int ks = a.ksplit > 1 ? a.ksplit : 1;
+  const int total = ntl * nbn * ks, chunk = (total + 7) >> 3;
   const int kk = blockIdx.x >> 3;
   if (kk >= chunk) return;
-  const int w = (blockIdx.x & 7) * chunk + kk;
-  if (w >= total) return;
+  const int w0 = (blockIdx.x & 7) * chunk + kk;
+  if (w0 >= total) return;
+  const int split = w0 % ks, w = w0 / ks;
   const int tile = w / nbn, nblk = w - tile * nbn;
   int e = 0, valid, p0;
   if (ROUTED) {
@@ -556,10 +566,12 @@ __global__ __launch_bounds__(256, 2) void k_gemm_fast(GemmArgs a) {
   const int mt_valid = (valid + 31) >> 5;
   const uint16_t* arow;
   {
+    const int64_t lda = a.lda ? a.lda : kdim;
     const int r0 = wv * 32 + ln;
     const int rr = r0 < valid ? r0 : 0;                  // rows past the tile reload row 0 (outputs dropped)
-    if (ROUTED && MODE == GEMM_GATEUP) arow = a.a + static_cast<int64_t>(a.perm[p0 + rr] / a.K) * kdim;
-    else arow = a.a + static_cast<int64_t>(p0 + rr) * kdim;
+    if (ROUTED && MODE == GEMM_GATEUP) arow = a.a + static_cast<int64_t>(a.perm[p0 + rr] / a.K) * lda;
+    else arow = a.a + static_cast<int64_t>(p0 + rr) * lda;
+    arow += static_cast<int64_t>(split) * kdim;
   }
   int brow[2];
   bool bvalid[2];
@@ -596,15 +608,17 @@ __global__ __launch_bounds__(256, 2) void k_gemm_fast(GemmArgs a) {
       default: gemm_dma_mainloop<4>(A0, A1, A2, C0, C1, C2, S0, S1, S2, arow, bq, bs, brow, wv, lane, g, kdim, acc); break;
     }
   } else {
+  GemmArgs as = a;
+  as.bb += static_cast<int64_t>(split) * kdim;
   __shared__ uint4 L0[1024];
   __shared__ uint4 L1[1024];
   __shared__ uint4 L2[NST > 2 ? 1024 : 1];
   __shared__ uint4 L3[NST > 3 ? 1024 : 1];
   switch (mt_valid) {
-    case 1: gemm_fast_mainloop<NVFP4, NST, 1>(a, L0, L1, *reinterpret_cast<uint4(*)[1024]>(&L2[0]), *reinterpret_cast<uint4(*)[1024]>(&L3[0]), arow, bq, bs, brow, wv, lane, g, kdim, acc); break;
-    case 2: gemm_fast_mainloop<NVFP4, NST, 2>(a, L0, L1, *reinterpret_cast<uint4(*)[1024]>(&L2[0]), *reinterpret_cast<uint4(*)[1024]>(&L3[0]), arow, bq, bs, brow, wv, lane, g, kdim, acc); break;
-    case 3: gemm_fast_mainloop<NVFP4, NST, 3>(a, L0, L1, *reinterpret_cast<uint4(*)[1024]>(&L2[0]), *reinterpret_cast<uint4(*)[1024]>(&L3[0]), arow, bq, bs, brow, wv, lane, g, kdim, acc); break;
-    default: gemm_fast_mainloop<NVFP4, NST, 4>(a, L0, L1, *reinterpret_cast<uint4(*)[1024]>(&L2[0]), *reinterpret_cast<uint4(*)[1024]>(&L3[0]), arow, bq, bs, brow, wv, lane, g, kdim, acc); break;
+    case 1: gemm_fast_mainloop<NVFP4, NST, 1>(as, L0, L1, *reinterpret_cast<uint4(*)[1024]>(&L2[0]), *reinterpret_cast<uint4(*)[1024]>(&L3[0]), arow, bq, bs, brow, wv, lane, g, kdim, acc); break;
+    case 2: gemm_fast_mainloop<NVFP4, NST, 2>(as, L0, L1, *reinterpret_cast<uint4(*)[1024]>(&L2[0]), *reinterpret_cast<uint4(*)[1024]>(&L3[0]), arow, bq, bs, brow, wv, lane, g, kdim, acc); break;
+    case 3: gemm_fast_mainloop<NVFP4, NST, 3>(as, L0, L1, *reinterpret_cast<uint4(*)[1024]>(&L2[0]), *reinterpret_cast<uint4(*)[1024]>(&L3[0]), arow, bq, bs, brow, wv, lane, g, kdim, acc); break;
+    default: gemm_fast_mainloop<NVFP4, NST, 4>(as, L0, L1, *reinterpret_cast<uint4(*)[1024]>(&L2[0]), *reinterpret_cast<uint4(*)[1024]>(&L3[0]), arow, bq, bs, brow, wv, lane, g, kdim, acc); break;
   }
   }
   float g0 = 1.0f, g1 = 1.0f;
@@ -638,7 +652,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_fast(GemmArgs a) {
           if (MODE == GEMM_DOWN_BF16)
             static_cast<uint16_t*>(a.out)[orow * a.ldo + n] = f32_to_bf16(acc[mt][nt][j]);
           else
-            static_cast<float*>(a.out)[orow * a.ldo + n] = g0 * acc[mt][nt][j];
+            static_cast<float*>(a.out)[split * a.split_out + orow * a.ldo + n] = g0 * acc[mt][nt][j];
         }
       }
     }

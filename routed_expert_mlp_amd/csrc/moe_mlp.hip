@@ -61,6 +61,7 @@ struct Plan {
   size_t h = 0, hs = 0, y = 0, ys = 0;
   size_t wsplit = 0;                                                             // router weight, 3 bf16 planes
   int logit_planes = 1;
+  int logit_splits = 1;       // reduction parts of the split-weight logits GEMM
   size_t total = 0;
   int64_t max_tiles = 0;
 };
@@ -104,8 +105,11 @@ Plan make_plan(const moe_mlp_config* c, int64_t T, int prefill) {
   if (mfma_logits(c, T, prefill)) {
     p.logit_planes = 3;
     p.wsplit = a.take(size_t(3 * E * H) * 2);
+    // the logits GEMM has only ceil(T/128) x ceil(3E/256) output tiles: cut
+    // its reduction into 4 parts when H allows, for 4x the workgroups
+    if (H % 256 == 0) p.logit_splits = 4;
   }
-  p.logits = a.take(size_t(T * E * p.logit_planes) * 4);
+  p.logits = a.take(size_t(T * E * p.logit_planes * p.logit_splits) * 4);
   p.ids = a.take(size_t(S) * 4);
   p.wts = a.take(size_t(S) * 4);
   if (prefill) {
@@ -210,10 +214,10 @@ void topk_bucket(int E, const float* logits, const float* bias, int T, int K, fl
 }
 
 void topk_tokens(int E, const float* logits, const float* bias, int T, int K, float rsf, int32_t* ids,
-                 float* wts, int32_t* ids_out, float* w_out, hipStream_t s, Ev ev, int planes = 1) {
+                 float* wts, int32_t* ids_out, float* w_out, hipStream_t s, Ev ev, int planes = 1, int splits = 1) {
   with_nj(E, [&](auto nj) {
     launch(k_topk<decltype(nj)::value>, dim3(static_cast<unsigned>(cdiv(T, 4))), dim3(256), s, ev.a, ev.b, logits,
-           bias, T, E, K, rsf, ids, wts, ids_out, w_out, planes);
+           bias, T, E, K, rsf, ids, wts, ids_out, w_out, planes, splits);
   });
 }
 
@@ -274,7 +278,7 @@ void gemm(const GemmArgs& a0, int64_t m_tiles, hipStream_t s, Ev ev) {
   }
   if (a.kdim % 64 == 0) {
     a.n_blocks = static_cast<int>(cdiv(a.half_n, MODE == GEMM_GATEUP ? 128 : 256));
-    const int64_t work = m_tiles * a.n_blocks;
+    const int64_t work = m_tiles * a.n_blocks * (a.ksplit > 1 ? a.ksplit : 1);
     const dim3 grid(static_cast<unsigned>(8 * cdiv(work, 8)));
     constexpr int NST = NVFP4 ? 4 : 3;
     launch(k_gemm_fast<NVFP4, MODE, ROUTED, NST>, grid, dim3(256), s, ev.a, ev.b, a);
@@ -326,8 +330,12 @@ void router_logits_plan(const Plan& p, void* ws, const uint16_t* x, const float*
   uint16_t* planes = at<uint16_t>(ws, p.wsplit);
   const int64_t n = static_cast<int64_t>(E) * H;
   launch(k_split_bf16x3, dim3(static_cast<unsigned>(cdiv(n / 8, 256))), dim3(256), s, ev.a, nullptr, wr, planes, n);
-  gemm<false, GEMM_DOWN_F32, false>(bf16_gemm_args(x, H, planes, 3 * E, static_cast<int>(T), logits, 3 * E, 1.0f),
-                                    cdiv(T, GM_BM), s, Ev{nullptr, ev.b});
+  GemmArgs ga = bf16_gemm_args(x, H / p.logit_splits, planes, 3 * E, static_cast<int>(T), logits, 3 * E, 1.0f);
+  ga.lda = H;
+  ga.ldb = H;
+  ga.ksplit = p.logit_splits;
+  ga.split_out = T * 3 * E;
+  gemm<false, GEMM_DOWN_F32, false>(ga, cdiv(T, GM_BM), s, Ev{nullptr, ev.b});
 }
 
 const char* const kDecodeStages[] = {"router_logits", "topk_bucket", "shared_gateup", "routed_gateup",
@@ -492,7 +500,8 @@ int run_layer(const moe_mlp_config* c, const moe_mlp_weights* w, const uint16_t*
     router_logits_plan(p, ws, x, w->router_w, logits, T, H, E, s, ev(0));
   }
   if (prefill) {
-    topk_tokens(E, logits, w->router_bias, Ti, K, rsf, ids, wts, ids_out, w_out, s, ev(1), p.logit_planes);
+    topk_tokens(E, logits, w->router_bias, Ti, K, rsf, ids, wts, ids_out, w_out, s, ev(1), p.logit_planes,
+                p.logit_splits);
     Perm pm{at<int32_t>(ws, p.count), at<int32_t>(ws, p.offset), at<int32_t>(ws, p.perm),
             at<int32_t>(ws, p.n_tiles), at<int32_t>(ws, p.tile_e), at<int32_t>(ws, p.tile_m0)};
     const Ev pe = ev(2);
@@ -657,7 +666,7 @@ int moe_router_topk(const moe_mlp_config* cfg, const float* router_w, const floa
   float* logits = at<float>(workspace, p.logits);
   router_logits_plan(p, workspace, x, router_w, logits, T, cfg->hidden, cfg->num_experts, s, Ev{});
   topk_tokens(cfg->num_experts, logits, router_bias, static_cast<int>(T), cfg->top_k,
-              cfg->routed_scaling_factor, ids, w, nullptr, nullptr, s, Ev{}, p.logit_planes);
+              cfg->routed_scaling_factor, ids, w, nullptr, nullptr, s, Ev{}, p.logit_planes, p.logit_splits);
   return launch_status();
 }
 

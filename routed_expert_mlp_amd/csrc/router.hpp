@@ -190,22 +190,30 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
 
 // Logit e of a row: one fp32 value, or (planes == 3, the split-weight router
 // GEMM) the sum of the three partial logits against the hi, mid and lo bf16
-// parts of the router weight, added as (lo + mid) + hi.
-__device__ __forceinline__ float logit_of(const float* __restrict__ lrow, int E, int planes, int e) {
-  return planes == 3 ? (lrow[2 * E + e] + lrow[E + e]) + lrow[e] : lrow[e];
+// parts of the router weight, added as (lo + mid) + hi.  With splits > 1 the
+// GEMM's reduction was cut into that many parts whose rows sit sstride floats
+// apart; their sums are added in part order.
+__device__ __forceinline__ float logit_of(const float* __restrict__ lrow, int E, int planes, int e, int splits = 1,
+                                          int64_t sstride = 0) {
+  float v = planes == 3 ? (lrow[2 * E + e] + lrow[E + e]) + lrow[e] : lrow[e];
+  for (int q = 1; q < splits; ++q) {
+    const float* l = lrow + q * sstride;
+    v += planes == 3 ? (l[2 * E + e] + l[E + e]) + l[e] : l[e];
+  }
+  return v;
 }
 
 template <int NJ>
 __device__ __forceinline__ int topk_wave(const float* __restrict__ lrow, const float* __restrict__ bias, int E,
                                          int K, float rsf, int want, int32_t* ids, float* wts, int32_t* ids2,
-                                         float* wts2, int planes = 1) {
+                                         float* wts2, int planes = 1, int splits = 1, int64_t sstride = 0) {
   const int lane = threadIdx.x & 63;
   uint64_t key[NJ];
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
     const int e = lane + 64 * j;
     key[j] = e < E ? u64_of(0xFFFFFFFFu - static_cast<uint32_t>(e),
-                            f32_order_bits(1.0f / (1.0f + expf(-logit_of(lrow, E, planes, e))) + bias[e]))
+                            f32_order_bits(1.0f / (1.0f + expf(-logit_of(lrow, E, planes, e, splits, sstride))) + bias[e]))
                    : 0;                          // below every real key
   }
 #pragma unroll
@@ -232,7 +240,7 @@ __device__ __forceinline__ int topk_wave(const float* __restrict__ lrow, const f
   }
   if (ids) {
     // the same expression as above on the same logit: the same bits
-    const float my_s = lane < K ? 1.0f / (1.0f + expf(-logit_of(lrow, E, planes, my_id))) : 0.0f;
+    const float my_s = lane < K ? 1.0f / (1.0f + expf(-logit_of(lrow, E, planes, my_id, splits, sstride))) : 0.0f;
     float sum = 0.0f;
     for (int k = 0; k < K; ++k) sum += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_s), k));
     if (lane < K) {
@@ -250,12 +258,13 @@ template <int NJ>
 __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ logits, const float* __restrict__ bias,
                                               int T, int E, int K, float rsf, int32_t* __restrict__ ids,
                                               float* __restrict__ wts, int32_t* ids_out, float* w_out,
-                                              int planes) {
+                                              int planes, int splits) {
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
   const int64_t o = static_cast<int64_t>(t) * K;
   topk_wave<NJ>(logits + static_cast<int64_t>(t) * E * planes, bias, E, K, rsf, 0, ids + o, wts + o,
-                ids_out ? ids_out + o : nullptr, w_out ? w_out + o : nullptr, planes);
+                ids_out ? ids_out + o : nullptr, w_out ? w_out + o : nullptr, planes, splits,
+                static_cast<int64_t>(T) * E * planes);
 }
 
 // ---------------------------------------------------------------------------
