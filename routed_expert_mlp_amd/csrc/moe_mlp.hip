@@ -15,6 +15,7 @@
 #include "common.hpp"
 #include "decode1.hpp"
 #include "gemm.hpp"
+#include "gemm_bf16.hpp"
 #include "gemm_fp4.hpp"
 #include "gemv.hpp"
 #include "permute.hpp"
@@ -259,7 +260,9 @@ void gemv(const GemvArgs& a, int groups, hipStream_t s, Ev ev) {
 }
 
 // Routed NVFP4 projections with a reduction length that is a multiple of 256
-// and at least 512 take k_gemm_nvfp4; other reduction lengths that are a multiple of 64 the
+// and at least 512 take k_gemm_nvfp4, BF16 projections (shared expert, dense
+// FFN, router logits) with a reduction length that is a multiple of 128 take
+// k_gemm_bf16; other reduction lengths that are a multiple of 64 the
 // 32x32x16-MFMA kernel (k_gemm_fast); the rest the general 16x16x32 kernel.
 template <bool NVFP4, int MODE, bool ROUTED>
 void gemm(const GemmArgs& a0, int64_t m_tiles, hipStream_t s, Ev ev) {
@@ -273,6 +276,17 @@ void gemm(const GemmArgs& a0, int64_t m_tiles, hipStream_t s, Ev ev) {
       a.n_blocks = static_cast<int>(cdiv(a.half_n, MODE == GEMM_GATEUP ? F4_WROWS / 2 : F4_WROWS));
       const int64_t work = m_tiles * a.n_blocks;
       launch(k_gemm_nvfp4<MODE>, dim3(static_cast<unsigned>(8 * cdiv(work, 8))), dim3(F4_THREADS), s, ev.a, ev.b, a);
+      return;
+    }
+  }
+  if constexpr (!NVFP4 && !ROUTED) {
+    // 32-bit DMA offsets: rows times row stride (in bytes) below 2^31
+    const int64_t lda = a.lda ? a.lda : a.kdim, ldb = a.ldb ? a.ldb : a.kdim;
+    const int64_t w_rows = MODE == GEMM_GATEUP ? 2 * int64_t(a.half_n) : int64_t(a.half_n);
+    if (a.kdim % 128 == 0 && int64_t(a.T) * lda * 2 < (int64_t(1) << 31) && w_rows * ldb * 2 < (int64_t(1) << 31)) {
+      a.n_blocks = static_cast<int>(cdiv(a.half_n, MODE == GEMM_GATEUP ? B16_BN / 2 : B16_BN));
+      const int64_t work = cdiv(a.T, B16_BM) * a.n_blocks * (a.ksplit > 1 ? a.ksplit : 1);
+      launch(k_gemm_bf16<MODE>, dim3(static_cast<unsigned>(8 * cdiv(work, 8))), dim3(B16_THREADS), s, ev.a, ev.b, a);
       return;
     }
   }
