@@ -220,6 +220,19 @@ def test_dense_ragged(prefill):
     _dense("ragged_dense_prefill", prefill, 300, T=256 if not prefill else 300)
 
 
+# BF16 tile GEMM shapes: row tails of 44, 77 and 1 rows; weight-row blocks cut at
+# the matrix edge (gate/up 320 = 2.5 x 128 columns, down 640 = 2.5 x 256 rows);
+# the shortest reduction (128 = one pair of 64-wide stages); a down reduction
+# of 320 (not a multiple of 128) that takes the 32x32 fallback kernel.
+DENSE_TILES = [dict(T=300, H=640, Id=384), dict(T=77, H=512, Id=320),
+               dict(T=513, H=256, Id=1024), dict(T=40, H=128, Id=128)]
+
+
+@pytest.mark.parametrize("overrides", DENSE_TILES, ids=[f"T{o['T']}_H{o['H']}_Id{o['Id']}" for o in DENSE_TILES])
+def test_dense_bf16_tiles(overrides):
+    _dense("ragged_dense_prefill", True, 100000, **overrides)
+
+
 def test_dense_prefill_full_size():
     _dense("dense_prefill_t4096", True, 6)
 
