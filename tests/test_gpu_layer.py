@@ -131,11 +131,14 @@ def _fresh(name, prefill, n_sample=64, w13_g=None, w2_g=None, **overrides):
 # the matrix edge in gate/up and in down, reductions of 8, 12 and 16 stages
 # (no, one and two middle blocks of the DMA schedule), and a 256-long
 # reduction (the other grouped GEMM kernel); every token checked.
+# H=1024 I=160 and H=256 I=512 run one projection on the tile kernel and the
+# other on the fallback kernel.
 FP4_TILES = [dict(T=600, H=512, I=512, E=16, K=4, Is=256),
              dict(T=300, H=768, I=512, E=8, K=2, Is=96),
              dict(T=200, H=1024, I=160, E=8, K=2, Is=96),
              dict(T=700, H=512, I=768, E=4, K=2, Is=0),
-             dict(T=100, H=256, I=256, E=4, K=2, Is=64)]
+             dict(T=100, H=256, I=256, E=4, K=2, Is=64),
+             dict(T=150, H=256, I=512, E=8, K=2, Is=64)]
 
 
 @pytest.mark.parametrize("overrides", FP4_TILES, ids=[f"T{o['T']}_H{o['H']}_I{o['I']}_E{o['E']}" for o in FP4_TILES])
