@@ -118,6 +118,17 @@ typedef struct moe_mlp_weights {
   const uint16_t* shared_w2;    /* [H, Is] bf16 */
   const uint16_t* dense_w13;    /* [2 Id, H] bf16: gate rows then up rows (DENSE) */
   const uint16_t* dense_w2;     /* [H, Id] bf16 (DENSE) */
+  /* Optional (NULL = not given): the routed codes and scales again, in the
+   * tile layout of moe_nvfp4_tile_pack (same sizes as the row-major arrays).
+   * When a projection's codes AND scales are given, the grouped-GEMM form
+   * (moe_mlp_prefill, decode from 64 tokens) reads them instead of the
+   * row-major arrays wherever its NVFP4 tile kernel runs; the values and the
+   * arithmetic are the same, so the results are bitwise the same.  The
+   * row-major arrays stay required (the GEMV forms read them). */
+  const uint8_t*  w13_q_tiled;  /* moe_nvfp4_tile_pack(w13_q, w13_s, E, 2I, H, ...) codes */
+  const uint8_t*  w13_s_tiled;  /* ... and scales */
+  const uint8_t*  w2_q_tiled;   /* moe_nvfp4_tile_pack(w2_q, w2_s, E, H, I, ...) codes */
+  const uint8_t*  w2_s_tiled;   /* ... and scales */
 } moe_mlp_weights;
 
 /*
@@ -208,6 +219,28 @@ int moe_router_topk(const moe_mlp_config* cfg, const float* router_w, const floa
  */
 int moe_nvfp4_dequant(const uint8_t* q, const uint8_t* s, float global, int64_t rows,
                       int64_t cols, float* out_f32, uint16_t* out_bf16, void* stream);
+
+/*
+ * NVFP4 weights (Module glm5next_mlp, the NVFP4 expert weights: E2M1 codes and
+ * one E4M3 scale per 16 columns of a row) copied from the row-major layout
+ * into the tile layout that the grouped GEMM's loads read in whole 128-byte
+ * lines: `mats` matrices of [rows, cols], codes q [mats, rows, cols/2] and
+ * scales s [mats, rows, cols/16] -> q_tiled and s_tiled of the same sizes
+ * (device pointers, 16-byte aligned, caller-owned; the inputs are only
+ * read).  Done once when the weights are loaded.
+ *   q_tiled: for matrix m, 16-row group r and 128-column unit u, a 1024-byte
+ *     block at ((m * rows/16 + r) * cols/128 + u) * 1024 whose 16-byte piece
+ *     L (0..63) is bytes 64u + 16 ((L % 4) ^ z(L / 4)) .. +15 of the codes of
+ *     row 16r + L/4, with z(i) = ((i >> 1) & 3) ^ ((i >> 3) & 1) (the XOR
+ *     swizzle of the kernel's LDS layout).
+ *   s_tiled: for matrix m, 32-row group r and 256-column unit v, a 512-byte
+ *     block at ((m * rows/32 + r) * cols/256 + v) * 512 whose 16-byte piece
+ *     l (0..31) is scale bytes 16v .. 16v+15 of row 32r + l.
+ * rows a multiple of 32, cols a multiple of 256 (BAD_SHAPE otherwise);
+ * mats >= 0.  Stream-ordered; no allocation.
+ */
+int moe_nvfp4_tile_pack(const uint8_t* q, const uint8_t* s, int64_t mats, int64_t rows, int64_t cols,
+                        uint8_t* q_tiled, uint8_t* s_tiled, void* stream);
 
 /* Human-readable name of a status code (static string; never NULL). */
 const char* moe_mlp_status_string(int status);

@@ -36,7 +36,8 @@ KIND_ROUTED = 0
 KIND_DENSE = 1
 
 EXPORTED = ("moe_mlp_workspace_size", "moe_mlp_decode", "moe_mlp_prefill", "moe_mlp_forward_profiled",
-            "moe_mlp_stage_name", "moe_router_topk", "moe_nvfp4_dequant", "moe_mlp_status_string")
+            "moe_mlp_stage_name", "moe_router_topk", "moe_nvfp4_dequant", "moe_nvfp4_tile_pack",
+            "moe_mlp_status_string")
 
 
 class MoeMlpError(RuntimeError):
@@ -55,7 +56,8 @@ class moe_mlp_config(ctypes.Structure):
 class moe_mlp_weights(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
         "router_w", "router_bias", "w13_q", "w13_s", "w13_g", "w2_q", "w2_s", "w2_g",
-        "shared_w13", "shared_w2", "dense_w13", "dense_w2")]
+        "shared_w13", "shared_w2", "dense_w13", "dense_w2",
+        "w13_q_tiled", "w13_s_tiled", "w2_q_tiled", "w2_s_tiled")]
 
 
 _LIB = None
@@ -80,6 +82,7 @@ def lib() -> ctypes.CDLL:
         L.moe_mlp_stage_name.restype = ctypes.c_char_p
         L.moe_router_topk.argtypes = [cfgp, vp, vp, vp, i64, vp, vp, vp, sz, vp]
         L.moe_nvfp4_dequant.argtypes = [vp, vp, ctypes.c_float, i64, i64, vp, vp, vp]
+        L.moe_nvfp4_tile_pack.argtypes = [vp, vp, i64, i64, i64, vp, vp, vp]
         L.moe_mlp_status_string.argtypes = [ctypes.c_int]
         L.moe_mlp_status_string.restype = ctypes.c_char_p
         for n in ("moe_mlp_workspace_size", "moe_mlp_decode", "moe_mlp_prefill", "moe_router_topk",
@@ -135,6 +138,11 @@ class Weights:
     shared_w2: Optional[torch.Tensor] = None     # [H, Is] bf16
     dense_w13: Optional[torch.Tensor] = None     # [2 Id, H] bf16
     dense_w2: Optional[torch.Tensor] = None      # [H, Id] bf16
+    # optional tile-layout copies of the routed codes / scales (moe_nvfp4_tile_pack)
+    w13_q_tiled: Optional[torch.Tensor] = None   # [E, 2I, H/2] u8
+    w13_s_tiled: Optional[torch.Tensor] = None   # [E, 2I, H/16] u8
+    w2_q_tiled: Optional[torch.Tensor] = None    # [E, H, I/2] u8
+    w2_s_tiled: Optional[torch.Tensor] = None    # [E, H, I/16] u8
 
     def check(self, cfg: Config) -> None:
         H, I, E = cfg.hidden, cfg.moe_intermediate, cfg.num_experts
@@ -147,7 +155,10 @@ class Weights:
             want.update(router_w=((E, H), torch.float32), router_bias=((E,), torch.float32),
                         w13_q=((E, 2 * I, H // 2), torch.uint8), w13_s=((E, 2 * I, H // 16), torch.uint8),
                         w13_g=((E, 2), torch.float32), w2_q=((E, H, I // 2), torch.uint8),
-                        w2_s=((E, H, I // 16), torch.uint8), w2_g=((E,), torch.float32))
+                        w2_s=((E, H, I // 16), torch.uint8), w2_g=((E,), torch.float32),
+                        w13_q_tiled=((E, 2 * I, H // 2), torch.uint8),
+                        w13_s_tiled=((E, 2 * I, H // 16), torch.uint8),
+                        w2_q_tiled=((E, H, I // 2), torch.uint8), w2_s_tiled=((E, H, I // 16), torch.uint8))
             if cfg.n_shared_experts:
                 want["shared_w13"] = ((2 * Is, H), torch.bfloat16)
                 want["shared_w2"] = ((H, Is), torch.bfloat16)
@@ -319,3 +330,38 @@ def moe_nvfp4_dequant(q: torch.Tensor, s: torch.Tensor, global_scale: float, out
     st = lib().moe_nvfp4_dequant(q.data_ptr(), s.data_ptr(), float(global_scale), rows, cols, _ptr(out_f32),
                                  _ptr(out_bf16), _stream(stream))
     _check(st, "moe_nvfp4_dequant")
+
+
+def moe_nvfp4_tile_pack(q: torch.Tensor, s: torch.Tensor, q_tiled=None, s_tiled=None, stream=None):
+    """Row-major NVFP4 codes q [.., rows, cols/2] and scales s [.., rows, cols/16]
+    (u8, any number of leading matrix dims) -> (q_tiled, s_tiled) of the same
+    shapes in the grouped GEMM's tile layout (see include/moe_mlp.h)."""
+    rows, half = q.shape[-2], q.shape[-1]
+    cols = 2 * half
+    mats = q.numel() // max(1, rows * half)
+    _check_tensor(q, "q", tuple(q.shape), torch.uint8)
+    _check_tensor(s, "s", tuple(q.shape[:-1]) + (cols // 16,), torch.uint8)
+    q_tiled = torch.empty_like(q) if q_tiled is None else q_tiled
+    s_tiled = torch.empty_like(s) if s_tiled is None else s_tiled
+    _check_tensor(q_tiled, "q_tiled", tuple(q.shape), torch.uint8)
+    _check_tensor(s_tiled, "s_tiled", tuple(s.shape), torch.uint8)
+    st = lib().moe_nvfp4_tile_pack(q.data_ptr(), s.data_ptr(), mats, rows, cols, q_tiled.data_ptr(),
+                                   s_tiled.data_ptr(), _stream(stream))
+    _check(st, "moe_nvfp4_tile_pack")
+    return q_tiled, s_tiled
+
+
+def _tileable(q: torch.Tensor) -> bool:
+    return q.shape[-2] % 32 == 0 and (2 * q.shape[-1]) % 256 == 0
+
+
+def with_tiled_weights(w: Weights, stream=None) -> Weights:
+    """A copy of w whose routed codes and scales also come in the tile layout,
+    for each projection whose shape has one (rows a multiple of 32, columns a
+    multiple of 256); allocated by torch, the row-major tensors are shared."""
+    q13 = s13 = q2 = s2 = None
+    if _tileable(w.w13_q):
+        q13, s13 = moe_nvfp4_tile_pack(w.w13_q, w.w13_s, stream=stream)
+    if _tileable(w.w2_q):
+        q2, s2 = moe_nvfp4_tile_pack(w.w2_q, w.w2_s, stream=stream)
+    return dataclasses.replace(w, w13_q_tiled=q13, w13_s_tiled=s13, w2_q_tiled=q2, w2_s_tiled=s2)

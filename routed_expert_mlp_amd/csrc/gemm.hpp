@@ -45,6 +45,8 @@ struct GemmArgs {
   const uint8_t* bq;         // NVFP4 codes [E][rows][kdim/2]
   const uint8_t* bs;         // NVFP4 scales [E][rows][kdim/16]
   const uint16_t* bb;        // BF16 weights [rows][kdim]
+  const uint8_t* bq_t;       // NVFP4 codes and scales in the tile layout (tile
+  const uint8_t* bs_t;       //   kernel only; null = read bq / bs)
   int64_t stride_q, stride_s;
   const float* gscale;       // routed globals (gate/up: [E,2]; down: [E]); null = 1
   int half_n;                // gate/up: I (gate rows, up rows = I + j); down: output columns

@@ -31,6 +31,14 @@
 //     (the next k-step's activation fragments are read during the current
 //     k-step's MFMAs); scale words are read by asm.
 //
+//   * Weight layout.  In the row-major layout a code instruction reads 64
+//     bytes of each of 16 rows (16 half lines) and a scale instruction 16
+//     bytes of each of 64 rows (64 lines).  The tile layout
+//     (k_nvfp4_tile_pack) stores exactly the bytes of one instruction
+//     contiguously, in the order its lanes deliver them to LDS (the LDS
+//     swizzle included): 1 KB of codes, two 512-byte runs of scales.  LDS
+//     contents, and so everything after the loads, are the same for both.
+//
 // Rows past the tile's valid count load row 0 again (outputs dropped); weight
 // rows past the matrix edge load row 0 again (outputs not stored).  Requires
 // kdim % 256 == 0 and kdim >= 512.
@@ -89,7 +97,7 @@ struct F4Src {
   uint32_t so;
 };
 
-template <int MODE, int MTV>
+template <int MODE, int MTV, bool TILED>
 __device__ __forceinline__ void f4_mainloop(const F4Lds& L, const F4Src& src, int wv, int lane, int kdim,
                                             f32x16 (&acc)[4][2]) {
   constexpr int S_BYTES = F4_WROWS * 16;       // one scale group (four stages)
@@ -108,16 +116,21 @@ __device__ __forceinline__ void f4_mainloop(const F4Lds& L, const F4Src& src, in
                                        (void __attribute__((address_space(3)))*)(L.a[SL] + wv * 128 + i * 64),
                                        16, 0, 0);
   };
+  // code unit u (two stages) and scale group v (four stages) advance by 64
+  // and 16 bytes along a row in the row-major layout, by a 1 KB and a 512-byte
+  // block in the tile layout
+  constexpr uint32_t C_STEP = TILED ? 1024u : 64u;
+  constexpr uint32_t S_STEP = TILED ? 512u : 16u;
   auto issue_c = [&](int u, auto slot_c) {
     constexpr int SL = decltype(slot_c)::value;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      __builtin_amdgcn_global_load_lds(static_cast<const void*>(src.c + (src.co[i] + 64u * u)),
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(src.c + (src.co[i] + C_STEP * u)),
                                        (void __attribute__((address_space(3)))*)(L.c[SL] + wv * 256 + i * 64),
                                        16, 0, 0);
   };
   auto issue_s = [&](int v) {
-    __builtin_amdgcn_global_load_lds(static_cast<const void*>(src.s + (src.so + 16u * v)),
+    __builtin_amdgcn_global_load_lds(static_cast<const void*>(src.s + (src.so + S_STEP * v)),
                                      (void __attribute__((address_space(3)))*)(L.s + (v & 1) * S_BYTES + wv * 1024),
                                      16, 0, 0);
   };
@@ -228,8 +241,9 @@ __device__ __forceinline__ void f4_mainloop(const F4Lds& L, const F4Src& src, in
 // Grid: 1-D, XCD-aware as in k_gemm_fast (block b runs on XCD b % 8; each XCD
 // takes a contiguous run of (tile, column block) work, column blocks of a
 // tile back to back).  n_blocks = column blocks of F4_WROWS weight rows
-// (gate/up: 256 gate columns each).
-template <int MODE>
+// (gate/up: 256 gate columns each).  TILED: codes and scales in the tile
+// layout (a.bq_t, a.bs_t).
+template <int MODE, bool TILED>
 __global__ __launch_bounds__(F4_THREADS, 1) void k_gemm_nvfp4(GemmArgs a) {
   const int nbn = a.n_blocks;
   const int ntl = *a.n_tiles;
@@ -268,16 +282,28 @@ __global__ __launch_bounds__(F4_THREADS, 1) void k_gemm_nvfp4(GemmArgs a) {
     }
   };
   // code DMA: instruction i of wave wv covers workgroup rows 16 (4 wv + i) .. +15,
-  // 4 lanes per row, lane -> 16-byte piece (lane & 3) ^ swizzle of a 64-byte unit
-  src.c = a.bq + e * a.stride_q;
+  // 4 lanes per row, lane -> 16-byte piece q = (lane & 3) ^ swizzle of a 64-byte
+  // unit.  Tile layout: row R's piece q sits at 16 (4 (R % 16) + (q ^ z(R % 16)))
+  // of its 16-row group's block, i.e. at 16 lane when the rows are in the matrix
+  // (z = the same swizzle, which depends on R % 16 only).
+  src.c = (TILED ? a.bq_t : a.bq) + e * a.stride_q;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int p = 16 * (4 * wv + i) + (lane >> 2);
-    src.co[i] = static_cast<uint32_t>(wrow(p) * (kdim >> 1) + 16 * ((lane & 3) ^ f4_swz_c(p)));
+    const int q = (lane & 3) ^ f4_swz_c(p);
+    const int64_t R = wrow(p);
+    src.co[i] = TILED ? static_cast<uint32_t>((R >> 4) * (kdim >> 7) * 1024 +
+                                              16 * (4 * (R & 15) + (q ^ f4_swz_c(static_cast<int>(R & 15)))))
+                      : static_cast<uint32_t>(R * (kdim >> 1) + 16 * q);
   }
-  // scale DMA: workgroup row 64 wv + lane, 16 bytes (four stages) per group
-  src.s = a.bs + e * a.stride_s;
-  src.so = static_cast<uint32_t>(wrow(64 * wv + lane) * (kdim >> 4));
+  // scale DMA: workgroup row 64 wv + lane, 16 bytes (four stages) per group;
+  // tile layout: piece R % 32 of its 32-row group's block
+  src.s = (TILED ? a.bs_t : a.bs) + e * a.stride_s;
+  {
+    const int64_t R = wrow(64 * wv + lane);
+    src.so = TILED ? static_cast<uint32_t>((R >> 5) * (kdim >> 8) * 512 + 16 * (R & 31))
+                   : static_cast<uint32_t>(R * (kdim >> 4));
+  }
 
   __shared__ uint4 la0[1024], la1[1024], la2[1024], la3[1024];   // activation ring (16 KB each)
   __shared__ uint4 lc0[2048], lc1[2048];                          // code ring (32 KB each)
@@ -291,10 +317,10 @@ __global__ __launch_bounds__(F4_THREADS, 1) void k_gemm_nvfp4(GemmArgs a) {
 #pragma unroll
       for (int j = 0; j < 16; ++j) acc[mt][nt][j] = 0.0f;
   switch ((valid + 31) >> 5) {
-    case 1: f4_mainloop<MODE, 1>(L, src, wv, lane, kdim, acc); break;
-    case 2: f4_mainloop<MODE, 2>(L, src, wv, lane, kdim, acc); break;
-    case 3: f4_mainloop<MODE, 3>(L, src, wv, lane, kdim, acc); break;
-    default: f4_mainloop<MODE, 4>(L, src, wv, lane, kdim, acc); break;
+    case 1: f4_mainloop<MODE, 1, TILED>(L, src, wv, lane, kdim, acc); break;
+    case 2: f4_mainloop<MODE, 2, TILED>(L, src, wv, lane, kdim, acc); break;
+    case 3: f4_mainloop<MODE, 3, TILED>(L, src, wv, lane, kdim, acc); break;
+    default: f4_mainloop<MODE, 4, TILED>(L, src, wv, lane, kdim, acc); break;
   }
 
   const int mt_valid = (valid + 31) >> 5;
@@ -327,6 +353,33 @@ __global__ __launch_bounds__(F4_THREADS, 1) void k_gemm_nvfp4(GemmArgs a) {
         }
       }
     }
+  }
+}
+
+// Row-major NVFP4 codes / scales -> the tile layout (moe_nvfp4_tile_pack):
+// one thread per 16-byte piece, codes first (mats * rows * cols/32 pieces),
+// then scales (mats * rows * cols/256 pieces).  rows % 32 == 0, cols % 256 == 0.
+__global__ __launch_bounds__(256) void k_nvfp4_tile_pack(const uint8_t* __restrict__ q,
+                                                         const uint8_t* __restrict__ s, int64_t mats, int64_t rows,
+                                                         int64_t cols, uint8_t* __restrict__ qt,
+                                                         uint8_t* __restrict__ st) {
+  const int64_t nq = mats * rows * (cols >> 5), ns = mats * rows * (cols >> 8);
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (idx < nq) {
+    const int L = static_cast<int>(idx & 63);
+    const int64_t blk = idx >> 6, units = cols >> 7, groups = rows >> 4;
+    const int64_t u = blk % units, r = (blk / units) % groups, m = blk / units / groups;
+    const int64_t row = m * rows + 16 * r + (L >> 2);
+    const int piece = (L & 3) ^ f4_swz_c(L >> 2);
+    reinterpret_cast<uint4*>(qt)[idx] =
+        *reinterpret_cast<const uint4*>(q + row * (cols >> 1) + 64 * u + 16 * piece);
+  } else if (idx < nq + ns) {
+    const int64_t j = idx - nq;
+    const int l = static_cast<int>(j & 31);
+    const int64_t blk = j >> 5, units = cols >> 8, groups = rows >> 5;
+    const int64_t v = blk % units, r = (blk / units) % groups, m = blk / units / groups;
+    const int64_t row = m * rows + 32 * r + l;
+    reinterpret_cast<uint4*>(st)[j] = *reinterpret_cast<const uint4*>(s + row * (cols >> 4) + 16 * v);
   }
 }
 

@@ -171,6 +171,11 @@ int validate_weights(const moe_mlp_config* c, const moe_mlp_weights* w) {
     if (!need[i]) return MOE_MLP_ERR_KIND_MISMATCH;
   for (int i = 0; i < n; ++i)
     if (!aligned(need[i])) return MOE_MLP_ERR_MISALIGNED;
+  if (c->kind == MOE_MLP_KIND_ROUTED) {   // the optional tile-layout copies
+    const void* opt[4] = {w->w13_q_tiled, w->w13_s_tiled, w->w2_q_tiled, w->w2_s_tiled};
+    for (const void* q : opt)
+      if (q && !aligned(q)) return MOE_MLP_ERR_MISALIGNED;
+  }
   return MOE_MLP_OK;
 }
 
@@ -274,8 +279,11 @@ void gemm(const GemmArgs& a0, int64_t m_tiles, hipStream_t s, Ev ev) {
     if (a.kdim % 256 == 0 && a.kdim >= 512 && int64_t(a.T) * a.kdim * 2 < (int64_t(1) << 31) &&
         w_rows * a.kdim / 2 < (int64_t(1) << 31)) {
       a.n_blocks = static_cast<int>(cdiv(a.half_n, MODE == GEMM_GATEUP ? F4_WROWS / 2 : F4_WROWS));
-      const int64_t work = m_tiles * a.n_blocks;
-      launch(k_gemm_nvfp4<MODE>, dim3(static_cast<unsigned>(8 * cdiv(work, 8))), dim3(F4_THREADS), s, ev.a, ev.b, a);
+      const dim3 grid(static_cast<unsigned>(8 * cdiv(m_tiles * a.n_blocks, 8)));
+      if (a.bq_t && a.bs_t)
+        launch(k_gemm_nvfp4<MODE, true>, grid, dim3(F4_THREADS), s, ev.a, ev.b, a);
+      else
+        launch(k_gemm_nvfp4<MODE, false>, grid, dim3(F4_THREADS), s, ev.a, ev.b, a);
       return;
     }
   }
@@ -542,6 +550,10 @@ int run_layer(const moe_mlp_config* c, const moe_mlp_weights* w, const uint16_t*
     gu.kdim = H;
     gu.bq = w->w13_q;
     gu.bs = w->w13_s;
+    if (w->w13_q_tiled && w->w13_s_tiled) {
+      gu.bq_t = w->w13_q_tiled;
+      gu.bs_t = w->w13_s_tiled;
+    }
     gu.stride_q = int64_t(2) * I * H / 2;
     gu.stride_s = int64_t(2) * I * H / 16;
     gu.gscale = w->w13_g;
@@ -556,6 +568,10 @@ int run_layer(const moe_mlp_config* c, const moe_mlp_weights* w, const uint16_t*
     gd.kdim = I;
     gd.bq = w->w2_q;
     gd.bs = w->w2_s;
+    if (w->w2_q_tiled && w->w2_s_tiled) {
+      gd.bq_t = w->w2_q_tiled;
+      gd.bs_t = w->w2_s_tiled;
+    }
     gd.stride_q = int64_t(H) * I / 2;
     gd.stride_s = int64_t(H) * I / 16;
     gd.gscale = w->w2_g;
@@ -681,6 +697,19 @@ int moe_router_topk(const moe_mlp_config* cfg, const float* router_w, const floa
   router_logits_plan(p, workspace, x, router_w, logits, T, cfg->hidden, cfg->num_experts, s, Ev{});
   topk_tokens(cfg->num_experts, logits, router_bias, static_cast<int>(T), cfg->top_k,
               cfg->routed_scaling_factor, ids, w, nullptr, nullptr, s, Ev{}, p.logit_planes, p.logit_splits);
+  return launch_status();
+}
+
+int moe_nvfp4_tile_pack(const uint8_t* q, const uint8_t* s, int64_t mats, int64_t rows, int64_t cols,
+                        uint8_t* q_tiled, uint8_t* s_tiled, void* stream) {
+  if (!q || !s || !q_tiled || !s_tiled) return MOE_MLP_ERR_NULL_ARG;
+  if (mats < 0 || rows <= 0 || cols <= 0 || rows % 32 != 0 || cols % 256 != 0) return MOE_MLP_ERR_BAD_SHAPE;
+  if (!aligned(q) || !aligned(s) || !aligned(q_tiled) || !aligned(s_tiled)) return MOE_MLP_ERR_MISALIGNED;
+  const int64_t pieces = mats * rows * (cols / 32) + mats * rows * (cols / 256);
+  if (pieces == 0) return MOE_MLP_OK;
+  if (cdiv(pieces, 256) > int64_t(0x7FFFFFFF)) return MOE_MLP_ERR_BAD_SHAPE;
+  k_nvfp4_tile_pack<<<static_cast<unsigned>(cdiv(pieces, 256)), 256, 0, static_cast<hipStream_t>(stream)>>>(
+      q, s, mats, rows, cols, q_tiled, s_tiled);
   return launch_status();
 }
 

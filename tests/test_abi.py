@@ -178,6 +178,24 @@ def test_dequant_validation():
     assert L.moe_nvfp4_dequant(FAKE, FAKE, 1.0, 0, 64, FAKE, None, None) == capi.OK
 
 
+def test_tile_pack_validation():
+    L = R.lib()
+    assert L.moe_nvfp4_tile_pack(None, FAKE, 2, 64, 512, FAKE, FAKE, None) == capi.ERR_NULL_ARG
+    assert L.moe_nvfp4_tile_pack(FAKE, FAKE, 2, 64, 512, FAKE, None, None) == capi.ERR_NULL_ARG
+    assert L.moe_nvfp4_tile_pack(FAKE, FAKE, 2, 48, 512, FAKE, FAKE, None) == capi.ERR_BAD_SHAPE
+    assert L.moe_nvfp4_tile_pack(FAKE, FAKE, 2, 64, 384, FAKE, FAKE, None) == capi.ERR_BAD_SHAPE
+    assert L.moe_nvfp4_tile_pack(FAKE, FAKE, -1, 64, 512, FAKE, FAKE, None) == capi.ERR_BAD_SHAPE
+    assert L.moe_nvfp4_tile_pack(FAKE, FAKE, 2, 0, 512, FAKE, FAKE, None) == capi.ERR_BAD_SHAPE
+    assert L.moe_nvfp4_tile_pack(FAKE + 8, FAKE, 2, 64, 512, FAKE, FAKE, None) == capi.ERR_MISALIGNED
+    assert L.moe_nvfp4_tile_pack(FAKE, FAKE, 2, 64, 512, FAKE, FAKE + 4, None) == capi.ERR_MISALIGNED
+    assert L.moe_nvfp4_tile_pack(FAKE, FAKE, 0, 64, 512, FAKE, FAKE, None) == capi.OK
+
+
+def test_misaligned_tiled_weights_rejected():
+    for field in ["w13_q_tiled", "w13_s_tiled", "w2_q_tiled", "w2_s_tiled"]:
+        assert call("moe_mlp_prefill", cfg(), full_weights(**{field: FAKE + 8})) == capi.ERR_MISALIGNED
+
+
 def test_profiled_entry_validation():
     L = R.lib()
     c = cfg()

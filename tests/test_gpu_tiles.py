@@ -1,0 +1,92 @@
+"""GPU: the tile layout of the routed NVFP4 weights (moe_nvfp4_tile_pack) and
+the grouped GEMM reading it.
+
+The layout is restated here in numpy from its definition in include/moe_mlp.h
+and compared byte for byte with the library's pack.  A layer given the tiled
+copies must produce bitwise the output (and ids, weights) it produces from
+the row-major arrays alone: the tile kernel loads the same bytes into the same
+LDS positions, so nothing after the loads differs.
+"""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from gpu_util import DEV, DeviceRouted, bf16_host_bits, device_workload, say
+from inputs import RoutedInputs
+from routed_expert_mlp_amd import capi
+
+pytestmark = pytest.mark.gpu
+
+
+def _z(i):
+    return ((i >> 1) & 3) ^ ((i >> 3) & 1)
+
+
+def tiled_codes(q):
+    """q [mats, rows, cols/2] -> the tile layout: per (matrix, 16-row group,
+    128-column unit) 64 pieces of 16 bytes, piece L = row 16r + L/4, bytes
+    64u + 16((L % 4) ^ z(L / 4)) .. +15."""
+    mats, rows, half = q.shape
+    src = q.reshape(mats, rows // 16, 16, half // 64, 64)
+    out = np.empty((mats, rows // 16, half // 64, 64, 16), np.uint8)
+    for L in range(64):
+        piece = (L % 4) ^ _z(L // 4)
+        out[:, :, :, L, :] = src[:, :, L // 4, :, 16 * piece:16 * piece + 16]
+    return out.reshape(q.shape)
+
+
+def tiled_scales(s):
+    """s [mats, rows, cols/16] -> per (matrix, 32-row group, 256-column unit)
+    32 pieces of 16 bytes, piece l = scale bytes 16v .. 16v+15 of row 32r + l."""
+    mats, rows, n = s.shape
+    return s.reshape(mats, rows // 32, 32, n // 16, 16).transpose(0, 1, 3, 2, 4).reshape(s.shape).copy()
+
+
+@pytest.mark.parametrize("mats,rows,cols", [(3, 96, 768), (1, 32, 256), (2, 64, 1024)])
+def test_tile_pack_matches_layout(mats, rows, cols):
+    say(f"[case] tile pack mats={mats} rows={rows} cols={cols}")
+    g = np.random.default_rng(7)
+    q = g.integers(0, 256, (mats, rows, cols // 2), dtype=np.uint8)
+    s = g.integers(0, 256, (mats, rows, cols // 16), dtype=np.uint8)
+    qt, st = capi.moe_nvfp4_tile_pack(torch.from_numpy(q).to(DEV), torch.from_numpy(s).to(DEV))
+    torch.cuda.synchronize()
+    assert np.array_equal(qt.cpu().numpy(), tiled_codes(q))
+    assert np.array_equal(st.cpu().numpy(), tiled_scales(s))
+
+
+def _run_both(d: DeviceRouted, what: str):
+    out0, ids0, w0 = d.run(True)
+    plain = d.weights
+    d.weights = capi.with_tiled_weights(plain)
+    try:
+        out1, ids1, w1 = d.run(True)
+    finally:
+        d.weights = plain
+    torch.cuda.synchronize()
+    assert torch.equal(ids0, ids1) and torch.equal(w0, w1), what
+    a, b = bf16_host_bits(out0), bf16_host_bits(out1)
+    n_diff = int((a != b).sum())
+    say(f"[parity] tiled vs row-major weights, {what}: {n_diff} of {a.size} outputs differ")
+    assert n_diff == 0
+
+
+# the tile-kernel shapes of the routed grouped-GEMM tests (both projections,
+# one of them, neither) and the full-size prefill workload
+TILE_CASES = [dict(T=600, H=512, I=512, E=16, K=4, Is=256),
+              dict(T=300, H=768, I=512, E=8, K=2, Is=96),
+              dict(T=200, H=1024, I=160, E=8, K=2, Is=96),
+              dict(T=150, H=256, I=512, E=8, K=2, Is=64),
+              dict(T=100, H=256, I=256, E=4, K=2, Is=64)]
+
+
+@pytest.mark.parametrize("overrides", TILE_CASES, ids=[f"T{o['T']}_H{o['H']}_I{o['I']}" for o in TILE_CASES])
+def test_tiled_weights_bitwise(overrides):
+    w = synth.workload("ragged_prefill", **overrides)
+    say(f"[case] tiled weights T={w.T} H={w.H} I={w.I} E={w.E} K={w.K}")
+    _run_both(DeviceRouted(RoutedInputs(w)), str(overrides))
+
+
+def test_tiled_weights_bitwise_full_size():
+    say("[case] tiled weights prefill_t4096")
+    _run_both(device_workload("prefill_t4096"), "prefill_t4096")
