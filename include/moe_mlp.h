@@ -234,8 +234,9 @@ int moe_nvfp4_dequant(const uint8_t* q, const uint8_t* s, float global, int64_t 
  *     row 16r + L/4, with z(i) = ((i >> 1) & 3) ^ ((i >> 3) & 1) (the XOR
  *     swizzle of the kernel's LDS layout).
  *   s_tiled: for matrix m, 32-row group r and 256-column unit v, a 512-byte
- *     block at ((m * rows/32 + r) * cols/256 + v) * 512 whose 16-byte piece
- *     l (0..31) is scale bytes 16v .. 16v+15 of row 32r + l.
+ *     block at ((m * rows/32 + r) * cols/256 + v) * 512, stage-major: bytes
+ *     128 t + 4 l .. +3 of the block are scale bytes 16v + 4t .. +3 of row
+ *     32r + l (t = 0..3, the four 64-column stages of the unit; l = 0..31).
  * rows a multiple of 32, cols a multiple of 256 (BAD_SHAPE otherwise);
  * mats >= 0.  Stream-ordered; no allocation.
  */

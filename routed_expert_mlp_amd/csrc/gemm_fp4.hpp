@@ -36,8 +36,13 @@
 //     bytes of each of 64 rows (64 lines).  The tile layout
 //     (k_nvfp4_tile_pack) stores exactly the bytes of one instruction
 //     contiguously, in the order its lanes deliver them to LDS (the LDS
-//     swizzle included): 1 KB of codes, two 512-byte runs of scales.  LDS
-//     contents, and so everything after the loads, are the same for both.
+//     swizzle included): 1 KB of codes, two 512-byte runs of scales.  The
+//     scale runs are stage-major (the 32 rows' words of one stage side by
+//     side), so that a stage's scale read touches 32 consecutive words: in
+//     the row-major layout's LDS image the rows are 16 bytes apart and rows
+//     16 apart share a bank (measured: those reads were every LDS bank
+//     conflict of the kernel).  Codes in LDS, and all arithmetic, are the
+//     same for both layouts.
 //
 // Rows past the tile's valid count load row 0 again (outputs dropped); weight
 // rows past the matrix edge load row 0 again (outputs not stored).  Requires
@@ -138,13 +143,18 @@ __device__ __forceinline__ void f4_mainloop(const F4Lds& L, const F4Src& src, in
   // ---- consumer offsets (uint4 units within a ring entry)
   const int prow = (MODE == GEMM_GATEUP ? 32 * wv : 64 * wv) + ln;   // weight row of n-tile 0
   const int sc = f4_swz_c(prow), sa = f4_swz_a(ln);
+  // scale word of (row, stage) in a scale slot: row-major image: row * 16 +
+  // 4 stage; tile layout (stage-major per 32-row group): (row / 32) * 512 +
+  // 128 stage + 4 (row % 32)
+  constexpr int S_STAGE = TILED ? 128 : 4;
   int aidx[4];
 #pragma unroll
   for (int s = 0; s < 4; ++s) aidx[s] = ln * 8 + ((4 * g + s) ^ sa);
   int cidx[2];
 #pragma unroll
   for (int t = 0; t < 2; ++t) cidx[t] = prow * 4 + ((2 * t + g) ^ sc);
-  const uint32_t sbase = lds_addr(L.s) + static_cast<uint32_t>(prow * 16);
+  const uint32_t sbase =
+      lds_addr(L.s) + static_cast<uint32_t>(TILED ? (prow >> 5) * 512 + 4 * (prow & 31) : prow * 16);
 
   // ---- one stage: wait for its data (VM = DMA instructions allowed to stay in
   // flight), barrier, then 4 k-steps of 8 MFMAs with the next k-step's
@@ -160,7 +170,7 @@ __device__ __forceinline__ void f4_mainloop(const F4Lds& L, const F4Src& src, in
     const uint4* As = L.a[SL];
     const uint4* Cs = L.c[SL >> 1];
     uint32_t sw[2];
-    f4_read_scales<NT_ROWS * 16>(sbase + ((k >> 2) & 1) * S_BYTES + 4 * SL, sw);
+    f4_read_scales<NT_ROWS * 16>(sbase + ((k >> 2) & 1) * S_BYTES + S_STAGE * SL, sw);
     uint4 cw[2];
     cw[0] = Cs[cidx[SL & 1]];
     cw[1] = Cs[cidx[SL & 1] + NT_ROWS * 4];
@@ -296,13 +306,16 @@ __global__ __launch_bounds__(F4_THREADS, 1) void k_gemm_nvfp4(GemmArgs a) {
                                               16 * (4 * (R & 15) + (q ^ f4_swz_c(static_cast<int>(R & 15)))))
                       : static_cast<uint32_t>(R * (kdim >> 1) + 16 * q);
   }
-  // scale DMA: workgroup row 64 wv + lane, 16 bytes (four stages) per group;
-  // tile layout: piece R % 32 of its 32-row group's block
+  // scale DMA, row-major: workgroup row 64 wv + lane, 16 bytes (four stages)
+  // per group.  Tile layout: lanes 32 G .. 32 G + 31 take the 512-byte block
+  // of the 32-row group that starts at workgroup row 64 wv + 32 G (a block is
+  // stage-major, so lane l's 16 bytes are stage l / 8, rows 4 (l % 8) .. +3).
   src.s = (TILED ? a.bs_t : a.bs) + e * a.stride_s;
-  {
-    const int64_t R = wrow(64 * wv + lane);
-    src.so = TILED ? static_cast<uint32_t>((R >> 5) * (kdim >> 8) * 512 + 16 * (R & 31))
-                   : static_cast<uint32_t>(R * (kdim >> 4));
+  if (TILED) {
+    const int64_t R0 = wrow(64 * wv + 32 * (lane >> 5));
+    src.so = static_cast<uint32_t>((R0 >> 5) * (kdim >> 8) * 512 + 16 * (lane & 31));
+  } else {
+    src.so = static_cast<uint32_t>(wrow(64 * wv + lane) * (kdim >> 4));
   }
 
   __shared__ uint4 la0[1024], la1[1024], la2[1024], la3[1024];   // activation ring (16 KB each)
@@ -374,12 +387,17 @@ __global__ __launch_bounds__(256) void k_nvfp4_tile_pack(const uint8_t* __restri
     reinterpret_cast<uint4*>(qt)[idx] =
         *reinterpret_cast<const uint4*>(q + row * (cols >> 1) + 64 * u + 16 * piece);
   } else if (idx < nq + ns) {
+    // piece P of a scale block: stage P / 8, rows 4 (P % 8) .. +3 of the group
     const int64_t j = idx - nq;
-    const int l = static_cast<int>(j & 31);
+    const int P = static_cast<int>(j & 31);
     const int64_t blk = j >> 5, units = cols >> 8, groups = rows >> 5;
     const int64_t v = blk % units, r = (blk / units) % groups, m = blk / units / groups;
-    const int64_t row = m * rows + 32 * r + l;
-    reinterpret_cast<uint4*>(st)[j] = *reinterpret_cast<const uint4*>(s + row * (cols >> 4) + 16 * v);
+    const int64_t row = m * rows + 32 * r + 4 * (P & 7);
+    const int64_t col = 16 * v + 4 * (P >> 3);
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i] = *reinterpret_cast<const uint32_t*>(s + (row + i) * (cols >> 4) + col);
+    reinterpret_cast<uint4*>(st)[j] = make_uint4(w[0], w[1], w[2], w[3]);
   }
 }
 

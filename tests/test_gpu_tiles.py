@@ -38,9 +38,11 @@ def tiled_codes(q):
 
 def tiled_scales(s):
     """s [mats, rows, cols/16] -> per (matrix, 32-row group, 256-column unit)
-    32 pieces of 16 bytes, piece l = scale bytes 16v .. 16v+15 of row 32r + l."""
+    a 512-byte block, stage-major: bytes 128 t + 4 l .. +3 = scale bytes
+    16v + 4t .. +3 of row 32r + l."""
     mats, rows, n = s.shape
-    return s.reshape(mats, rows // 32, 32, n // 16, 16).transpose(0, 1, 3, 2, 4).reshape(s.shape).copy()
+    g = s.reshape(mats, rows // 32, 32, n // 16, 4, 4)          # m, r, l, v, t, byte
+    return g.transpose(0, 1, 3, 4, 2, 5).reshape(s.shape).copy()   # m, r, v, t, l, byte
 
 
 @pytest.mark.parametrize("mats,rows,cols", [(3, 96, 768), (1, 32, 256), (2, 64, 1024)])
