@@ -27,9 +27,13 @@
 //     stages (32 KB each), scales 2 groups of four stages (8 KB each): 144 KB.
 //     The DMA schedule is static (a prologue, a first, middle and last block
 //     of four stages), so every wait is a compile-time count; activation and
-//     code slots are separate LDS arrays whose reads the compiler schedules
-//     (the next k-step's activation fragments are read during the current
-//     k-step's MFMAs); scale words are read by asm.
+//     code and scale slots are separate LDS arrays whose reads the compiler
+//     schedules (the next k-step's activation fragments are read during the
+//     current k-step's MFMAs).  The scale slot alternates per block of four
+//     stages, so the middle blocks run in pairs and the parity of the block
+//     count is a template parameter: every slot is a compile-time array (an
+//     asm read from a run-time slot had to wait on itself at every stage;
+//     measured 3% slower).
 //
 //   * Weight layout.  In the row-major layout a code instruction reads 64
 //     bytes of each of 16 rows (16 half lines) and a scale instruction 16
@@ -67,27 +71,13 @@ __device__ __forceinline__ int f4_swz_a(int r) { return (r & 7) ^ ((r >> 3) & 1)
 // 16-byte position of code piece q (0..3) of weight row p: q ^ f4_swz_c(p).
 __device__ __forceinline__ int f4_swz_c(int p) { return ((p >> 1) & 3) ^ ((p >> 3) & 1); }
 
-// This lane's two scale words of one stage (n-tile stride NT_S bytes): one asm
-// statement that waits for them (the scale ring alternates slots at run time,
-// so a compiler-visible read could not be told apart from the DMA in flight).
-template <int NT_S>
-__device__ __forceinline__ void f4_read_scales(uint32_t saddr, uint32_t (&sc)[2]) {
-  uint32_t s0, s1;
-  asm volatile("ds_read_b32 %0, %2\n\tds_read_b32 %1, %2 offset:%3\n\ts_waitcnt lgkmcnt(0)"
-               : "=&v"(s0), "=&v"(s1)
-               : "v"(saddr), "i"(NT_S)
-               : "memory");
-  sc[0] = s0;
-  sc[1] = s1;
-}
-
-// LDS of one workgroup: the activation ring as four arrays and the code ring
-// as two, so that the compiler's wait insertion can tell a read of one slot
-// from the DMA into another; the scale ring (read by asm only) is one array.
+// LDS of one workgroup: every ring slot is an array of its own (activations
+// four, codes two, scales two), so that the compiler's wait insertion can tell
+// a read of one slot from the DMA into another.
 struct F4Lds {
   uint4* a[4];
   uint4* c[2];
-  uint8_t* s;
+  uint8_t* s[2];
 };
 
 // DMA sources: wave-uniform bases and this lane's 32-bit byte offsets
@@ -102,10 +92,9 @@ struct F4Src {
   uint32_t so;
 };
 
-template <int MODE, int MTV, bool TILED>
+template <int MODE, int MTV, bool TILED, bool ODD>
 __device__ __forceinline__ void f4_mainloop(const F4Lds& L, const F4Src& src, int wv, int lane, int kdim,
                                             f32x16 (&acc)[4][2]) {
-  constexpr int S_BYTES = F4_WROWS * 16;       // one scale group (four stages)
   // weight-row stride between this lane's two n-tiles
   constexpr int NT_ROWS = MODE == GEMM_GATEUP ? 256 : 32;
   const int g = lane >> 5, ln = lane & 31;
@@ -134,9 +123,10 @@ __device__ __forceinline__ void f4_mainloop(const F4Lds& L, const F4Src& src, in
                                        (void __attribute__((address_space(3)))*)(L.c[SL] + wv * 256 + i * 64),
                                        16, 0, 0);
   };
-  auto issue_s = [&](int v) {
+  auto issue_s = [&](int v, auto slot_c) {
+    constexpr int SSL = decltype(slot_c)::value;
     __builtin_amdgcn_global_load_lds(static_cast<const void*>(src.s + (src.so + S_STEP * v)),
-                                     (void __attribute__((address_space(3)))*)(L.s + (v & 1) * S_BYTES + wv * 1024),
+                                     (void __attribute__((address_space(3)))*)(L.s[SSL] + wv * 1024),
                                      16, 0, 0);
   };
 
@@ -153,15 +143,15 @@ __device__ __forceinline__ void f4_mainloop(const F4Lds& L, const F4Src& src, in
   int cidx[2];
 #pragma unroll
   for (int t = 0; t < 2; ++t) cidx[t] = prow * 4 + ((2 * t + g) ^ sc);
-  const uint32_t sbase =
-      lds_addr(L.s) + static_cast<uint32_t>(TILED ? (prow >> 5) * 512 + 4 * (prow & 31) : prow * 16);
+  const int soff = (TILED ? (prow >> 5) * 512 + 4 * (prow & 31) : prow * 16) >> 2;   // in words
 
   // ---- one stage: wait for its data (VM = DMA instructions allowed to stay in
   // flight), barrier, then 4 k-steps of 8 MFMAs with the next k-step's
   // activation fragments read during the current one; the next loads are
   // issued after the first k-step
-  auto stage = [&](int k, auto slot_c, auto vm_c, auto issue) {
+  auto stage = [&](int k, auto slot_c, auto ss_c, auto vm_c, auto issue) {
     constexpr int SL = decltype(slot_c)::value;
+    constexpr int SS = decltype(ss_c)::value;
     constexpr int VM = decltype(vm_c)::value;
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(VM));
     asm volatile("" ::: "memory");
@@ -170,7 +160,11 @@ __device__ __forceinline__ void f4_mainloop(const F4Lds& L, const F4Src& src, in
     const uint4* As = L.a[SL];
     const uint4* Cs = L.c[SL >> 1];
     uint32_t sw[2];
-    f4_read_scales<NT_ROWS * 16>(sbase + ((k >> 2) & 1) * S_BYTES + S_STAGE * SL, sw);
+    {
+      const uint32_t* Ss = reinterpret_cast<const uint32_t*>(L.s[SS]);
+      sw[0] = Ss[soff + (S_STAGE >> 2) * SL];
+      sw[1] = Ss[soff + (S_STAGE >> 2) * SL + NT_ROWS * 4];
+    }
     uint4 cw[2];
     cw[0] = Cs[cidx[SL & 1]];
     cw[1] = Cs[cidx[SL & 1] + NT_ROWS * 4];
@@ -218,33 +212,53 @@ __device__ __forceinline__ void f4_mainloop(const F4Lds& L, const F4Src& src, in
   // The first block skips S and C at k = 0; the last block issues only
   // C(k/2+1) A(k+3) at its first stage.  Counting the DMA instructions issued
   // after the last one each stage needs gives the waits below.
-  issue_s(0);
+  issue_s(0, I0{});
   issue_c(0, I0{});
   issue_a(0, I0{});
   issue_c(1, I1{});
   issue_a(1, I1{});
   issue_a(2, I2{});
-  issue_s(1);
-  // first block
-  stage(0, I0{}, std::integral_constant<int, 9>{}, [&] { issue_a(3, I3{}); });
-  stage(1, I1{}, std::integral_constant<int, 5>{}, [&] { issue_a(4, I0{}); });
-  stage(2, I2{}, std::integral_constant<int, 5>{}, [&] { issue_c(2, I0{}); issue_a(5, I1{}); });
-  stage(3, I3{}, std::integral_constant<int, 8>{}, [&] { issue_a(6, I2{}); });
-  // middle blocks
-  for (int j = 1; j < nblk4 - 1; ++j) {
+  issue_s(1, I1{});
+  using V0 = std::integral_constant<int, 0>;
+  using V2 = std::integral_constant<int, 2>;
+  using V4 = std::integral_constant<int, 4>;
+  using V5 = std::integral_constant<int, 5>;
+  using V8 = std::integral_constant<int, 8>;
+  using V9 = std::integral_constant<int, 9>;
+  // first block (scale slot 0)
+  stage(0, I0{}, I0{}, V9{}, [&] { issue_a(3, I3{}); });
+  stage(1, I1{}, I0{}, V5{}, [&] { issue_a(4, I0{}); });
+  stage(2, I2{}, I0{}, V5{}, [&] { issue_c(2, I0{}); issue_a(5, I1{}); });
+  stage(3, I3{}, I0{}, V8{}, [&] { issue_a(6, I2{}); });
+  // middle block j reads scale slot j % 2 and loads group j + 1 into the other
+  auto middle = [&](int j, auto ss_c) {
+    using NS = std::integral_constant<int, decltype(ss_c)::value ^ 1>;
     const int k = 4 * j;
-    stage(k, I0{}, std::integral_constant<int, 4>{}, [&] { issue_s(j + 1); issue_c(2 * j + 1, I1{}); issue_a(k + 3, I3{}); });
-    stage(k + 1, I1{}, std::integral_constant<int, 9>{}, [&] { issue_a(k + 4, I0{}); });
-    stage(k + 2, I2{}, std::integral_constant<int, 4>{}, [&] { issue_c(2 * j + 2, I0{}); issue_a(k + 5, I1{}); });
-    stage(k + 3, I3{}, std::integral_constant<int, 8>{}, [&] { issue_a(k + 6, I2{}); });
-  }
-  // last block
-  {
+    stage(k, I0{}, ss_c, V4{}, [&] { issue_s(j + 1, NS{}); issue_c(2 * j + 1, I1{}); issue_a(k + 3, I3{}); });
+    stage(k + 1, I1{}, ss_c, V9{}, [&] { issue_a(k + 4, I0{}); });
+    stage(k + 2, I2{}, ss_c, V4{}, [&] { issue_c(2 * j + 2, I0{}); issue_a(k + 5, I1{}); });
+    stage(k + 3, I3{}, ss_c, V8{}, [&] { issue_a(k + 6, I2{}); });
+  };
+  auto last = [&](auto ss_c) {
     const int j = nblk4 - 1, k = 4 * j;
-    stage(k, I0{}, std::integral_constant<int, 4>{}, [&] { issue_c(2 * j + 1, I1{}); issue_a(k + 3, I3{}); });
-    stage(k + 1, I1{}, std::integral_constant<int, 8>{}, [] {});
-    stage(k + 2, I2{}, std::integral_constant<int, 2>{}, [] {});
-    stage(k + 3, I3{}, std::integral_constant<int, 0>{}, [] {});
+    stage(k, I0{}, ss_c, V4{}, [&] { issue_c(2 * j + 1, I1{}); issue_a(k + 3, I3{}); });
+    stage(k + 1, I1{}, ss_c, V8{}, [] {});
+    stage(k + 2, I2{}, ss_c, V2{}, [] {});
+    stage(k + 3, I3{}, ss_c, V0{}, [] {});
+  };
+  // middle blocks in pairs (slots 1, 0), so every slot is a compile-time
+  // array; ODD = an odd number of blocks of four stages (one unpaired middle
+  // block, and the last block then reads slot 0)
+  const int jend = nblk4 - 1 - (ODD ? 1 : 0);
+  for (int j = 1; j < jend; j += 2) {
+    middle(j, I1{});
+    middle(j + 1, I0{});
+  }
+  if constexpr (ODD) {
+    middle(nblk4 - 2, I1{});
+    last(I0{});
+  } else {
+    last(I1{});
   }
 }
 
@@ -320,8 +334,8 @@ __global__ __launch_bounds__(F4_THREADS, 1) void k_gemm_nvfp4(GemmArgs a) {
 
   __shared__ uint4 la0[1024], la1[1024], la2[1024], la3[1024];   // activation ring (16 KB each)
   __shared__ uint4 lc0[2048], lc1[2048];                          // code ring (32 KB each)
-  __shared__ __attribute__((aligned(16))) uint8_t ls[2 * F4_WROWS * 16];   // scale ring
-  const F4Lds L{{la0, la1, la2, la3}, {lc0, lc1}, ls};
+  __shared__ __attribute__((aligned(16))) uint8_t ls0[F4_WROWS * 16], ls1[F4_WROWS * 16];   // scale ring
+  const F4Lds L{{la0, la1, la2, la3}, {lc0, lc1}, {ls0, ls1}};
   f32x16 acc[4][2];
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt)
@@ -329,11 +343,20 @@ __global__ __launch_bounds__(F4_THREADS, 1) void k_gemm_nvfp4(GemmArgs a) {
     for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
       for (int j = 0; j < 16; ++j) acc[mt][nt][j] = 0.0f;
-  switch ((valid + 31) >> 5) {
-    case 1: f4_mainloop<MODE, 1, TILED>(L, src, wv, lane, kdim, acc); break;
-    case 2: f4_mainloop<MODE, 2, TILED>(L, src, wv, lane, kdim, acc); break;
-    case 3: f4_mainloop<MODE, 3, TILED>(L, src, wv, lane, kdim, acc); break;
-    default: f4_mainloop<MODE, 4, TILED>(L, src, wv, lane, kdim, acc); break;
+  if ((kdim >> 8) & 1) {
+    switch ((valid + 31) >> 5) {
+      case 1: f4_mainloop<MODE, 1, TILED, true>(L, src, wv, lane, kdim, acc); break;
+      case 2: f4_mainloop<MODE, 2, TILED, true>(L, src, wv, lane, kdim, acc); break;
+      case 3: f4_mainloop<MODE, 3, TILED, true>(L, src, wv, lane, kdim, acc); break;
+      default: f4_mainloop<MODE, 4, TILED, true>(L, src, wv, lane, kdim, acc); break;
+    }
+  } else {
+    switch ((valid + 31) >> 5) {
+      case 1: f4_mainloop<MODE, 1, TILED, false>(L, src, wv, lane, kdim, acc); break;
+      case 2: f4_mainloop<MODE, 2, TILED, false>(L, src, wv, lane, kdim, acc); break;
+      case 3: f4_mainloop<MODE, 3, TILED, false>(L, src, wv, lane, kdim, acc); break;
+      default: f4_mainloop<MODE, 4, TILED, false>(L, src, wv, lane, kdim, acc); break;
+    }
   }
 
   const int mt_valid = (valid + 31) >> 5;
