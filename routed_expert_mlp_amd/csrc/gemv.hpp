@@ -222,6 +222,9 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
 }
 
 // out[t][c] = bf16(ys[t][c] + sum_k w[t,k] * y[t*K+k][c]), k in order (fp32).
+// KMAX >= K: the K loads of a thread are all issued before the first sum (a
+// loop over a run-time K waited on each load in turn; measured slower).
+template <int KMAX>
 __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ y, const float* __restrict__ ys,
                                                  const float* __restrict__ wts, int T, int K, int H,
                                                  uint16_t* __restrict__ out) {
@@ -230,14 +233,24 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ y, co
   if (q >= nq) return;
   const int64_t t = q / (H >> 2);
   const int c4 = static_cast<int>(q - t * (H >> 2));
+  float w[KMAX];
+  float4 v[KMAX];
+#pragma unroll
+  for (int k = 0; k < KMAX; ++k) {
+    if (k < K) {
+      w[k] = wts[t * K + k];
+      v[k] = reinterpret_cast<const float4*>(y + (t * K + k) * H)[c4];
+    }
+  }
   float4 acc = ys ? reinterpret_cast<const float4*>(ys)[q] : make_float4(0, 0, 0, 0);
-  for (int k = 0; k < K; ++k) {
-    const float w = wts[t * K + k];
-    const float4 v = reinterpret_cast<const float4*>(y + (t * K + k) * H)[c4];
-    acc.x = fmaf(w, v.x, acc.x);
-    acc.y = fmaf(w, v.y, acc.y);
-    acc.z = fmaf(w, v.z, acc.z);
-    acc.w = fmaf(w, v.w, acc.w);
+#pragma unroll
+  for (int k = 0; k < KMAX; ++k) {
+    if (k < K) {
+      acc.x = fmaf(w[k], v[k].x, acc.x);
+      acc.y = fmaf(w[k], v[k].y, acc.y);
+      acc.z = fmaf(w[k], v[k].z, acc.z);
+      acc.w = fmaf(w[k], v[k].w, acc.w);
+    }
   }
   uint2 o;
   o.x = pack_bf16x2(acc.x, acc.y);

@@ -631,9 +631,14 @@ int run_layer(const moe_mlp_config* c, const moe_mlp_weights* w, const uint16_t*
   }
   const int64_t nq = T * (H / 4);
   const Ev ce = ev(prefill ? 7 : 6);
-  launch(k_combine, dim3(static_cast<unsigned>(cdiv(nq, 256))), dim3(256), s, ce.a, ce.b,
-         static_cast<const float*>(y), static_cast<const float*>(ys), static_cast<const float*>(wts), Ti, K, H,
-         out);
+  const dim3 cgrid(static_cast<unsigned>(cdiv(nq, 256)));
+  const float *yc = y, *ysc = ys, *wc = wts;
+  if (K <= 4)
+    launch(k_combine<4>, cgrid, dim3(256), s, ce.a, ce.b, yc, ysc, wc, Ti, K, H, out);
+  else if (K <= 8)
+    launch(k_combine<8>, cgrid, dim3(256), s, ce.a, ce.b, yc, ysc, wc, Ti, K, H, out);
+  else
+    launch(k_combine<MOE_MLP_MAX_TOP_K>, cgrid, dim3(256), s, ce.a, ce.b, yc, ysc, wc, Ti, K, H, out);
   return launch_status();
 }
 
