@@ -440,13 +440,21 @@ def main():
 
     # ---------------- decode T=16 / T=64 (same weights, more tokens) ----------------
     if not args.no_extra_decode:
+        wts_tiled = None
         for T in (2, 4, 16, 64):
             xs_t = [x_dev(w, range(100 + r * T, 100 + (r + 1) * T), dev) for r in range(R)]
             out_t = [torch.empty((T, w.H), dtype=torch.bfloat16, device=dev) for _ in range(R)]
             ids_t = [torch.empty((T, w.K), dtype=torch.int32, device=dev) for _ in range(R)]
             ws_t = capi.workspace(cfg, T, False, dev)
+            wts_t = wts
+            if T >= 64:
+                # from 64 tokens decode runs the grouped GEMM, which reads the
+                # tile-layout copies of the routed weights (packed once at load)
+                if wts_tiled is None:
+                    wts_tiled = [capi.with_tiled_weights(x) for x in wts]
+                wts_t = wts_tiled
 
-            calls_t = [capi.bind_layer(cfg, wts[r], xs_t[r], out_t[r], ids_t[r], ws=ws_t) for r in range(R)]
+            calls_t = [capi.bind_layer(cfg, wts_t[r], xs_t[r], out_t[r], ids_t[r], ws=ws_t) for r in range(R)]
 
             def step_t(i):
                 calls_t[i % R]()
@@ -459,7 +467,10 @@ def main():
             b = float(np.mean([decode_bytes(w, x, T) for x in u]))
             extra[f"decode_t{T}"] = {"gbs": round(b / s_t / 1e9, 1), "us_per_step": round(s_t * 1e6, 1),
                                      "tokens_per_s": round(T / s_t, 1), "unique_experts": float(np.mean(u))}
-            del calls_t, xs_t, out_t, ids_t, ws_t
+            if T >= 64:
+                extra[f"decode_t{T}"]["weights"] = "routed NVFP4 in the tile layout (grouped-GEMM form)"
+            del calls_t, xs_t, out_t, ids_t, ws_t, wts_t
+        del wts_tiled
 
     # ---------------- prefill T=4096 ----------------
     if not args.no_prefill:
