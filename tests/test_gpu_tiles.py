@@ -57,12 +57,12 @@ def test_tile_pack_matches_layout(mats, rows, cols):
     assert np.array_equal(st.cpu().numpy(), tiled_scales(s))
 
 
-def _run_both(d: DeviceRouted, what: str):
-    out0, ids0, w0 = d.run(True)
+def _run_both(d: DeviceRouted, what: str, prefill=True):
+    out0, ids0, w0 = d.run(prefill)
     plain = d.weights
     d.weights = capi.with_tiled_weights(plain)
     try:
-        out1, ids1, w1 = d.run(True)
+        out1, ids1, w1 = d.run(prefill)
     finally:
         d.weights = plain
     torch.cuda.synchronize()
@@ -92,3 +92,12 @@ def test_tiled_weights_bitwise(overrides):
 def test_tiled_weights_bitwise_full_size():
     say("[case] tiled weights prefill_t4096")
     _run_both(device_workload("prefill_t4096"), "prefill_t4096")
+
+
+@pytest.mark.parametrize("T", [1, 16, 64])
+def test_tiled_weights_decode_bitwise(T):
+    """Decode ignores the tiled copies below 64 tokens (GEMV forms) and reads
+    them from 64 tokens on (grouped-GEMM form): bitwise the same either way."""
+    w = synth.workload("ragged_decode", T=T, H=512, I=512, E=16, K=4, Is=128)
+    say(f"[case] tiled weights, decode T={w.T} H={w.H} I={w.I} E={w.E} K={w.K}")
+    _run_both(DeviceRouted(RoutedInputs(w)), f"decode T={T}", prefill=False)
