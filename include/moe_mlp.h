@@ -200,8 +200,11 @@ int moe_mlp_forward_profiled(const moe_mlp_config* cfg, const moe_mlp_weights* w
 const char* moe_mlp_stage_name(const moe_mlp_config* cfg, int64_t T, int prefill, int stage);
 
 /*
- * Router alone (test entry): logits = x . router_w^T (fp32), sigmoid scores,
- * top-K of score + bias, weights = rsf * score / sum of chosen scores.
+ * Router alone (test entry; Module glm5next_mlp, "The stack this layer runs":
+ * gate.weight -> fp32 logits -> router_topk -> ids[K], weights[K], with the
+ * selection and weight rules of "Traps this module exists to hold"):
+ * logits = x . router_w^T (fp32), sigmoid scores, top-K of score + bias,
+ * weights = rsf * score / sum of chosen scores.
  * Uses cfg->kind == ROUTED fields hidden, num_experts, top_k and
  * routed_scaling_factor.  ids [T, K] int32, w [T, K] fp32 (both required).
  * Workspace: moe_mlp_workspace_size(cfg, T, 1) bytes (prefill sizing).
@@ -211,8 +214,11 @@ int moe_router_topk(const moe_mlp_config* cfg, const float* router_w, const floa
                      void* workspace, size_t ws_bytes, void* stream);
 
 /*
- * NVFP4 dequantisation (test entry), the same device routines the GEMV and
- * grouped GEMM use: out[r][c] = global * e2m1(code[r][c]) * e4m3(scale[r][c/16]).
+ * NVFP4 dequantisation (test entry; Module glm5next_mlp, "The stack this
+ * layer runs": the routed experts' NVFP4 gate/up and down weights; element
+ * and scale formats of the OCP MX v1.0 and OFP8 specifications), the same
+ * device routines the GEMV and grouped GEMM use:
+ * out[r][c] = global * e2m1(code[r][c]) * e4m3(scale[r][c/16]).
  *   q [rows, cols/2], s [rows, cols/16]; cols a positive multiple of 32.
  *   out_f32 [rows, cols] fp32 and/or out_bf16 [rows, cols] bf16 (RNE); at
  *   least one non-NULL.  With global == 1 both outputs are exact.

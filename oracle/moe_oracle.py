@@ -16,16 +16,14 @@ float64 with NumPy, one step per function, in the order the pages give:
   outputs with the shared output; a DENSE layer is one BF16 gate/up, clamped
   SwiGLU, down FFN;
 
-and, same page, section "Traps this module exists to hold":
-  * the SwiGLU clamp is asymmetric: the gate has an upper bound only, the up
-    projection both, at swiglu_limit (never defaulted);
-  * the correction bias only changes which experts are chosen; a chosen
-    expert's weight uses its plain sigmoid score;
-  * routed_scaling_factor multiplies the top-k weights; the shared expert is
-    not scaled by it;
-  * num_experts is the full expert count, and the weights are renormalised
-    over the chosen experts of that full count.
-  Constants, KERNEL_MAX_TOP_K: at most 16 experts per token.
+and the rules of the same page's section "Traps this module exists to hold",
+written here as formulas (L = swiglu_limit, a required config value):
+  * h = silu(min(g, L)) * clip(u, -L, L): g is clipped from above only;
+  * experts are ranked by s + b (s the sigmoid score, b the correction
+    bias), and the weight of a chosen expert is built from s alone;
+  * w_k = rsf * s_k / sum_j s_j over the K chosen of all E experts; rsf
+    enters only through w, and the shared output is added with factor 1.
+  Constants, KERNEL_MAX_TOP_K: K <= 16.
 
 Number formats (not on the pages; public specifications):
   * NVFP4 element = FP4 E2M1 of the OCP Microscaling Formats (MX) v1.0 spec:
@@ -272,14 +270,26 @@ class RoutedWeights:
         self.shared_w2 = shared_w2
 
 
+def expert_rows(job):
+    """One chosen expert on the rows routed to it: job = (expert source, e,
+    x rows, gate/up globals, down global, limit, mode) -> routed_expert's
+    output for those rows."""
+    expert, e, xr, g13, g2, limit, mode = job
+    q13, s13, q2, s2 = expert(e)
+    return routed_expert(xr, q13, s13, g13, q2, s2, g2, limit, mode)
+
+
 def moe_layer(x_bits, wts: RoutedWeights, k: int, rsf: float, limit: float, mode="contract",
-              tokens=None):
+              tokens=None, map_fn=map):
     """Routed MoE MLP for tokens x [T, H] (bf16 bits).
 
     out[t] = shared(x[t]) + sum_k w[t, k] * expert_{ids[t, k]}(x[t]), summed
     over k in order, rounded to bf16 once in contract mode.  `tokens`
     restricts the computation to a subset of rows (the router still runs on
-    those rows only; tokens are independent).
+    those rows only; tokens are independent).  `map_fn(expert_rows, jobs)`
+    evaluates the per-expert jobs (the builtin map by default; any map that
+    returns expert_rows(job) for each job in order, e.g. a process pool's,
+    gives the same result, since the experts are independent).
 
     Returns (out [n, H] fp64, ids [n, K], w [n, K]).
     """
@@ -289,11 +299,12 @@ def moe_layer(x_bits, wts: RoutedWeights, k: int, rsf: float, limit: float, mode
     n, H = x.shape
     ids, w, _, _ = route(x, wts.router_w, wts.router_bias, k, rsf)
     y = np.zeros((n, k, H), dtype=F64)
-    for e in np.unique(ids):
-        rows, slots = np.nonzero(ids == e)
-        q13, s13, q2, s2 = wts.expert(int(e))
-        y[rows, slots] = routed_expert(x[rows], q13, s13, wts.w13_g[e], q2, s2, wts.w2_g[e],
-                                       limit, mode)
+    chosen = [int(e) for e in np.unique(ids)]
+    where = [np.nonzero(ids == e) for e in chosen]
+    jobs = [(wts.expert, e, x[rows], wts.w13_g[e], wts.w2_g[e], limit, mode)
+            for e, (rows, _) in zip(chosen, where)]
+    for (rows, slots), ye in zip(where, map_fn(expert_rows, jobs)):
+        y[rows, slots] = ye
     acc = np.zeros((n, H), dtype=F64)
     if wts.shared_w13 is not None:
         acc = acc + bf16_mlp(x, wts.shared_w13, wts.shared_w2, limit, mode)

@@ -56,6 +56,14 @@ class RoutedInputs:
         return O.RoutedWeights(self.router_w, self.router_bias, self.w13_g, self.w2_g, self.expert,
                                self.shared_w13, self.shared_w2)
 
-    def oracle(self, tokens=None, mode="contract"):
-        return O.moe_layer(self.x, self.oracle_weights(), self.w.K, self.w.rsf, self.w.swiglu_limit,
-                           mode=mode, tokens=tokens)
+    def oracle(self, tokens=None, mode="contract", parallel=False):
+        """The oracle's layer output on these inputs.  parallel=True runs the
+        per-expert work in the oracle_pool worker processes (same result)."""
+        if not parallel:
+            return O.moe_layer(self.x, self.oracle_weights(), self.w.K, self.w.rsf, self.w.swiglu_limit,
+                               mode=mode, tokens=tokens)
+        from oracle_pool import SynthExpert, pool_map
+        wts = O.RoutedWeights(self.router_w, self.router_bias, self.w13_g, self.w2_g, SynthExpert(self.w),
+                              self.shared_w13, self.shared_w2)
+        return O.moe_layer(self.x, wts, self.w.K, self.w.rsf, self.w.swiglu_limit, mode=mode, tokens=tokens,
+                           map_fn=pool_map)
