@@ -30,7 +30,8 @@
  *     travel as uint16_t bit patterns.
  *   - The caller owns every buffer, including the workspace.  The library
  *     never allocates, frees or synchronises, keeps no pointer after return
- *     and holds no global state; calls are reentrant.  Work is enqueued on
+ *     and holds no global state (except the per-device scratch array of
+ *     moe_mlp_decode_noalloc); calls are reentrant.  Work is enqueued on
  *     `stream` (a hipStream_t; NULL = the default stream) and the call
  *     returns without waiting.  Device faults surface at the caller's next
  *     synchronisation.
@@ -75,10 +76,13 @@ extern "C" {
 #define MOE_MLP_ERR_WORKSPACE_TOO_SMALL -6 /* ws_bytes below moe_mlp_workspace_size() */
 #define MOE_MLP_ERR_KIND_MISMATCH      -7  /* weights missing for the config's kind */
 #define MOE_MLP_ERR_HIP                -8  /* a kernel launch failed (hipGetLastError) */
+#define MOE_MLP_ERR_SCRATCH_LIMIT      -9  /* moe_mlp_decode_noalloc: the call needs more than
+                                              MOE_MLP_NOALLOC_SCRATCH_BYTES of scratch */
 
 #define MOE_MLP_MAX_TOP_K      16    /* Module glm5next_mlp, Constants, KERNEL_MAX_TOP_K */
 #define MOE_MLP_MAX_EXPERTS    1024  /* one wavefront holds at most 16 scores per lane */
 #define MOE_MLP_DECODE_MAX_T   256   /* moe_mlp_decode handles up to this many tokens */
+#define MOE_MLP_NOALLOC_SCRATCH_BYTES (32u << 20)   /* scratch of moe_mlp_decode_noalloc, per device */
 
 #define MOE_MLP_KIND_ROUTED 0   /* router + routed NVFP4 experts + optional shared expert */
 #define MOE_MLP_KIND_DENSE  1   /* dense BF16 FFN (layers before first_k_dense_replace) */
@@ -158,6 +162,26 @@ int moe_mlp_workspace_size(const moe_mlp_config* cfg, int64_t T, int prefill, si
 int moe_mlp_decode(const moe_mlp_config* cfg, const moe_mlp_weights* w, const uint16_t* x,
                    int64_t T, uint16_t* out, int32_t* ids_out, float* w_out,
                    void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * moe_mlp_decode for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same kernels and results, with the workspace taken from a device array
+ * of MOE_MLP_NOALLOC_SCRATCH_BYTES that the library's code object holds on
+ * every GPU it runs on, from the first call there until the process ends
+ * (its device address is looked up once per device, with that device
+ * current).  The call itself allocates and frees nothing.  The caller still
+ * passes x, out, ids_out, w_out (as moe_mlp_decode) and enqueues on `stream`
+ * of the current device.  Returns MOE_MLP_ERR_SCRATCH_LIMIT, before anything
+ * is enqueued, when moe_mlp_workspace_size(cfg, T, 0) exceeds the array
+ * (at H=4096, I=Is=1536, E=288, K=8: up to about 140 tokens fit).  Every call
+ * on one GPU uses that GPU's one array, which keeps the last call's contents
+ * (the kernels never read scratch they have not written in the same call):
+ * calls that overlap on one GPU (other streams, other host threads) race and
+ * must be serialised by the caller.
+ */
+int moe_mlp_decode_noalloc(const moe_mlp_config* cfg, const moe_mlp_weights* w, const uint16_t* x,
+                           int64_t T, uint16_t* out, int32_t* ids_out, float* w_out, void* stream);
 
 /*
  * Prefill form ("forward_prefill_gemm": the page's grouped-GEMM prefill),

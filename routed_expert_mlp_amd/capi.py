@@ -28,16 +28,18 @@ ERR_MISALIGNED = -5
 ERR_WORKSPACE_TOO_SMALL = -6
 ERR_KIND_MISMATCH = -7
 ERR_HIP = -8
+ERR_SCRATCH_LIMIT = -9
 
 MAX_TOP_K = 16
 MAX_EXPERTS = 1024
 DECODE_MAX_T = 256
+NOALLOC_SCRATCH_BYTES = 32 << 20
 KIND_ROUTED = 0
 KIND_DENSE = 1
 
 EXPORTED = ("moe_mlp_workspace_size", "moe_mlp_decode", "moe_mlp_prefill", "moe_mlp_forward_profiled",
             "moe_mlp_stage_name", "moe_router_topk", "moe_nvfp4_dequant", "moe_nvfp4_tile_pack",
-            "moe_mlp_status_string")
+            "moe_mlp_status_string", "moe_mlp_decode_noalloc")
 
 
 class MoeMlpError(RuntimeError):
@@ -75,6 +77,8 @@ def lib() -> ctypes.CDLL:
         L.moe_mlp_workspace_size.argtypes = [cfgp, i64, ctypes.c_int, ctypes.POINTER(sz)]
         for f in (L.moe_mlp_decode, L.moe_mlp_prefill):
             f.argtypes = [cfgp, wp, vp, i64, vp, vp, vp, vp, sz, vp]
+        L.moe_mlp_decode_noalloc.argtypes = [cfgp, wp, vp, i64, vp, vp, vp, vp]
+        L.moe_mlp_decode_noalloc.restype = ctypes.c_int
         L.moe_mlp_forward_profiled.argtypes = [cfgp, wp, vp, i64, vp, vp, vp, vp, sz, vp, ctypes.c_int,
                                                ctypes.POINTER(vp), ctypes.c_int]
         L.moe_mlp_forward_profiled.restype = ctypes.c_int
@@ -263,6 +267,23 @@ def bind_layer(cfg: Config, w: Weights, x: torch.Tensor, out: torch.Tensor, ids_
 def moe_mlp_decode(cfg: Config, w: Weights, x: torch.Tensor, out: torch.Tensor, ids_out=None, w_out=None,
                    ws: Optional[torch.Tensor] = None, stream=None) -> None:
     _layer("moe_mlp_decode", cfg, w, x, out, ids_out, w_out, ws, stream, prefill=False)
+
+
+def moe_mlp_decode_noalloc(cfg: Config, w: Weights, x: torch.Tensor, out: torch.Tensor, ids_out=None,
+                           w_out=None, stream=None) -> None:
+    """moe_mlp_decode with the library's own per-device scratch array as the workspace
+    (no allocation by the library or here)."""
+    T = x.shape[0] if x.dim() == 2 else -1
+    _check_tensor(x, "x", (T, cfg.hidden), torch.bfloat16)
+    _check_tensor(out, "out", (T, cfg.hidden), torch.bfloat16)
+    if ids_out is not None:
+        _check_tensor(ids_out, "ids_out", (T, cfg.top_k), torch.int32)
+    if w_out is not None:
+        _check_tensor(w_out, "w_out", (T, cfg.top_k), torch.float32)
+    w.check(cfg)
+    st = lib().moe_mlp_decode_noalloc(ctypes.byref(cfg.c()), ctypes.byref(w.c()), x.data_ptr(), T,
+                                      out.data_ptr(), _ptr(ids_out), _ptr(w_out), _stream(stream))
+    _check(st, "moe_mlp_decode_noalloc")
 
 
 def moe_mlp_prefill(cfg: Config, w: Weights, x: torch.Tensor, out: torch.Tensor, ids_out=None, w_out=None,

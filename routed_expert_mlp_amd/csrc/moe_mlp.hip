@@ -1,14 +1,17 @@
 // C ABI of the routed MoE MLP library (declarations and contract in
 // include/moe_mlp.h).  Host code: argument validation (before anything is
 // enqueued), workspace layout, and the launch sequences of the decode and
-// prefill forms.  The library allocates nothing, never synchronises, and
-// keeps no state between calls.
+// prefill forms.  The library allocates nothing and never synchronises; the
+// only state it keeps between calls is the per-device address of the
+// scratch array of moe_mlp_decode_noalloc.
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 #include <type_traits>
 
 #include "../../include/moe_mlp.h"
@@ -22,6 +25,13 @@
 #include "router.hpp"
 
 static_assert(MOE_MLP_MAX_EXPERTS <= moe::PERM_MAX_E, "k_perm_hist keeps one LDS counter per expert");
+
+// The workspace of moe_mlp_decode_noalloc: a device array in the library's
+// code object, so every GPU the library runs on holds its own copy from the
+// time the code object is loaded there until the process ends.  In host code
+// `scratch` names a host-side stand-in; kernels get the device address that
+// hipGetSymbolAddress returns for the current device (scratch_on_device).
+static __device__ __align__(256) unsigned char scratch[MOE_MLP_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -642,6 +652,28 @@ int run_layer(const moe_mlp_config* c, const moe_mlp_weights* w, const uint16_t*
   return launch_status();
 }
 
+// Device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept.
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+int scratch_on_device(void** ptr) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MOE_MLP_ERR_HIP;
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MOE_MLP_ERR_HIP;
+      g_scratch[dev].store(p, std::memory_order_release);
+    }
+  }
+  *ptr = p;
+  return MOE_MLP_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -664,6 +696,19 @@ int moe_mlp_prefill(const moe_mlp_config* cfg, const moe_mlp_weights* w, const u
                     uint16_t* out, int32_t* ids_out, float* w_out, void* workspace, size_t ws_bytes,
                     void* stream) {
   return run_layer(cfg, w, x, T, out, ids_out, w_out, workspace, ws_bytes, stream, 1);
+}
+
+int moe_mlp_decode_noalloc(const moe_mlp_config* cfg, const moe_mlp_weights* w, const uint16_t* x, int64_t T,
+                           uint16_t* out, int32_t* ids_out, float* w_out, void* stream) {
+  const int st = validate_cfg(cfg, T, 0);
+  if (st) return st;
+  if (T == 0) return run_layer(cfg, w, x, T, out, ids_out, w_out, nullptr, 0, stream, 0);
+  if (make_plan(cfg, T, gemm_form(cfg, T, 0)).total > MOE_MLP_NOALLOC_SCRATCH_BYTES)
+    return MOE_MLP_ERR_SCRATCH_LIMIT;
+  void* ws = nullptr;
+  const int sp = scratch_on_device(&ws);
+  if (sp) return sp;
+  return run_layer(cfg, w, x, T, out, ids_out, w_out, ws, MOE_MLP_NOALLOC_SCRATCH_BYTES, stream, 0);
 }
 
 int moe_mlp_forward_profiled(const moe_mlp_config* cfg, const moe_mlp_weights* w, const uint16_t* x, int64_t T,
@@ -744,6 +789,7 @@ const char* moe_mlp_status_string(int status) {
     case MOE_MLP_ERR_WORKSPACE_TOO_SMALL: return "MOE_MLP_ERR_WORKSPACE_TOO_SMALL";
     case MOE_MLP_ERR_KIND_MISMATCH: return "MOE_MLP_ERR_KIND_MISMATCH";
     case MOE_MLP_ERR_HIP: return "MOE_MLP_ERR_HIP";
+    case MOE_MLP_ERR_SCRATCH_LIMIT: return "MOE_MLP_ERR_SCRATCH_LIMIT";
     default: return "MOE_MLP_ERR_UNKNOWN";
   }
 }

@@ -224,3 +224,22 @@ def test_profiled_entry_validation():
     evs[3] = FAKE
     assert f(ctypes.byref(c), ctypes.byref(w), FAKE, 1, FAKE, None, None, FAKE, need - 1, None, 0, evs, 6) == \
         capi.ERR_WORKSPACE_TOO_SMALL
+
+
+def test_noalloc_decode_validation():
+    """moe_mlp_decode_noalloc validates like moe_mlp_decode, and rejects a call whose workspace
+    exceeds its scratch array, before touching the device."""
+    L = R.lib()
+    flash = cfg(hidden=4096, moe_intermediate=1536, num_experts=288, top_k=8, shared_intermediate=1536)
+    w = full_weights()
+
+    def noalloc(c, T, x=FAKE, out=FAKE + 0x10000):
+        return L.moe_mlp_decode_noalloc(ctypes.byref(c) if c is not None else None, ctypes.byref(w), x, T, out,
+                                        None, None, None)
+    assert noalloc(None, 1) == capi.ERR_NULL_ARG
+    assert noalloc(cfg(top_k=17), 1) == capi.ERR_BAD_TOPK
+    assert noalloc(flash, capi.DECODE_MAX_T + 1) == capi.ERR_BAD_SHAPE
+    assert noalloc(flash, 0, x=None, out=None) == capi.OK
+    assert ws_size(flash, capi.DECODE_MAX_T, 0)[1] > capi.NOALLOC_SCRATCH_BYTES
+    assert noalloc(flash, capi.DECODE_MAX_T) == capi.ERR_SCRATCH_LIMIT
+    assert "SCRATCH_LIMIT" in R.moe_mlp_status_string(capi.ERR_SCRATCH_LIMIT)
