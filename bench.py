@@ -412,17 +412,17 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    gu_ms = st["routed_gateup_shared_down"]
+    gu_ms = st["routed_gateup"]
     # algorithmic bytes of each one-token stage
     exp13 = 2 * w.I * w.H // 2 + 2 * w.I * w.H // 16          # NVFP4 gate/up of one expert
     exp2 = w.H * w.I // 2 + w.H * w.I // 16                    # NVFP4 down of one expert
     stage_bytes = {
         "logits_shared_gateup": 4 * w.E * w.H + 2 * 2 * w.Is * w.H + 2 * w.H + 4 * w.E + 2 * w.Is,
-        "routed_gateup_shared_down": (w.K * exp13 + 2 * w.H * w.Is + 2 * w.H + 4 * w.E * 2 + 2 * w.K * w.I
-                                      + 2 * w.Is + 4 * w.H + 8 * w.K),
-        "routed_down_combine": w.K * exp2 + 2 * w.K * w.I + 4 * w.H + 2 * w.H + 8 * w.K,
+        "routed_gateup": w.K * exp13 + 2 * w.H + 4 * w.E * 2 + 2 * w.K * w.I + 8 * w.K,
+        "shared_routed_down_combine": (w.K * exp2 + 2 * w.H * w.Is + 2 * w.K * w.I + 2 * w.Is + 2 * w.H
+                                       + 8 * w.K),
     }
-    gu_bytes = stage_bytes["routed_gateup_shared_down"]
+    gu_bytes = stage_bytes["routed_gateup"]
     gu_gbs = gu_bytes / (gu_ms * 1e-3) / 1e9
     traffic = read_traffic()
     extra = {"tokens_per_s": round(1.0 / sec, 1), "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
@@ -568,7 +568,7 @@ def main():
                    "tokens": 1, "hidden": w.H, "moe_intermediate": w.I, "experts": w.E, "top_k": w.K,
                    "weights": "nvfp4 (e2m1 + e4m3/16) routed, bf16 shared, fp32 router",
                    "weight_copies_rotated": R},
-        "roofline": {"bound": "hbm", "kernel": "routed_gateup_shared_down (k_dec_gateup: BF16 shared down, router top-k, NVFP4 gate/up + clamped SwiGLU)",
+        "roofline": {"bound": "hbm", "kernel": "routed_gateup (k_dec_gateup: router top-k, NVFP4 gate/up + clamped SwiGLU)",
                      "achieved": round(gu_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gu_gbs / HBM_PEAK_GBS, 4), "avg_launch_us": round(gu_ms * 1e3, 3),
                      "algorithmic_bytes_per_launch": int(gu_bytes),

@@ -4,18 +4,18 @@
 //   1. k_dec_logits_shared: router logits (fp32 rows of gate.weight) and the
 //      BF16 shared expert's gate/up + clamped SwiGLU, both of which only need
 //      x, in one grid;
-//   2. k_dec_gateup: its first blocks stream the shared expert's BF16 down
-//      rows (ys = W2s hs, fp32), which need nothing from the router, while
-//      the other blocks first redo the router top-k from the E logits
-//      (router.hpp topk_wave; "Traps": bias steers selection only, weights
-//      are the renormalised unbiased scores times rsf) to learn which expert
-//      they serve, then stream its NVFP4 gate/up rows + clamped SwiGLU -> h
-//      (bf16).  One wavefront also writes ids and weights.  The shared rows
-//      keep HBM busy while the selection runs, and redoing the selection
-//      (~1 KB of logits per wavefront) is cheaper than a launch of its own;
-//   3. k_dec_down_combine: routed NVFP4 down rows of all K experts and the
-//      combine out = bf16(ys + sum_k w_k y_k) for a block of output rows
-//      (fixed k order).
+//   2. k_dec_gateup: every wavefront first redoes the router top-k from the
+//      E logits (router.hpp topk_wave; "Traps": bias steers selection only,
+//      weights are the renormalised unbiased scores times rsf) to learn which
+//      expert it serves, then streams its NVFP4 gate/up rows + clamped SwiGLU
+//      -> h (bf16).  One wavefront also writes ids and weights.  Redoing the
+//      selection (~1 KB of logits per wavefront) is cheaper than a launch of
+//      its own;
+//   3. k_dec_down_combine: for a block of output rows, the shared expert's
+//      BF16 down rows (issued first: they need nothing from the router, so
+//      they stream while the expert ids arrive), the routed NVFP4 down rows of
+//      all K experts, and the combine out = bf16(ys + sum_k w_k y_k) (fixed k
+//      order) from the block's own partial sums.
 //
 // Each wavefront issues all loads of its rows before using any of them, so a
 // wavefront has its whole share of the weight stream in flight at once.
@@ -176,86 +176,60 @@ __global__ __launch_bounds__(256) void k_dec_logits_shared_t(const uint16_t* __r
   }
 }
 
+// Layer geometry of the decode kernels: compile-time constants (a kernel
+// instance for one layer shape; the selection and index arithmetic fold) or
+// 0 = taken from the kernel arguments (IS: -1).
+template <int H_, int I_, int E_, int K_, int IS_>
+struct DecGeo {
+  static constexpr int H = H_, I = I_, E = E_, K = K_, IS = IS_;
+};
+using DecGeoAny = DecGeo<0, 0, 0, 0, -1>;
+
 // -------------------------------------------------------------------------
-// 2. shared down + top-k + routed gate/up for one token.  1-D grid:
-//  * blocks [0, n_sd): shared down rows r = (b*4 + wave)*RS .. +RS,
-//    ys[r] = sum_j W2s[r, j] hs[j] in fp32 (lane l takes the 16-byte chunks
-//    l, l+64, ... of each row, NSC of them);
-//  * blocks n_sd + a: slot k = a / njb finds its expert (topk_wave,
-//    NJ >= E / 64) and runs gate rows j = ((a % njb)*4 + wave)*RJ .. +RJ and
-//    up rows I + j, njb = ceil(I / (4 RJ)).  Lane l covers the 16-byte chunks
-//    l, l+64, ... (NC of them) of each row, so every load instruction reads
-//    1 KB contiguous.  Wavefront 0 of the first gate/up block runs all K
-//    rounds and writes ids/wts (and ids_out/w_out when not null).
+// 2. top-k + routed gate/up for T tokens (T*K slots, slot = t*K + k).  1-D
+// grid; block a serves slot a / njb, njb = ceil(I / (4 RJ)): its wavefront 0
+// finds the slot's expert (topk_wave, NJ >= E / 64) and hands it to the
+// other wavefronts through LDS (one selection per block: a selection costs
+// a few hundred instructions, too many to repeat in every wavefront), and
+// wavefront w runs gate rows j = ((a % njb)*4 + w)*RJ .. +RJ and up rows
+// I + j.  Lane l covers the 16-byte chunks l, l+64, ... (NC of them; EXACT:
+// every lane has all NC, i.e. H == 2048 NC) of each row, so every load
+// instruction reads 1 KB contiguous.
+// Wavefront 0 of the first block of each token's slot 0 runs all K rounds
+// and writes ids/wts (and ids_out / w_out when not null).
 // -------------------------------------------------------------------------
-template <int RJ, int NC, int NJ, int RS, int NSC>
+template <int RJ, int NC, bool EXACT, int NJ, class G>
 __global__ __launch_bounds__(256) void k_dec_gateup(const uint16_t* __restrict__ x, const uint8_t* __restrict__ q13,
                                                     const uint8_t* __restrict__ s13, const float* __restrict__ g13,
                                                     const float* __restrict__ logits, const float* __restrict__ bias,
-                                                    int K, float rsf, int32_t* __restrict__ ids,
-                                                    float* __restrict__ wts, int32_t* ids_out, float* w_out, int E,
-                                                    int H, int I, float L, uint16_t* __restrict__ h,
-                                                    const uint16_t* __restrict__ sw2, const uint16_t* __restrict__ hs,
-                                                    int Is, float* __restrict__ ys, int n_sd, int T) {
+                                                    int K_, float rsf, int32_t* __restrict__ ids,
+                                                    float* __restrict__ wts, int32_t* ids_out, float* w_out, int E_,
+                                                    int H_, int I_, float L, uint16_t* __restrict__ h) {
+  const int K = G::K ? G::K : K_, E = G::E ? G::E : E_, H = G::H ? G::H : H_, I = G::I ? G::I : I_;
+  __shared__ int s_sel;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  if (static_cast<int>(blockIdx.x) < n_sd) {
-    const int r0 = (blockIdx.x * 4 + wv) * RS;
-    if (r0 >= H) return;
-    const int nsc = Is >> 3;                     // 8-bf16 chunks per row
-    uint4 w[RS][NSC];
-#pragma unroll
-    for (int r = 0; r < RS; ++r) {
-      const uint4* row = reinterpret_cast<const uint4*>(sw2 + static_cast<int64_t>(min(r0 + r, H - 1)) * Is);
-#pragma unroll
-      for (int i = 0; i < NSC; ++i) {
-        const int c = lane + 64 * i;
-        w[r][i] = c < nsc ? row[c] : make_uint4(0, 0, 0, 0);
-      }
-    }
-    for (int t = 0; t < T; ++t) {
-      uint32_t hv[NSC][4];
-#pragma unroll
-      for (int i = 0; i < NSC; ++i) {
-        const int c = lane + 64 * i;
-        const uint4 v = c < nsc ? reinterpret_cast<const uint4*>(hs + static_cast<int64_t>(t) * Is)[c]
-                                : make_uint4(0, 0, 0, 0);
-        hv[i][0] = v.x; hv[i][1] = v.y; hv[i][2] = v.z; hv[i][3] = v.w;
-      }
-      float acc[RS];
-#pragma unroll
-      for (int r = 0; r < RS; ++r) {
-        acc[r] = 0.0f;
-#pragma unroll
-        for (int i = 0; i < NSC; ++i) acc[r] = bf16_chunk_dot(w[r][i], hv[i], acc[r]);
-        acc[r] = wave_sum(acc[r]);
-      }
-      if (lane < RS) {
-        float v = acc[0];
-#pragma unroll
-        for (int r = 1; r < RS; ++r)
-          if (lane == r) v = acc[r];
-        if (r0 + lane < H) ys[static_cast<int64_t>(t) * H + r0 + lane] = v;
-      }
-    }
-    return;
-  }
-  const int a = blockIdx.x - n_sd;
+  const int a = blockIdx.x;
   const int njb = static_cast<int>(cdiv(I, 4 * RJ));
   const int slot = a / njb;                          // t * K + k
   const int t = slot / K, k = slot - t * K;
   const int jb = a - slot * njb;
   const int j0 = (jb * 4 + wv) * RJ;
-  if (j0 >= I) return;
-  const bool writer = jb == 0 && k == 0 && wv == 0;
-  const int64_t o = static_cast<int64_t>(t) * K;
-  const int sel = topk_wave<NJ>(logits + static_cast<int64_t>(t) * E, bias, E, K, rsf, k, writer ? ids + o : nullptr,
-                                wts + o, ids_out ? ids_out + o : nullptr, w_out ? w_out + o : nullptr);
+  const int nch = H >> 5;
   x += static_cast<int64_t>(t) * H;
-  const int e = min(max(sel, 0), E - 1);
+  if (wv == 0) {
+    const bool writer = jb == 0 && k == 0;
+    const int64_t o = static_cast<int64_t>(t) * K;
+    const int sel = topk_wave<NJ>(logits + static_cast<int64_t>(t) * E, bias, E, K, rsf, k,
+                                  writer ? ids + o : nullptr, wts + o, ids_out ? ids_out + o : nullptr,
+                                  w_out ? w_out + o : nullptr);
+    if (lane == 0) s_sel = sel;
+  }
+  __syncthreads();
+  if (j0 >= I) return;
+  const int e = min(max(s_sel, 0), E - 1);
   const int64_t rq = H >> 1, rs = H >> 4;                 // code / scale bytes per row
   const uint8_t* qe = q13 + static_cast<int64_t>(e) * 2 * I * rq;
   const uint8_t* se = s13 + static_cast<int64_t>(e) * 2 * I * rs;
-  const int nch = H >> 5;
   uint4 cg[RJ][NC], cu[RJ][NC];
   uint32_t sg[RJ][NC], su[RJ][NC];
 #pragma unroll
@@ -264,7 +238,7 @@ __global__ __launch_bounds__(256) void k_dec_gateup(const uint16_t* __restrict__
 #pragma unroll
     for (int i = 0; i < NC; ++i) {
       const int c = lane + 64 * i;
-      const bool ok = c < nch;
+      const bool ok = EXACT || c < nch;
       cg[r][i] = ok ? *reinterpret_cast<const uint4*>(qe + j * rq + 16 * c) : make_uint4(0, 0, 0, 0);
       cu[r][i] = ok ? *reinterpret_cast<const uint4*>(qe + (I + j) * rq + 16 * c) : make_uint4(0, 0, 0, 0);
       sg[r][i] = ok ? *reinterpret_cast<const uint16_t*>(se + j * rs + 2 * c) : 0u;
@@ -284,7 +258,7 @@ __global__ __launch_bounds__(256) void k_dec_gateup(const uint16_t* __restrict__
     const uint4* xv = reinterpret_cast<const uint4*>(x + 32 * c);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const uint4 v = c < nch ? xv[q] : make_uint4(0, 0, 0, 0);
+      const uint4 v = (EXACT || c < nch) ? xv[q] : make_uint4(0, 0, 0, 0);
       xp[4 * q] = v.x; xp[4 * q + 1] = v.y; xp[4 * q + 2] = v.z; xp[4 * q + 3] = v.w;
     }
 #pragma unroll
@@ -314,24 +288,76 @@ __global__ __launch_bounds__(256) void k_dec_gateup(const uint16_t* __restrict__
 }
 
 // -------------------------------------------------------------------------
-// 3. routed down + combine for T tokens (T*K slots, slot = t*K + k).  Block
-// b owns output rows r0 = b*R .. +R and has KW wavefronts; wavefront w
-// streams those R rows of expert ids[s]'s NVFP4 down projection against h_s
-// for its slots s = w, w + KW, ... (NP of them; one 16-byte chunk per lane,
-// lanes < I/32, the h_s chunk in registers), every load issued before any
-// arithmetic.  Per-(slot, row) partials meet in LDS and thread (t, r) writes
-// out[t][r0+r] = bf16(ys[t] + sum_k (w_{tK+k} g2) acc_{tK+k}), k in order
+// 3. shared down + routed down + combine for T <= 4 tokens (T*K slots, slot
+// = t*K + k).  Block b owns output rows r0 = b*R .. +R and NW >= R
+// wavefronts.  Every wavefront first asks for the ids and weights of its
+// slots s = w + NW p (p < NP), then (w < R) its shared down row r0 + w
+// (BF16, lane l its 16-byte chunks l, l+64, ..., NSC of them) and the first
+// token's hs chunks, and the h_s chunks of its slots -- none of which depend
+// on the ids, so they stream while the ids arrive -- and finally the R rows
+// of each slot's NVFP4 down projection (lane l its 16-byte chunk l, lanes <
+// I/32).  ys[t][r] = W2s[r] . hs[t] and the per-(slot, row) products
+// (w_s g2) acc_s meet in LDS, and thread (t, r) writes
+// out[t][r0+r] = bf16(ys + sum_k (w_{tK+k} g2) acc_{tK+k}), k in order
 // (ys = 0 without a shared expert).
 // -------------------------------------------------------------------------
-template <int R, int KW, int NP>
-__global__ __launch_bounds__(KW * 64) void k_dec_down_combine(
+constexpr int DEC_MAX_T = 4;
+
+template <int R, int NW, int NP, int NSC, class G>
+__global__ __launch_bounds__(NW * 64) void k_dec_down_combine(
     const uint16_t* __restrict__ h, const uint8_t* __restrict__ q2, const uint8_t* __restrict__ s2,
-    const float* __restrict__ g2, const float* __restrict__ ys, const int32_t* __restrict__ ids,
-    const float* __restrict__ wts, int E, int K, int H, int I, uint16_t* __restrict__ out, int T) {
-  __shared__ float part[KW * NP][R];
+    const float* __restrict__ g2, const uint16_t* __restrict__ sw2, const uint16_t* __restrict__ hs, int Is_,
+    const int32_t* __restrict__ ids, const float* __restrict__ wts, int E_, int K_, int H_, int I_,
+    uint16_t* __restrict__ out, int T) {
+  static_assert(R <= NW, "one wavefront per shared down row");
+  const int K = G::K ? G::K : K_, E = G::E ? G::E : E_, H = G::H ? G::H : H_, I = G::I ? G::I : I_;
+  const int Is = G::IS >= 0 ? G::IS : Is_;
+  __shared__ float part[NW * NP][R];
+  __shared__ float ysp[DEC_MAX_T][R];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int r0 = blockIdx.x * R;
   const int S = T * K;
+  const bool dlane = lane < (I >> 5);                  // lanes that hold a routed down chunk
+  // 1. ids and weights of this wavefront's slots
+  int idv[NP];
+  float wsl[NP];
+#pragma unroll
+  for (int p = 0; p < NP; ++p) {
+    const int sl = wv + NW * p;
+    idv[p] = sl < S ? ids[sl] : 0;
+    wsl[p] = sl < S ? wts[sl] : 0.0f;
+  }
+  // 2. loads that do not depend on the ids: the shared down row, hs of token 0, h of each slot
+  const bool shared_row = Is > 0 && wv < R;
+  const int nsc = Is >> 3;                               // 8-bf16 chunks per shared row
+  uint4 sw[NSC];
+  uint32_t hs0[NSC][4];
+  if (shared_row) {
+    const uint4* row = reinterpret_cast<const uint4*>(sw2 + static_cast<int64_t>(min(r0 + wv, H - 1)) * Is);
+#pragma unroll
+    for (int i = 0; i < NSC; ++i) {
+      const int c = lane + 64 * i;
+      sw[i] = c < nsc ? row[c] : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < NSC; ++i) {
+      const int c = lane + 64 * i;
+      const uint4 v = c < nsc ? reinterpret_cast<const uint4*>(hs)[c] : make_uint4(0, 0, 0, 0);
+      hs0[i][0] = v.x; hs0[i][1] = v.y; hs0[i][2] = v.z; hs0[i][3] = v.w;
+    }
+  }
+  uint32_t xp[NP][16];
+#pragma unroll
+  for (int p = 0; p < NP; ++p) {
+    const int sl = wv + NW * p;
+    const uint4* hp = reinterpret_cast<const uint4*>(h + static_cast<int64_t>(sl) * I + 32 * lane);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint4 v = (sl < S && dlane) ? hp[q] : make_uint4(0, 0, 0, 0);
+      xp[p][4 * q] = v.x; xp[p][4 * q + 1] = v.y; xp[p][4 * q + 2] = v.z; xp[p][4 * q + 3] = v.w;
+    }
+  }
+  // 3. the routed down rows of this wavefront's slots
   const int64_t rq = I >> 1, rs = I >> 4;
   int e[NP];
   bool act[NP];
@@ -339,10 +365,9 @@ __global__ __launch_bounds__(KW * 64) void k_dec_down_combine(
   uint32_t sc[NP][R];
 #pragma unroll
   for (int p = 0; p < NP; ++p) {
-    const int sl = wv + KW * p;
-    const bool routed = sl < S;
-    e[p] = routed ? min(max(ids[sl], 0), E - 1) : 0;
-    act[p] = routed && lane < (I >> 5);
+    const int sl = wv + NW * p;
+    e[p] = min(max(idv[p], 0), E - 1);
+    act[p] = sl < S && dlane;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const int64_t base = static_cast<int64_t>(e[p]) * H + min(r0 + r, H - 1);
@@ -350,26 +375,40 @@ __global__ __launch_bounds__(KW * 64) void k_dec_down_combine(
       sc[p][r] = act[p] ? *reinterpret_cast<const uint16_t*>(s2 + base * rs + 2 * lane) : 0u;
     }
   }
+  float gk[NP];
+#pragma unroll
+  for (int p = 0; p < NP; ++p) gk[p] = wv + NW * p < S ? g2[e[p]] : 0.0f;
+  if (shared_row) {
+    for (int t = 0; t < T; ++t) {
+      float acc = 0.0f;
+#pragma unroll
+      for (int i = 0; i < NSC; ++i) {
+        uint32_t hv[4] = {hs0[i][0], hs0[i][1], hs0[i][2], hs0[i][3]};
+        if (t > 0) {
+          const int c = lane + 64 * i;
+          const uint4 v = c < nsc ? reinterpret_cast<const uint4*>(hs + static_cast<int64_t>(t) * Is)[c]
+                                  : make_uint4(0, 0, 0, 0);
+          hv[0] = v.x; hv[1] = v.y; hv[2] = v.z; hv[3] = v.w;
+        }
+        acc = bf16_chunk_dot(sw[i], hv, acc);
+      }
+      acc = wave_sum(acc);
+      if (lane == 0) ysp[t][wv] = acc;
+    }
+  }
 #pragma unroll
   for (int p = 0; p < NP; ++p) {
-    const int sl = wv + KW * p;
-    uint32_t xp[16];
-    const uint4* hp = reinterpret_cast<const uint4*>(h + static_cast<int64_t>(sl) * I + 32 * lane);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint4 v = act[p] ? hp[q] : make_uint4(0, 0, 0, 0);
-      xp[4 * q] = v.x; xp[4 * q + 1] = v.y; xp[4 * q + 2] = v.z; xp[4 * q + 3] = v.w;
-    }
+    const int sl = wv + NW * p;
     float acc[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      acc[r] = fmaf(e2m1x16_dot(cw[p][r].x, cw[p][r].y, xp), e4m3_to_f32<0>(sc[p][r]), 0.0f);
-      acc[r] = fmaf(e2m1x16_dot(cw[p][r].z, cw[p][r].w, xp + 8), e4m3_to_f32<1>(sc[p][r]), acc[r]);
+      acc[r] = fmaf(e2m1x16_dot(cw[p][r].x, cw[p][r].y, xp[p]), e4m3_to_f32<0>(sc[p][r]), 0.0f);
+      acc[r] = fmaf(e2m1x16_dot(cw[p][r].z, cw[p][r].w, xp[p] + 8), e4m3_to_f32<1>(sc[p][r]), acc[r]);
     }
 #pragma unroll
     for (int r = 0; r < R; ++r) acc[r] = wave_sum(acc[r]);
-    if (lane == 0) {
-      const float wk = sl < S ? wts[sl] * g2[e[p]] : 0.0f;
+    if (lane == 0 && sl < S) {
+      const float wk = wsl[p] * gk[p];
 #pragma unroll
       for (int r = 0; r < R; ++r) part[sl][r] = wk * acc[r];
     }
@@ -379,10 +418,9 @@ __global__ __launch_bounds__(KW * 64) void k_dec_down_combine(
   if (tid < T * R) {
     const int t = tid / R, r = tid - t * R;
     if (r0 + r < H) {
-      const int64_t oi = static_cast<int64_t>(t) * H + r0 + r;
-      float o = ys ? ys[oi] : 0.0f;
+      float o = Is > 0 ? ysp[t][r] : 0.0f;
       for (int k = 0; k < K; ++k) o += part[t * K + k][r];
-      out[oi] = f32_to_bf16(o);
+      out[static_cast<int64_t>(t) * H + r0 + r] = f32_to_bf16(o);
     }
   }
 }

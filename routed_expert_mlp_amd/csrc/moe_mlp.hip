@@ -372,8 +372,7 @@ void router_logits_plan(const Plan& p, void* ws, const uint16_t* x, const float*
 
 const char* const kDecodeStages[] = {"router_logits", "topk_bucket", "shared_gateup", "routed_gateup",
                                     "shared_down", "routed_down", "combine"};
-const char* const kDecode1Stages[] = {"logits_shared_gateup", "routed_gateup_shared_down",
-                                       "routed_down_combine"};
+const char* const kDecode1Stages[] = {"logits_shared_gateup", "routed_gateup", "shared_routed_down_combine"};
 const char* const kPrefillStages[] = {"router_logits", "topk", "permute", "routed_gateup", "routed_down",
                                      "shared_gateup", "shared_down", "combine"};
 const char* const kDenseStages[] = {"dense_gateup", "dense_down"};
@@ -382,11 +381,10 @@ const char* const kDenseStages[] = {"dense_gateup", "dense_down"};
 // H <= 4096 and I, Is <= 2048.
 constexpr int kDec1MaxH = 4096;
 
-int dec1_kw(int K) { return K <= 4 ? 4 : K <= 8 ? 8 : 16; }
-
 // The few-token decode kernels (decode1.hpp) take up to 4 tokens (the MTP
 // verify shapes: one token plus up to three drafted ones), T*K <= 64 slots.
 constexpr int64_t kDecFewMaxT = 4;
+static_assert(kDecFewMaxT <= DEC_MAX_T, "k_dec_down_combine keeps the shared rows' sums of DEC_MAX_T tokens");
 
 bool decode1_ok(const moe_mlp_config* c, int64_t T, int prefill) {
   if (prefill || T < 1 || T > kDecFewMaxT || c->kind != MOE_MLP_KIND_ROUTED) return false;
@@ -401,35 +399,68 @@ int n_stages(const moe_mlp_config* c, int64_t T, int prefill) {
   return gemm_form(c, T, prefill) ? 8 : 7;
 }
 
-// Few-token decode (1..4 tokens): 3 launches (see decode1.hpp).
-template <int NSC>
+// Few-token decode (1..4 tokens): 3 launches (see decode1.hpp).  The layer
+// shape of GLM-5.3-Flash (H 4096, I and Is 1536, 288 experts, top-8) has
+// kernel instances of its own with the geometry compiled in.
+using DecGeoFlash = DecGeo<4096, 1536, 288, 8, 1536>;
+
+bool glm_flash_geometry(const moe_mlp_config* c) {
+  return c->hidden == DecGeoFlash::H && c->moe_intermediate == DecGeoFlash::I &&
+         c->num_experts == DecGeoFlash::E && c->top_k == DecGeoFlash::K && c->n_shared_experts == 1 &&
+         c->shared_intermediate == DecGeoFlash::IS;
+}
+
+// Routed gate/up: RJ (gate, up) row pairs per wavefront (16 KB of codes at H = 4096).
+constexpr int kDecRJ = 4;
+
 void dec_gateup(const moe_mlp_config* c, const moe_mlp_weights* w, const uint16_t* x, const float* logits,
-                int32_t* ids, float* wts, int32_t* ids_out, float* w_out, uint16_t* h, const uint16_t* hs,
-                float* ys, int T, hipStream_t s, Ev ev) {
-  constexpr int RJ = 4, NC = 2, RS = 8;
+                int32_t* ids, float* wts, int32_t* ids_out, float* w_out, uint16_t* h, int T, hipStream_t s, Ev ev) {
+  constexpr int NC = 2;
   const int H = c->hidden, I = c->moe_intermediate, K = c->top_k;
-  const int Is = c->n_shared_experts ? c->shared_intermediate : 0;
-  const int n_sd = Is ? static_cast<int>(cdiv(H, 4 * RS)) : 0;
-  const unsigned grid = static_cast<unsigned>(n_sd + T * K * cdiv(I, 4 * RJ));
+  const unsigned grid = static_cast<unsigned>(T * K * cdiv(I, 4 * kDecRJ));
+  auto go = [&](auto kern) {
+    launch(kern, dim3(grid), dim3(256), s, ev.a, ev.b, x, w->w13_q, w->w13_s, w->w13_g, logits, w->router_bias, K,
+           c->routed_scaling_factor, ids, wts, ids_out, w_out, c->num_experts, H, I, c->swiglu_limit, h);
+  };
+  if (glm_flash_geometry(c)) {
+    go(k_dec_gateup<kDecRJ, NC, true, 5, DecGeoFlash>);
+    return;
+  }
   with_nj(c->num_experts, [&](auto nj) {
-    launch(k_dec_gateup<RJ, NC, decltype(nj)::value, RS, NSC>, dim3(grid), dim3(256), s, ev.a, ev.b, x, w->w13_q,
-           w->w13_s, w->w13_g, logits, w->router_bias, K, c->routed_scaling_factor, ids, wts, ids_out, w_out,
-           c->num_experts, H, I, c->swiglu_limit, h, w->shared_w2, hs, Is, ys, n_sd, T);
+    constexpr int NJ = decltype(nj)::value;
+    if (H == 64 * 32 * NC) go(k_dec_gateup<kDecRJ, NC, true, NJ, DecGeoAny>);     // every lane holds NC chunks
+    else go(k_dec_gateup<kDecRJ, NC, false, NJ, DecGeoAny>);
   });
 }
 
-template <int KW, int NP>
-void launch_down_combine(const moe_mlp_config* c, const moe_mlp_weights* w, const uint16_t* h, const float* ys,
+// Shared + routed down + combine: 4 output rows per block; NW wavefronts with
+// NP slots each (NW * NP >= T * K), NSC 16-byte chunks per lane of a shared row.
+template <int NW, int NP>
+void launch_down_combine(const moe_mlp_config* c, const moe_mlp_weights* w, const uint16_t* h, const uint16_t* hs,
                          const int32_t* ids, const float* wts, uint16_t* out, int T, hipStream_t s, Ev ev) {
   constexpr int R = 4;
   const int H = c->hidden;
-  launch(k_dec_down_combine<R, KW, NP>, dim3(static_cast<unsigned>(cdiv(H, R))), dim3(KW * 64), s, ev.a, ev.b, h,
-         w->w2_q, w->w2_s, w->w2_g, ys, ids, wts, c->num_experts, c->top_k, H, c->moe_intermediate, out, T);
+  const int Is = c->n_shared_experts ? c->shared_intermediate : 0;
+  const dim3 grid(static_cast<unsigned>(cdiv(H, R))), block(NW * 64);
+  auto go = [&](auto kern) {
+    launch(kern, grid, block, s, ev.a, ev.b, h, w->w2_q, w->w2_s, w->w2_g, w->shared_w2, hs, Is, ids, wts,
+           c->num_experts, c->top_k, H, c->moe_intermediate, out, T);
+  };
+  if (glm_flash_geometry(c)) {
+    go(k_dec_down_combine<R, NW, NP, 3, DecGeoFlash>);
+    return;
+  }
+  switch (static_cast<int>(cdiv(Is / 8, 64))) {
+    case 0: case 1: go(k_dec_down_combine<R, NW, NP, 1, DecGeoAny>); break;
+    case 2: go(k_dec_down_combine<R, NW, NP, 2, DecGeoAny>); break;
+    case 3: go(k_dec_down_combine<R, NW, NP, 3, DecGeoAny>); break;
+    default: go(k_dec_down_combine<R, NW, NP, 4, DecGeoAny>); break;
+  }
 }
 
 void decode1(const moe_mlp_config* c, const moe_mlp_weights* w, const uint16_t* x, int T, uint16_t* out,
              int32_t* ids_out, float* w_out, float* logits, int32_t* ids, float* wts, uint16_t* h, uint16_t* hs,
-             float* ys, hipStream_t s, Ev e0, Ev e1, Ev e2) {
+             hipStream_t s, Ev e0, Ev e1, Ev e2) {
   const int H = c->hidden, E = c->num_experts, K = c->top_k;
   const int Is = c->n_shared_experts ? c->shared_intermediate : 0;
   const int nlb = static_cast<int>(cdiv(E, 4)), nsb = static_cast<int>(cdiv(Is, 4));
@@ -439,20 +470,14 @@ void decode1(const moe_mlp_config* c, const moe_mlp_weights* w, const uint16_t* 
   else
     launch(k_dec_logits_shared_t<16, 8>, dim3(nlb + nsb), dim3(256), s, e0.a, e0.b, x, w->router_w, logits, E, H,
            w->shared_w13, Is, hs, c->swiglu_limit, nlb, T);
-  const int nsc = static_cast<int>(cdiv(Is / 8, 64));
-  if (nsc <= 1) dec_gateup<1>(c, w, x, logits, ids, wts, ids_out, w_out, h, hs, ys, T, s, e1);
-  else if (nsc == 2) dec_gateup<2>(c, w, x, logits, ids, wts, ids_out, w_out, h, hs, ys, T, s, e1);
-  else if (nsc == 3) dec_gateup<3>(c, w, x, logits, ids, wts, ids_out, w_out, h, hs, ys, T, s, e1);
-  else dec_gateup<4>(c, w, x, logits, ids, wts, ids_out, w_out, h, hs, ys, T, s, e1);
-  const float* ysr = Is ? ys : nullptr;
-  // one wavefront per slot at one token (K <= 16), else 16 wavefronts looping over the T*K slots
+  dec_gateup(c, w, x, logits, ids, wts, ids_out, w_out, h, T, s, e1);
+  // one slot per wavefront up to 8 slots (4 or 8 wavefronts), else 16 wavefronts with up to 4 slots each
   const int S = T * K;
-  if (T == 1 && dec1_kw(K) == 4) launch_down_combine<4, 1>(c, w, h, ysr, ids, wts, out, T, s, e2);
-  else if (T == 1 && dec1_kw(K) == 8) launch_down_combine<8, 1>(c, w, h, ysr, ids, wts, out, T, s, e2);
-  else if (S <= 16) launch_down_combine<16, 1>(c, w, h, ysr, ids, wts, out, T, s, e2);
-  else if (S <= 32) launch_down_combine<16, 2>(c, w, h, ysr, ids, wts, out, T, s, e2);
-  else if (S <= 48) launch_down_combine<16, 3>(c, w, h, ysr, ids, wts, out, T, s, e2);
-  else launch_down_combine<16, 4>(c, w, h, ysr, ids, wts, out, T, s, e2);
+  if (S <= 4) launch_down_combine<4, 1>(c, w, h, hs, ids, wts, out, T, s, e2);
+  else if (S <= 8) launch_down_combine<8, 1>(c, w, h, hs, ids, wts, out, T, s, e2);
+  else if (S <= 16) launch_down_combine<16, 1>(c, w, h, hs, ids, wts, out, T, s, e2);
+  else if (S <= 32) launch_down_combine<16, 2>(c, w, h, hs, ids, wts, out, T, s, e2);
+  else launch_down_combine<16, 4>(c, w, h, hs, ids, wts, out, T, s, e2);
 }
 
 int run_layer(const moe_mlp_config* c, const moe_mlp_weights* w, const uint16_t* x, int64_t T, uint16_t* out,
@@ -517,7 +542,7 @@ int run_layer(const moe_mlp_config* c, const moe_mlp_weights* w, const uint16_t*
   const float rsf = c->routed_scaling_factor;
 
   if (decode1_ok(c, T, prefill)) {
-    decode1(c, w, x, Ti, out, ids_out, w_out, logits, ids, wts, h, hs, ys, s, ev(0), ev(1), ev(2));
+    decode1(c, w, x, Ti, out, ids_out, w_out, logits, ids, wts, h, hs, s, ev(0), ev(1), ev(2));
     return launch_status();
   }
   // decode of up to 16 tokens with H <= 4096: router logits and the shared

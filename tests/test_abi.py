@@ -202,11 +202,11 @@ def test_profiled_entry_validation():
     w = full_weights()
     n = 3                               # one-token decode stages of this config
     names = [L.moe_mlp_stage_name(ctypes.byref(c), 1, 0, i) for i in range(n + 1)]
-    assert [x.decode() for x in names[:n]] == ["logits_shared_gateup", "routed_gateup_shared_down",
-                                                   "routed_down_combine"]
+    assert [x.decode() for x in names[:n]] == ["logits_shared_gateup", "routed_gateup",
+                                                   "shared_routed_down_combine"]
     assert names[n] is None
     assert [L.moe_mlp_stage_name(ctypes.byref(c), 8, 0, i).decode() for i in range(7)][3] == "routed_gateup"
-    assert L.moe_mlp_stage_name(ctypes.byref(c), 4, 0, 1).decode() == "routed_gateup_shared_down"
+    assert L.moe_mlp_stage_name(ctypes.byref(c), 4, 0, 2).decode() == "shared_routed_down_combine"
     assert L.moe_mlp_stage_name(ctypes.byref(c), 64, 0, 2).decode() == "permute"
     assert L.moe_mlp_stage_name(ctypes.byref(c), 2, 1, 8) is None
     assert L.moe_mlp_stage_name(None, 1, 0, 0) is None
