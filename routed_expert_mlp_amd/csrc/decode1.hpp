@@ -317,15 +317,21 @@ __global__ __launch_bounds__(NW * 64) void k_dec_down_combine(
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int r0 = blockIdx.x * R;
   const int S = T * K;
-  const bool dlane = lane < (I >> 5);                  // lanes that hold a routed down chunk
+  // Every load is issued unconditionally from an in-bounds address (lanes and
+  // slots past the end re-read a valid element and are zeroed afterwards), so
+  // no load sits behind a branch and the waits before the arithmetic can be
+  // exact.
+  const int nd = I >> 5;                               // routed down chunks per row
+  const bool dlane = lane < nd;
+  const int dl = dlane ? lane : nd - 1;
   // 1. ids and weights of this wavefront's slots
   int idv[NP];
   float wsl[NP];
 #pragma unroll
   for (int p = 0; p < NP; ++p) {
-    const int sl = wv + NW * p;
-    idv[p] = sl < S ? ids[sl] : 0;
-    wsl[p] = sl < S ? wts[sl] : 0.0f;
+    const int sl = min(wv + NW * p, S - 1);
+    idv[p] = ids[sl];
+    wsl[p] = wts[sl];
   }
   // 2. loads that do not depend on the ids: the shared down row, hs of token 0, h of each slot
   const bool shared_row = Is > 0 && wv < R;
@@ -335,49 +341,60 @@ __global__ __launch_bounds__(NW * 64) void k_dec_down_combine(
   if (shared_row) {
     const uint4* row = reinterpret_cast<const uint4*>(sw2 + static_cast<int64_t>(min(r0 + wv, H - 1)) * Is);
 #pragma unroll
-    for (int i = 0; i < NSC; ++i) {
-      const int c = lane + 64 * i;
-      sw[i] = c < nsc ? row[c] : make_uint4(0, 0, 0, 0);
-    }
+    for (int i = 0; i < NSC; ++i) sw[i] = row[min(lane + 64 * i, nsc - 1)];
 #pragma unroll
     for (int i = 0; i < NSC; ++i) {
-      const int c = lane + 64 * i;
-      const uint4 v = c < nsc ? reinterpret_cast<const uint4*>(hs)[c] : make_uint4(0, 0, 0, 0);
+      const uint4 v = reinterpret_cast<const uint4*>(hs)[min(lane + 64 * i, nsc - 1)];
       hs0[i][0] = v.x; hs0[i][1] = v.y; hs0[i][2] = v.z; hs0[i][3] = v.w;
     }
   }
   uint32_t xp[NP][16];
 #pragma unroll
   for (int p = 0; p < NP; ++p) {
-    const int sl = wv + NW * p;
-    const uint4* hp = reinterpret_cast<const uint4*>(h + static_cast<int64_t>(sl) * I + 32 * lane);
+    const int sl = min(wv + NW * p, S - 1);
+    const uint4* hp = reinterpret_cast<const uint4*>(h + static_cast<int64_t>(sl) * I + 32 * dl);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const uint4 v = (sl < S && dlane) ? hp[q] : make_uint4(0, 0, 0, 0);
+      const uint4 v = hp[q];
       xp[p][4 * q] = v.x; xp[p][4 * q + 1] = v.y; xp[p][4 * q + 2] = v.z; xp[p][4 * q + 3] = v.w;
     }
   }
   // 3. the routed down rows of this wavefront's slots
   const int64_t rq = I >> 1, rs = I >> 4;
   int e[NP];
-  bool act[NP];
   uint4 cw[NP][R];
   uint32_t sc[NP][R];
 #pragma unroll
   for (int p = 0; p < NP; ++p) {
-    const int sl = wv + NW * p;
     e[p] = min(max(idv[p], 0), E - 1);
-    act[p] = sl < S && dlane;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const int64_t base = static_cast<int64_t>(e[p]) * H + min(r0 + r, H - 1);
-      cw[p][r] = act[p] ? *reinterpret_cast<const uint4*>(q2 + base * rq + 16 * lane) : make_uint4(0, 0, 0, 0);
-      sc[p][r] = act[p] ? *reinterpret_cast<const uint16_t*>(s2 + base * rs + 2 * lane) : 0u;
+      cw[p][r] = *reinterpret_cast<const uint4*>(q2 + base * rq + 16 * dl);
+      sc[p][r] = *reinterpret_cast<const uint16_t*>(s2 + base * rs + 2 * dl);
     }
   }
   float gk[NP];
 #pragma unroll
-  for (int p = 0; p < NP; ++p) gk[p] = wv + NW * p < S ? g2[e[p]] : 0.0f;
+  for (int p = 0; p < NP; ++p) gk[p] = g2[e[p]];
+  __builtin_amdgcn_sched_barrier(0);
+  if (shared_row) {
+#pragma unroll
+    for (int i = 0; i < NSC; ++i)
+      if (lane + 64 * i >= nsc) sw[i] = make_uint4(0, 0, 0, 0);
+  }
+  bool act[NP];
+#pragma unroll
+  for (int p = 0; p < NP; ++p) {
+    act[p] = wv + NW * p < S && dlane;
+    if (!act[p]) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        cw[p][r] = make_uint4(0, 0, 0, 0);
+        sc[p][r] = 0u;
+      }
+    }
+  }
   if (shared_row) {
     for (int t = 0; t < T; ++t) {
       float acc = 0.0f;
