@@ -8,17 +8,22 @@ H=4096, I=1536, E=288 experts resident on the GPU, K=8, shared expert
 intermediate 1536.  Inputs are synthetic (seeded), already in HBM.
 
 `value` is decode weight-stream GB/s: the algorithmic bytes of a step
-(8 touched experts x 10,616,832 B NVFP4 + 37,748,736 B shared BF16 +
-4,718,592 B fp32 router + x and out) over the measured step time.  Steps
+(unique touched experts x 10,616,832 B NVFP4 + 37,748,736 B shared BF16 +
+4,718,592 B fp32 router + x and out) over the measured step time of the
+K timed steps (issued back to back between two stream events).  Steps
 rotate over several copies of the layer's weights (each with its own input
-token) so that every step streams its weights from HBM, not from the
-256 MB last-level cache, as a layer inside a full model would.
+token; 8 copies touch ~1 GB between two visits of one copy, 4x the 256 MB
+last-level cache) so every step streams its weights from HBM, as a layer
+inside a full model would.  The median and p10/p90 step time come from 64
+further event-bracketed runs of 8 back-to-back steps.
 
-Also reported: per-stage times from HIP events recorded on the launch
-stream (moe_mlp_forward_profiled), the roofline of the dominant kernel
-(routed gate/up GEMV), decode at T=16/64, the prefill grouped-GEMM path at
-T=4096 (TFLOP/s), and the fp64 CPU oracle timed on a bounded sample on the
-host cores.
+Also reported: per-stage kernel times (HIP events attached to the stages'
+dispatches, steps issued back to back), the roofline of the dominant
+kernel (routed gate/up GEMV) with its rocprofv3 HBM traffic, a measured
+device-copy bandwidth beside the 8 TB/s datasheet peak, decode at T=2, 4,
+16, 64, the skewed 64-token top-16 workload, the literal-bias workloads,
+the prefill grouped-GEMM path at T=4096 (TFLOP/s), the dense FFN, and the
+fp64 CPU oracle timed on bounded samples on the host cores.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -35,10 +40,12 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E
 CALIB_BYTES = 512 << 20         # the counter-calibration copy
+COPY_BYTES = 1 << 30            # the measured device copy
 BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "routed_gateup_shared_down_flash_decode_t1_traffic.txt")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "routed_gateup_flash_decode_t1_traffic.txt")
 GEMV_SOURCES = ["routed_expert_mlp_amd/csrc/decode1.hpp", "routed_expert_mlp_amd/csrc/router.hpp",
                 "routed_expert_mlp_amd/csrc/gemv.hpp", "routed_expert_mlp_amd/csrc/common.hpp"]
+DOMINANT = "routed_gateup"      # stage of the dominant one-token kernel (k_dec_gateup)
 
 
 def log(*a):
@@ -48,13 +55,14 @@ def log(*a):
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=500)
-    p.add_argument("--warmup", type=int, default=50)
-    p.add_argument("--copies", type=int, default=4, help="weight copies rotated over (cold HBM reads)")
+    p.add_argument("--steps", type=int, default=400)
+    p.add_argument("--warmup", type=int, default=40)
+    p.add_argument("--copies", type=int, default=8, help="weight copies rotated over (cold HBM reads)")
     p.add_argument("--no-prefill", action="store_true")
     p.add_argument("--no-extra-decode", action="store_true")
+    p.add_argument("--no-variants", action="store_true", help="skip the skewed and literal-bias workloads")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle CPU time")
+    p.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle CPU time per sample")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="end the decode part with 3 device copies of 512 MiB (counter calibration)")
     p.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -69,7 +77,6 @@ class HipEvents:
         self.hip = ctypes.CDLL("libamdhip64.so.7")
         self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
         self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
-        self.hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
         self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
 
     def create(self, n):
@@ -86,9 +93,6 @@ class HipEvents:
         if self.hip.hipEventElapsedTime(ctypes.byref(ms), a, b) != 0:
             raise RuntimeError("hipEventElapsedTime failed")
         return ms.value
-
-    def sync(self, e):
-        self.hip.hipEventSynchronize(e)
 
     def destroy(self, evs):
         for e in evs:
@@ -202,7 +206,9 @@ def summarize_traffic(fetch_csv, write_csv):
     per = {}
     for label, path in (("fetch", fetch_csv), ("write", write_csv)):
         vals, order = per_kernel(path)
-        copies = [v for n, v in order if "copyBuffer" in n][-3:]
+        # the calibration copies: the first three copies after the last decode dispatch
+        last = max(i for i, (n, _) in enumerate(order) if "k_dec_" in n)
+        copies = [v for n, v in order[last + 1:] if "copyBuffer" in n][:3]
         if len(copies) < 3:
             raise SystemExit(f"{path}: the calibration copies are missing")
         scale[label] = CALIB_BYTES / (float(np.mean(copies)) * 1024.0)
@@ -226,7 +232,8 @@ def summarize_traffic(fetch_csv, write_csv):
     return out
 
 
-def run_decode_steps(fn, n):
+def loop_seconds(fn, n):
+    """Mean seconds per call of n calls issued back to back (one synchronisation at each end)."""
     import torch
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -236,68 +243,148 @@ def run_decode_steps(fn, n):
     return (time.perf_counter() - t0) / max(n, 1)
 
 
-def stage_times(cfg, wts, xs, out, prefill, n, ev, ws, per_step=None):
-    """Average per-stage milliseconds over n profiled steps: HIP events attached to the
-    stages' first and last kernel dispatches on the launch stream.  per_step, when a
-    list, receives each step's first-kernel-start to last-kernel-end milliseconds."""
+def timed_region_ms(fn, n):
+    """Exactly n calls back to back between two stream events, with a device synchronisation on
+    both sides: ms from the first event to the second."""
+    import torch
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record()
+    for i in range(n):
+        fn(i)
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b)
+
+
+def chunk_step_ms(fn, n_chunks, per_chunk):
+    """n_chunks runs of per_chunk back-to-back calls with a stream event between runs (none inside
+    a run): the mean ms per call of each run."""
+    import torch
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(n_chunks + 1)]
+    torch.cuda.synchronize()
+    evs[0].record()
+    i = 0
+    for c in range(n_chunks):
+        for _ in range(per_chunk):
+            fn(i)
+            i += 1
+        evs[c + 1].record()
+    torch.cuda.synchronize()
+    return [evs[c].elapsed_time(evs[c + 1]) / per_chunk for c in range(n_chunks)]
+
+
+def pctl(vals_ms):
+    import numpy as np
+    a = np.asarray(vals_ms, dtype=np.float64) * 1e3
+    return [round(float(v), 2) for v in np.percentile(a, [10, 50, 90])]
+
+
+def stage_times(cfg, wts, xs, out, prefill, n, ev, ws):
+    """Per-stage milliseconds (mean over n steps) from HIP events attached to each stage's first
+    and last kernel dispatch; the n steps are issued back to back and read after one sync."""
+    import numpy as np
     import torch
     from routed_expert_mlp_amd import capi
     names = capi.stage_names(cfg, xs[0].shape[0], prefill)
-    sums = [0.0] * len(names)
-    evs = ev.create(2 * len(names))
+    m = 2 * len(names)
+    evs = ev.create(m * n)
     try:
+        torch.cuda.synchronize()
         for i in range(n):
             r = i % len(wts)
-            capi.moe_mlp_forward_profiled(cfg, wts[r], xs[r], out[r], prefill, evs, ws=ws)
-            ev.sync(evs[-1])
+            capi.moe_mlp_forward_profiled(cfg, wts[r], xs[r], out[r], prefill, evs[m * i:m * (i + 1)], ws=ws)
+        torch.cuda.synchronize()
+        t = np.zeros((n, len(names)))
+        for i in range(n):
             for j in range(len(names)):
-                sums[j] += ev.elapsed_ms(evs[2 * j], evs[2 * j + 1])
-            if per_step is not None:
-                per_step.append(ev.elapsed_ms(evs[0], evs[-1]))
+                t[i, j] = ev.elapsed_ms(evs[m * i + 2 * j], evs[m * i + 2 * j + 1])
     finally:
         torch.cuda.synchronize()
         ev.destroy(evs)
-    return {nm: s / n for nm, s in zip(names, sums)}
+    skip = min(n // 4, 8)                        # the first steps start on an idle GPU
+    return {nm: float(np.mean(t[skip:, j])) for j, nm in enumerate(names)}
 
 
-def cpu_baseline(w, budget_s):
-    """The fp64 oracle, as it stands, on a bounded sample of decode tokens."""
+def device_copy_gbs(device):
+    """Read+write GB/s of a 1 GiB device-to-device copy (best of 5)."""
+    import torch
+    src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=device).fill_(1.0)
+    dst = torch.empty_like(src)
+    best = 1e9
+    for i in range(6):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        dst.copy_(src)
+        b.record()
+        torch.cuda.synchronize()
+        if i:
+            best = min(best, a.elapsed_time(b))
+    del src, dst
+    torch.cuda.empty_cache()
+    return 2 * COPY_BYTES / (best * 1e-3) / 1e9
+
+
+def decode_line(cfg, w, wts, xs, T, dev, steps, ws=None):
+    """Decode of T tokens over rotated weight copies: GB/s, us/step (mean of a back-to-back loop),
+    tokens/s, unique experts touched."""
     import numpy as np
+    import torch
+    from routed_expert_mlp_amd import capi
+    R = len(wts)
+    out_t = [torch.empty((T, w.H), dtype=torch.bfloat16, device=dev) for _ in range(R)]
+    ids_t = [torch.empty((T, w.K), dtype=torch.int32, device=dev) for _ in range(R)]
+    ws = capi.workspace(cfg, T, False, dev) if ws is None else ws
+    calls = [capi.bind_layer(cfg, wts[r], xs[r], out_t[r], ids_t[r], ws=ws) for r in range(R)]
+    for i in range(2 * R):
+        calls[i % R]()
+    s_t = loop_seconds(lambda i: calls[i % R](), steps)
+    u = [int(torch.unique(ids_t[r]).numel()) for r in range(R)]
+    b = float(np.mean([decode_bytes(w, x, T) for x in u]))
+    return {"gbs": round(b / s_t / 1e9, 1), "us_per_step": round(s_t * 1e6, 1),
+            "tokens_per_s": round(T / s_t, 1), "unique_experts": float(np.mean(u))}
+
+
+def cpu_decode_baseline(w, budget_s, blas_threads=None):
+    """The fp64 oracle, as it stands, on a bounded sample of single-token decodes."""
+    import contextlib
     import psutil
     import threadpoolctl
     import oracle as O
     import synth
-    blas = threadpoolctl.threadpool_info()
-    threads = max([b.get("num_threads", 1) for b in blas] or [1])
-    rw, rb = synth.router_weight(w), synth.router_bias(w)
-    g13, g2 = synth.w13_globals(w), synth.w2_globals(w)
-    s13, s2 = synth.shared_w13(w), synth.shared_w2(w)
-    cache = {}
+    limiter = threadpoolctl.threadpool_limits(blas_threads) if blas_threads else contextlib.nullcontext()
+    with limiter:
+        blas = threadpoolctl.threadpool_info()
+        threads = max([b.get("num_threads", 1) for b in blas] or [1])
+        rw, rb = synth.router_weight(w), synth.router_bias(w)
+        g13, g2 = synth.w13_globals(w), synth.w2_globals(w)
+        s13, s2 = synth.shared_w13(w), synth.shared_w2(w)
+        cache = {}
 
-    def expert(e):
-        if e not in cache:
-            cache[e] = synth.expert_w13(w, e) + synth.expert_w2(w, e)
-        return cache[e]
+        def expert(e):
+            if e not in cache:
+                cache[e] = synth.expert_w13(w, e) + synth.expert_w2(w, e)
+            return cache[e]
 
-    wts = O.RoutedWeights(rw, rb, g13, g2, expert, s13, s2)
-    proc = psutil.Process()
-    done, elapsed, cpu = 0, 0.0, 0.0
-    t = 0
-    while elapsed < budget_s and done < 64:
-        x = synth.x_row(w, 1000 + t)[None, :]
-        ids, _, _, _ = O.route(O.decode_bf16(x), rw, rb, w.K, w.rsf)
-        for e in ids[0]:
-            expert(int(e))                    # input generation is not timed
-        c0 = proc.cpu_times()
-        t0 = time.perf_counter()
-        O.moe_layer(x, wts, w.K, w.rsf, w.swiglu_limit)
-        elapsed += time.perf_counter() - t0
-        c1 = proc.cpu_times()
-        cpu += (c1.user - c0.user) + (c1.system - c0.system)
-        done += 1
-        t += 1
-        if len(cache) > 64:
-            cache.clear()
+        wts = O.RoutedWeights(rw, rb, g13, g2, expert, s13, s2)
+        proc = psutil.Process()
+        done, elapsed, cpu = 0, 0.0, 0.0
+        t = 0
+        while elapsed < budget_s and done < 64:
+            x = synth.x_row(w, 1000 + t)[None, :]
+            ids, _, _, _ = O.route(O.decode_bf16(x), rw, rb, w.K, w.rsf)
+            for e in ids[0]:
+                expert(int(e))                    # input generation is not timed
+            c0 = proc.cpu_times()
+            t0 = time.perf_counter()
+            O.moe_layer(x, wts, w.K, w.rsf, w.swiglu_limit)
+            elapsed += time.perf_counter() - t0
+            c1 = proc.cpu_times()
+            cpu += (c1.user - c0.user) + (c1.system - c0.system)
+            done += 1
+            t += 1
+            if len(cache) > 64:
+                cache.clear()
     per_tok = elapsed / done
     return {
         "value": round(decode_bytes(w, w.K, 1) / per_tok / 1e9, 4),
@@ -310,6 +397,28 @@ def cpu_baseline(w, budget_s):
     }
 
 
+def cpu_prefill_baseline(wp, n_tokens):
+    """The fp64 oracle on the first n_tokens tokens of the 4096-token prefill workload (one
+    moe_layer call; its cost is dominated by building the touched experts' fp64 weights)."""
+    import numpy as np
+    import threadpoolctl
+    import oracle as O
+    import synth
+    threads = max([b.get("num_threads", 1) for b in threadpoolctl.threadpool_info()] or [1])
+    x = synth.x_rows(wp, n_tokens)
+    wts = O.RoutedWeights(synth.router_weight(wp), synth.router_bias(wp), synth.w13_globals(wp),
+                          synth.w2_globals(wp), lambda e: synth.expert_w13(wp, e) + synth.expert_w2(wp, e),
+                          synth.shared_w13(wp), synth.shared_w2(wp))
+    t0 = time.perf_counter()
+    _, ids, _ = O.moe_layer(x, wts, wp.K, wp.rsf, wp.swiglu_limit)
+    el = time.perf_counter() - t0
+    fl = 2.0 * n_tokens * (wp.K * 3 * wp.H * wp.I + 3 * wp.H * wp.Is + wp.H * wp.E)
+    return {"value": round(fl / el / 1e9, 3), "unit": "GFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"the first {n_tokens} tokens of the 4096-token prefill workload in one oracle call "
+                      f"({len(np.unique(ids))} experts touched, expert weights regenerated inside the "
+                      f"timed call); {el:.1f} s, {n_tokens / el:.3f} tokens/s"}
+
+
 def main():
     args = parse()
     if args.summarize_traffic:
@@ -317,12 +426,13 @@ def main():
         head = ["# HBM traffic of the one-token decode kernels, flash_decode_t1 (T=1, H=4096, I=1536, E=288, K=8,",
                 "# Is=1536), from two rocprofv3 counter runs on one MI355X (from the repository root):",
                 "#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch -o run -- \\",
-                "#       python3 bench.py --steps 20 --warmup 5 --no-prefill --no-extra-decode --no-cpu-baseline --calibrate-copy",
+                "#       python3 bench.py --steps 20 --warmup 5 --no-prefill --no-extra-decode --no-variants \\",
+                "#       --no-cpu-baseline --calibrate-copy",
                 "#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write -o run -- (same)",
                 "#   python3 bench.py --summarize-traffic <fetch counter_collection.csv> <write counter_collection.csv>",
                 "# FETCH_SIZE / WRITE_SIZE are KiB per dispatch; each is scaled so that the run's 512 MiB device",
-                "# copies read and write 512 MiB.  bench.py reports hbm_bytes_per_launch as roofline.traffic while",
-                "# source_sha256_16 matches the kernel sources."]
+                "# copies read and write 512 MiB.  bench.py reports hbm_bytes_per_launch (k_dec_gateup) as",
+                "# roofline.traffic while source_sha256_16 matches the kernel sources."]
         with open(TRAFFIC_FILE, "w") as f:
             f.write("\n".join(head + lines) + "\n")
         print("\n".join(lines))
@@ -366,18 +476,17 @@ def main():
     uniq = [int(torch.unique(ids[r]).numel()) for r in range(R)]
     step_bytes = float(np.mean([decode_bytes(w, u, 1) for u in uniq]))
     log(f"[bench] timing {args.steps} decode steps over {R} weight copies")
-    sec = run_decode_steps(step, args.steps)
+    total_ms = timed_region_ms(step, args.steps)
+    sec = total_ms * 1e-3 / args.steps
     gbs = step_bytes / sec / 1e9
+    n_chunks = 64
+    p10, p50, p90 = pctl(chunk_step_ms(step, n_chunks, R))
 
-    n_prof = max(50, min(args.steps, 500))
-    step_ms = []
-    st = stage_times(cfg, wts, xs, outs, False, n_prof, ev, ws, step_ms)
-    prof_step_ms = sum(st.values())
-    p10, p50, p90 = (float(v) for v in np.percentile(np.asarray(step_ms) * 1e3, [10, 50, 90]))
+    st = stage_times(cfg, wts, xs, outs, False, 8 * R, ev, ws)
     # warm: one weight copy, so the 8 experts + shared + router (~128 MB) stay in the 256 MB MALL
     for i in range(20):
         calls[0]()
-    sec_warm = min(run_decode_steps(lambda i: calls[0](), args.steps) for _ in range(3))
+    sec_warm = min(loop_seconds(lambda i: calls[0](), 400) for _ in range(3))
     # the same steps replayed from HIP graphs of 16 steps each (one graph per starting copy)
     graph_us = None
     try:
@@ -393,7 +502,7 @@ def main():
             gs.append(g)
         for i in range(2 * R):
             gs[i % R].replay()
-        n_rep = max(4, args.steps // 16)
+        n_rep = max(8, 400 // 16)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for i in range(n_rep):
@@ -412,7 +521,7 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    gu_ms = st["routed_gateup"]
+    dom_ms = st[DOMINANT]
     # algorithmic bytes of each one-token stage
     exp13 = 2 * w.I * w.H // 2 + 2 * w.I * w.H // 16          # NVFP4 gate/up of one expert
     exp2 = w.H * w.I // 2 + w.H * w.I // 16                    # NVFP4 down of one expert
@@ -422,30 +531,33 @@ def main():
         "shared_routed_down_combine": (w.K * exp2 + 2 * w.H * w.Is + 2 * w.K * w.I + 2 * w.Is + 2 * w.H
                                        + 8 * w.K),
     }
-    gu_bytes = stage_bytes["routed_gateup"]
-    gu_gbs = gu_bytes / (gu_ms * 1e-3) / 1e9
+    dom_bytes = stage_bytes[DOMINANT]
+    dom_gbs = dom_bytes / (dom_ms * 1e-3) / 1e9
     traffic = read_traffic()
+    copy_gbs = None
+    if not args.calibrate_copy:
+        log("[bench] measuring the device copy bandwidth")
+        copy_gbs = device_copy_gbs(dev)
     extra = {"tokens_per_s": round(1.0 / sec, 1), "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
              "bytes_per_step": int(step_bytes),
+             "step_us_p10_p50_p90": [p10, p50, p90],
+             "step_timing": f"value and ms_per_step: the {args.steps} timed steps issued back to back between two "
+                            f"stream events; percentiles: {n_chunks} further runs of {R} back-to-back steps (one per "
+                            f"weight copy) with a stream event between runs, mean per step of each run",
              "decode_stage_us": {k: round(v * 1e3, 2) for k, v in st.items()},
              "decode_stage_gbs": {k: round(stage_bytes[k] / (v * 1e-3) / 1e9, 1)
                                   for k, v in st.items() if k in stage_bytes and v > 0},
-             "profiled_step_us": round(prof_step_ms * 1e3, 2),
-             "profiled_step_us_p10_p50_p90": [round(p10, 2), round(p50, 2), round(p90, 2)],
              "decode_graph_us_per_step": None if graph_us is None else round(graph_us, 2),
              "decode_warm": {"us_per_step": round(sec_warm * 1e6, 2),
                              "gbs": round(decode_bytes(w, uniq[0], 1) / sec_warm / 1e9, 1),
                              "tokens_per_s": round(1.0 / sec_warm, 1),
                              "note": "one weight copy, resident in the 256 MB last-level cache"}}
 
-    # ---------------- decode T=16 / T=64 (same weights, more tokens) ----------------
+    # ---------------- decode T=2..64 (same weights, more tokens) ----------------
     if not args.no_extra_decode:
         wts_tiled = None
         for T in (2, 4, 16, 64):
             xs_t = [x_dev(w, range(100 + r * T, 100 + (r + 1) * T), dev) for r in range(R)]
-            out_t = [torch.empty((T, w.H), dtype=torch.bfloat16, device=dev) for _ in range(R)]
-            ids_t = [torch.empty((T, w.K), dtype=torch.int32, device=dev) for _ in range(R)]
-            ws_t = capi.workspace(cfg, T, False, dev)
             wts_t = wts
             if T >= 64:
                 # from 64 tokens decode runs the grouped GEMM, which reads the
@@ -453,58 +565,74 @@ def main():
                 if wts_tiled is None:
                     wts_tiled = [capi.with_tiled_weights(x) for x in wts]
                 wts_t = wts_tiled
-
-            calls_t = [capi.bind_layer(cfg, wts_t[r], xs_t[r], out_t[r], ids_t[r], ws=ws_t) for r in range(R)]
-
-            def step_t(i):
-                calls_t[i % R]()
-
-            for i in range(10):
-                step_t(i)
-            n = max(20, args.steps // 4)
-            s_t = run_decode_steps(step_t, n)
-            u = [int(torch.unique(ids_t[r]).numel()) for r in range(R)]
-            b = float(np.mean([decode_bytes(w, x, T) for x in u]))
-            extra[f"decode_t{T}"] = {"gbs": round(b / s_t / 1e9, 1), "us_per_step": round(s_t * 1e6, 1),
-                                     "tokens_per_s": round(T / s_t, 1), "unique_experts": float(np.mean(u))}
+            extra[f"decode_t{T}"] = decode_line(cfg, w, wts_t, xs_t, T, dev, max(40, args.steps // 4))
             if T >= 64:
                 extra[f"decode_t{T}"]["weights"] = "routed NVFP4 in the tile layout (grouped-GEMM form)"
-            del calls_t, xs_t, out_t, ids_t, ws_t, wts_t
         del wts_tiled
+    del calls
+    del wts[1:]
+    torch.cuda.empty_cache()
+
+    # ---------------- skewed top-16 and literal-bias decode workloads ----------------
+    if not args.no_variants:
+        RV = 4          # weight copies per variant (4 x 3.06 GB)
+        for name, T in (("skewed_decode_t64_k16", 64), ("flash_decode_t1_literal_bias", 1),
+                        ("flash_decode_t64_literal_bias", 64)):
+            wv = synth.workload(name)
+            cfgv = config_of(wv)
+            log(f"[bench] generating + uploading {name}")
+            bv = upload_routed(wv, dev)
+            wts_v = [bv] + [clone_weights(bv) for _ in range(RV - 1)]
+            if T >= 64:
+                wts_v = [capi.with_tiled_weights(x) for x in wts_v]
+            xs_v = [x_dev(wv, range(r * T, (r + 1) * T), dev) for r in range(RV)]
+            line = decode_line(cfgv, wv, wts_v, xs_v, T, dev, max(40, args.steps // 4))
+            line["workload"] = f"T={T}, K={wv.K}, E={wv.E}, bias " + (
+                "+1.0 on 8 hot experts, U(-0.1,0.1) elsewhere" if wv.hot_experts else f"U(-{wv.bias_amp}, {wv.bias_amp})")
+            if T >= 64:
+                line["weights"] = "routed NVFP4 in the tile layout (grouped-GEMM form)"
+            extra[name] = line
+            del wts_v, bv, xs_v
+            torch.cuda.empty_cache()
 
     # ---------------- prefill T=4096 ----------------
     if not args.no_prefill:
-        del calls
-        del wts[1:]
+        del wts
         torch.cuda.empty_cache()
-        wp = synth.workload("prefill_t4096")
-        cfgp = config_of(wp)
-        log(f"[bench] generating + uploading {wp.name}")
-        wt_rm = upload_routed(wp, dev)
-        # the grouped GEMM reads the routed weights in the tile layout, packed
-        # once at load (the row-major arrays stay for the GEMV forms)
-        wtp = capi.with_tiled_weights(wt_rm)
-        xp = torch.from_numpy(synth.x_rows(wp).view(np.int16)).to(dev).view(torch.bfloat16)
-        outp = torch.empty((wp.T, wp.H), dtype=torch.bfloat16, device=dev)
-        wsp = capi.workspace(cfgp, wp.T, True, dev)
-        for _ in range(3):
-            capi.moe_mlp_prefill(cfgp, wtp, xp, outp, ws=wsp)
-        n = 10
-        s_rm = run_decode_steps(lambda i: capi.moe_mlp_prefill(cfgp, wt_rm, xp, outp, ws=wsp), n)
-        s_p = run_decode_steps(lambda i: capi.moe_mlp_prefill(cfgp, wtp, xp, outp, ws=wsp), n)
-        stp = stage_times(cfgp, [wtp], [xp], [outp], True, 5, ev, wsp)
-        T, K, H, I, Is, E = wp.T, wp.K, wp.H, wp.I, wp.Is, wp.E
-        fl_routed = 2.0 * T * K * 3 * H * I
-        fl_total = fl_routed + 2.0 * T * 3 * H * Is + 2.0 * T * H * E
-        gg_ms = stp["routed_gateup"] + stp["routed_down"]
-        extra["prefill_t4096"] = {
-            "ms_per_step": round(s_p * 1e3, 3), "layer_tflops": round(fl_total / s_p / 1e12, 1),
-            "weights": "routed NVFP4 in the tile layout (packed once at load)",
-            "ms_per_step_row_major_weights": round(s_rm * 1e3, 3),
-            "grouped_gemm_tflops": round(fl_routed / (gg_ms * 1e-3) / 1e12, 1),
-            "grouped_gemm_frac_bf16_peak": round(fl_routed / (gg_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
-            "stage_us": {k: round(v * 1e3, 1) for k, v in stp.items()}}
-        del wtp, wt_rm, xp, outp, wsp
+        for pname in ("prefill_t4096", "prefill_t4096_literal_bias"):
+            wp = synth.workload(pname)
+            cfgp = config_of(wp)
+            log(f"[bench] generating + uploading {wp.name}")
+            wt_rm = upload_routed(wp, dev)
+            # the grouped GEMM reads the routed weights in the tile layout, packed
+            # once at load (the row-major arrays stay for the GEMV forms)
+            wtp = capi.with_tiled_weights(wt_rm)
+            xp = torch.from_numpy(synth.x_rows(wp).view(np.int16)).to(dev).view(torch.bfloat16)
+            outp = torch.empty((wp.T, wp.H), dtype=torch.bfloat16, device=dev)
+            wsp = capi.workspace(cfgp, wp.T, True, dev)
+            for _ in range(3):
+                capi.moe_mlp_prefill(cfgp, wtp, xp, outp, ws=wsp)
+            n = 10
+            s_rm = loop_seconds(lambda i: capi.moe_mlp_prefill(cfgp, wt_rm, xp, outp, ws=wsp), n)
+            s_p = loop_seconds(lambda i: capi.moe_mlp_prefill(cfgp, wtp, xp, outp, ws=wsp), n)
+            stp = stage_times(cfgp, [wtp], [xp], [outp], True, 8, ev, wsp)
+            T, K, H, I, Is, E = wp.T, wp.K, wp.H, wp.I, wp.Is, wp.E
+            fl_routed = 2.0 * T * K * 3 * H * I
+            fl_total = fl_routed + 2.0 * T * 3 * H * Is + 2.0 * T * H * E
+            gg_ms = stp["routed_gateup"] + stp["routed_down"]
+            rm_bytes = sum(t.numel() for t in (wt_rm.w13_q, wt_rm.w13_s, wt_rm.w2_q, wt_rm.w2_s))
+            extra[pname] = {
+                "ms_per_step": round(s_p * 1e3, 3), "layer_tflops": round(fl_total / s_p / 1e12, 1),
+                "weights": "routed NVFP4 in the tile layout (packed once at load)",
+                "resident_routed_weight_bytes": {"row_major": int(rm_bytes), "tile_layout": int(rm_bytes),
+                                                 "note": "both copies stay resident: the GEMV forms read the "
+                                                         "row-major arrays, the grouped GEMM the tile layout"},
+                "ms_per_step_row_major_weights": round(s_rm * 1e3, 3),
+                "grouped_gemm_tflops": round(fl_routed / (gg_ms * 1e-3) / 1e12, 1),
+                "grouped_gemm_frac_bf16_peak": round(fl_routed / (gg_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+                "stage_us": {k: round(v * 1e3, 1) for k, v in stp.items()}}
+            del wtp, wt_rm, xp, outp, wsp
+            torch.cuda.empty_cache()
 
         # ---------------- dense FFN variant: prefill T=4096 and one-token decode ----------------
         wd = synth.workload("dense_prefill_t4096")
@@ -523,8 +651,8 @@ def main():
         call_d = capi.bind_layer(cfgd, wtd, xd, outd, ws=wsd, prefill=True)
         for _ in range(3):
             call_d()
-        s_d = run_decode_steps(lambda i: call_d(), 10)
-        std = stage_times(cfgd, [wtd], [xd], [outd], True, 5, ev, wsd)
+        s_d = loop_seconds(lambda i: call_d(), 10)
+        std = stage_times(cfgd, [wtd], [xd], [outd], True, 8, ev, wsd)
         fl_d = 2.0 * wd.T * 3 * wd.H * wd.Id
         x1 = xd[:1].contiguous()
         out1 = torch.empty((1, wd.H), dtype=torch.bfloat16, device=dev)
@@ -532,7 +660,7 @@ def main():
         call_d1 = capi.bind_layer(cfgd, wtd, x1, out1, ws=ws1)
         for _ in range(10):
             call_d1()
-        s_d1 = run_decode_steps(lambda i: call_d1(), 200)
+        s_d1 = loop_seconds(lambda i: call_d1(), 200)
         dense_bytes = 2 * 3 * wd.H * wd.Id
         extra["dense_prefill_t4096"] = {
             "ms_per_step": round(s_d * 1e3, 3), "tflops": round(fl_d / s_d / 1e12, 1),
@@ -544,11 +672,13 @@ def main():
                     "from the 256 MB last-level cache only in part)"}
         del call_d, call_d1, wtd, xd, outd, wsd
 
-    # ---------------- CPU oracle baseline ----------------
+    # ---------------- CPU oracle baselines ----------------
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle")
-        cpu = cpu_baseline(w, args.cpu_seconds)
+        cpu = cpu_decode_baseline(w, args.cpu_seconds)
+        extra["cpu_baseline_1_blas_thread"] = cpu_decode_baseline(w, args.cpu_seconds / 2, blas_threads=1)
+        extra["cpu_baseline_prefill_t4096"] = cpu_prefill_baseline(synth.workload("prefill_t4096"), 8)
 
     rec = {
         "metric": "MoE-MLP decode weight GB/s (% HBM peak) + tokens/s; prefill TFLOP/s",
@@ -568,11 +698,14 @@ def main():
                    "tokens": 1, "hidden": w.H, "moe_intermediate": w.I, "experts": w.E, "top_k": w.K,
                    "weights": "nvfp4 (e2m1 + e4m3/16) routed, bf16 shared, fp32 router",
                    "weight_copies_rotated": R},
-        "roofline": {"bound": "hbm", "kernel": "routed_gateup (k_dec_gateup: router top-k, NVFP4 gate/up + clamped SwiGLU)",
-                     "achieved": round(gu_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(gu_gbs / HBM_PEAK_GBS, 4), "avg_launch_us": round(gu_ms * 1e3, 3),
-                     "algorithmic_bytes_per_launch": int(gu_bytes),
-                     "traffic": None if traffic is None else int(traffic)},
+        "roofline": {"bound": "hbm",
+                     "kernel": "routed_gateup (k_dec_gateup: router top-k, NVFP4 gate/up + clamped SwiGLU)",
+                     "achieved": round(dom_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(dom_gbs / HBM_PEAK_GBS, 4), "avg_launch_us": round(dom_ms * 1e3, 3),
+                     "algorithmic_bytes_per_launch": int(dom_bytes),
+                     "traffic": None if traffic is None else int(traffic),
+                     "measured_copy_gbs": None if copy_gbs is None else round(copy_gbs, 1),
+                     "measured_copy_note": "1 GiB device-to-device copy, read + write bytes over its time"},
         "cpu_baseline": cpu,
     }
     rec.update(extra)

@@ -30,17 +30,32 @@ namespace moe {
 // Lane l of a wavefront covers chunks l, l+64, ..., of a row (one coalesced
 // 1 KB load per instruction); a chunk is 16 bytes.
 
+// Layer geometry of the decode kernels: compile-time constants (a kernel
+// instance for one layer shape; the selection and index arithmetic fold) or
+// 0 = taken from the kernel arguments (IS: -1).
+template <int H_, int I_, int E_, int K_, int IS_>
+struct DecGeo {
+  static constexpr int H = H_, I = I_, E = E_, K = K_, IS = IS_;
+};
+using DecGeoAny = DecGeo<0, 0, 0, 0, -1>;
+
+
 // -------------------------------------------------------------------------
 // 1. logits + shared gate/up.  Blocks [0, n_logit_blocks) take 4 router rows
 // each (one per wavefront), the rest take 4 shared (gate, up) row pairs.
 //   NR: float4 chunks per lane of a router row (>= H / 256)
 //   NS: 8-bf16 chunks per lane of a shared row (>= H / 512)
 // -------------------------------------------------------------------------
-template <int NR, int NS>
+template <int NR, int NS, class G>
 __global__ __launch_bounds__(256) void k_dec_logits_shared(const uint16_t* __restrict__ x,
                                                            const float* __restrict__ wr, float* __restrict__ logits,
-                                                           int E, int H, const uint16_t* __restrict__ sw13, int Is,
+                                                           int E_, int H_, const uint16_t* __restrict__ sw13, int Is_,
                                                            uint16_t* __restrict__ hs, float L, int n_logit_blocks) {
+  const int E = G::E ? G::E : E_, H = G::H ? G::H : H_;
+  const int Is = G::IS >= 0 ? G::IS : Is_;
+  // with the geometry compiled in and rows of exactly 64 NR float4 / 64 NS
+  // 8-bf16 chunks, no load needs a lane guard
+  constexpr bool EXACT_R = G::H == 256 * NR, EXACT_S = G::H == 512 * NS;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   if (static_cast<int>(blockIdx.x) < n_logit_blocks) {
     const int e = blockIdx.x * 4 + wv;
@@ -53,8 +68,8 @@ __global__ __launch_bounds__(256) void k_dec_logits_shared(const uint16_t* __res
 #pragma unroll
     for (int i = 0; i < NR; ++i) {
       const int c = lane + 64 * i;
-      w[i] = c < nch ? row[c] : make_float4(0, 0, 0, 0);
-      xs[i] = c < nch ? xv[c] : make_uint2(0, 0);
+      w[i] = (EXACT_R || c < nch) ? row[c] : make_float4(0, 0, 0, 0);
+      xs[i] = (EXACT_R || c < nch) ? xv[c] : make_uint2(0, 0);
     }
     float acc = 0.0f;
 #pragma unroll
@@ -77,7 +92,7 @@ __global__ __launch_bounds__(256) void k_dec_logits_shared(const uint16_t* __res
 #pragma unroll
     for (int i = 0; i < NS; ++i) {
       const int c = lane + 64 * i;
-      const bool ok = c < nch;
+      const bool ok = EXACT_S || c < nch;
       wg[i] = ok ? g[c] : make_uint4(0, 0, 0, 0);
       wu[i] = ok ? u[c] : make_uint4(0, 0, 0, 0);
       xs[i] = ok ? xv[c] : make_uint4(0, 0, 0, 0);
@@ -175,15 +190,6 @@ __global__ __launch_bounds__(256) void k_dec_logits_shared_t(const uint16_t* __r
     }
   }
 }
-
-// Layer geometry of the decode kernels: compile-time constants (a kernel
-// instance for one layer shape; the selection and index arithmetic fold) or
-// 0 = taken from the kernel arguments (IS: -1).
-template <int H_, int I_, int E_, int K_, int IS_>
-struct DecGeo {
-  static constexpr int H = H_, I = I_, E = E_, K = K_, IS = IS_;
-};
-using DecGeoAny = DecGeo<0, 0, 0, 0, -1>;
 
 // -------------------------------------------------------------------------
 // 2. top-k + routed gate/up for T tokens (T*K slots, slot = t*K + k).  1-D

@@ -464,9 +464,12 @@ void decode1(const moe_mlp_config* c, const moe_mlp_weights* w, const uint16_t* 
   const int H = c->hidden, E = c->num_experts, K = c->top_k;
   const int Is = c->n_shared_experts ? c->shared_intermediate : 0;
   const int nlb = static_cast<int>(cdiv(E, 4)), nsb = static_cast<int>(cdiv(Is, 4));
-  if (T == 1)
-    launch(k_dec_logits_shared<16, 8>, dim3(nlb + nsb), dim3(256), s, e0.a, e0.b, x, w->router_w, logits, E, H,
-           w->shared_w13, Is, hs, c->swiglu_limit, nlb);
+  if (T == 1 && glm_flash_geometry(c))
+    launch(k_dec_logits_shared<16, 8, DecGeoFlash>, dim3(nlb + nsb), dim3(256), s, e0.a, e0.b, x, w->router_w, logits,
+           E, H, w->shared_w13, Is, hs, c->swiglu_limit, nlb);
+  else if (T == 1)
+    launch(k_dec_logits_shared<16, 8, DecGeoAny>, dim3(nlb + nsb), dim3(256), s, e0.a, e0.b, x, w->router_w, logits,
+           E, H, w->shared_w13, Is, hs, c->swiglu_limit, nlb);
   else
     launch(k_dec_logits_shared_t<16, 8>, dim3(nlb + nsb), dim3(256), s, e0.a, e0.b, x, w->router_w, logits, E, H,
            w->shared_w13, Is, hs, c->swiglu_limit, nlb, T);
