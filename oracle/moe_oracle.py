@@ -46,6 +46,11 @@ Readings where the pages are silent:
     neither;
   * NVFP4 layout: [out, in] row-major, low nibble = even column, unswizzled
     scales [out, in/16].
+  * FP8 experts (the second checkpoint format of the TensorRT-LLM
+    GLM-5.3-Flash page, "the official FP8 checkpoint", which gives no
+    layout): E4M3 ("fn") bytes [out, in] row-major and one fp32 scale per
+    128 x 128 block [out/128, in/128], multiplied; no global scale; bf16
+    activations (W8A16).
 
 Parity pins: every function here is pinned by a CPU test against hand
 tables, closed forms, brute force or a library routine (tests/test_oracle_*).
@@ -147,6 +152,32 @@ def nvfp4_linear(x, q, s, g) -> np.ndarray:
     return float(g) * (np.asarray(x, dtype=F64) @ W.T)
 
 
+FP8_BLOCK = 128
+
+
+def dequant_fp8_block(q, s, block: int = FP8_BLOCK) -> np.ndarray:
+    """FP8 block-scaled weight W[r, c] = E4M3(q[r, c]) * S[r // 128, c // 128], exact in fp64.
+
+    q [rows, cols] holds OCP E4M3 ("fn") bytes; S [rows/128, cols/128] one
+    fp32 scale per 128 x 128 block, multiplied (see the FP8 reading in the
+    module docstring).
+    """
+    q = np.asarray(q, dtype=np.uint8)
+    rows, cols = q.shape
+    s = np.asarray(s, dtype=F64)
+    nb = (-(-rows // block), -(-cols // block))
+    if s.shape != nb:
+        raise ValueError(f"scale shape must be {nb}")
+    vals = decode_e4m3(np.arange(256))[q]
+    scl = np.repeat(np.repeat(s, block, axis=0)[:rows], block, axis=1)[:, :cols]
+    return vals * scl
+
+
+def fp8_linear(x, q, s) -> np.ndarray:
+    """y[n, r] = sum_c x[n, c] * W[r, c] for an FP8 block-scaled weight (W8A16 projection)."""
+    return np.asarray(x, dtype=F64) @ dequant_fp8_block(q, s).T
+
+
 def bf16_linear(x, w_bits) -> np.ndarray:
     """y[n, r] = sum_c x[n, c] * W[r, c] for a bf16 weight [rows, cols]."""
     return np.asarray(x, dtype=F64) @ decode_bf16(w_bits).T
@@ -233,6 +264,22 @@ def routed_expert(x, q13, s13, g13, q2, s2, g2, limit, mode="contract") -> np.nd
     return nvfp4_linear(h, q2, s2, g2)
 
 
+def routed_expert_fp8(x, q13, s13, q2, s2, limit, mode="contract") -> np.ndarray:
+    """One routed FP8 block-scaled expert on rows x [n, H] -> y [n, H].
+
+    gate/up = rows [0, I) and [I, 2I) of W13 (scales over the stacked
+    [2I, H] matrix); h = clamped SwiGLU (bf16 in contract mode);
+    y = W2 . h.  No per-expert global scale: the block scales carry it.
+    """
+    W13 = dequant_fp8_block(q13, s13)
+    I = W13.shape[0] // 2
+    a = np.asarray(x, dtype=F64) @ W13.T
+    h = swiglu_clamped(a[:, :I], a[:, I:], limit)
+    if mode == "contract":
+        h = round_bf16(h)
+    return fp8_linear(h, q2, s2)
+
+
 def bf16_mlp(x, w13_bits, w2_bits, limit, mode="contract") -> np.ndarray:
     """BF16 gate/up -> clamped SwiGLU -> BF16 down (shared expert, dense FFN).
 
@@ -257,10 +304,15 @@ class RoutedWeights:
     router_w [E, H] fp32; router_bias [E] fp32; w13_g [E, 2] fp32;
     w2_g [E] fp32; shared_w13 [2 Is, H] and shared_w2 [H, Is] bf16 bits (or
     None when there is no shared expert); expert(e) -> (q13, s13, q2, s2)
-    returns expert e's NVFP4 codes and scales.
+    returns expert e's weights: NVFP4 codes and E4M3 scales (fmt "nvfp4"),
+    or E4M3 bytes and fp32 128 x 128 block scales (fmt "fp8", which has no
+    global scales: w13_g / w2_g are not used).
     """
 
-    def __init__(self, router_w, router_bias, w13_g, w2_g, expert, shared_w13=None, shared_w2=None):
+    def __init__(self, router_w, router_bias, w13_g, w2_g, expert, shared_w13=None, shared_w2=None,
+                 fmt="nvfp4"):
+        if fmt not in ("nvfp4", "fp8"):
+            raise ValueError(f"unknown expert format {fmt!r}")
         self.router_w = router_w
         self.router_bias = router_bias
         self.w13_g = w13_g
@@ -268,14 +320,17 @@ class RoutedWeights:
         self.expert = expert
         self.shared_w13 = shared_w13
         self.shared_w2 = shared_w2
+        self.fmt = fmt
 
 
 def expert_rows(job):
     """One chosen expert on the rows routed to it: job = (expert source, e,
-    x rows, gate/up globals, down global, limit, mode) -> routed_expert's
-    output for those rows."""
-    expert, e, xr, g13, g2, limit, mode = job
+    x rows, gate/up globals, down global, limit, mode, format) -> the
+    expert's output for those rows (routed_expert or routed_expert_fp8)."""
+    expert, e, xr, g13, g2, limit, mode, fmt = job
     q13, s13, q2, s2 = expert(e)
+    if fmt == "fp8":
+        return routed_expert_fp8(xr, q13, s13, q2, s2, limit, mode)
     return routed_expert(xr, q13, s13, g13, q2, s2, g2, limit, mode)
 
 
@@ -301,7 +356,7 @@ def moe_layer(x_bits, wts: RoutedWeights, k: int, rsf: float, limit: float, mode
     y = np.zeros((n, k, H), dtype=F64)
     chosen = [int(e) for e in np.unique(ids)]
     where = [np.nonzero(ids == e) for e in chosen]
-    jobs = [(wts.expert, e, x[rows], wts.w13_g[e], wts.w2_g[e], limit, mode)
+    jobs = [(wts.expert, e, x[rows], wts.w13_g[e], wts.w2_g[e], limit, mode, wts.fmt)
             for e, (rows, _) in zip(chosen, where)]
     for (rows, slots), ye in zip(where, map_fn(expert_rows, jobs)):
         y[rows, slots] = ye

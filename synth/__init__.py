@@ -45,7 +45,7 @@ __all__ = [
     "expert_w13", "expert_w2", "w13_globals", "w2_globals",
     "router_weight", "router_bias", "shared_w13", "shared_w2",
     "dense_w13", "dense_w2", "x_row", "x_rows", "unit_normal_rows",
-    "for_each_expert", "SHARED_SIGMA",
+    "for_each_expert", "SHARED_SIGMA", "FP8_CODE_SIGMA", "fp8_code_table",
 ]
 
 # Stream ids: one per tensor kind.  Never renumber (it changes every input).
@@ -62,6 +62,10 @@ _TID_DENSE_W13 = 10
 _TID_DENSE_W2 = 11
 _TID_HOT = 12
 _TID_X_UNIT = 13
+_TID_W13_F8Q = 14
+_TID_W13_F8S = 15
+_TID_W2_F8Q = 16
+_TID_W2_F8S = 17
 
 _ROW_CHUNK = 256          # rows per stream for the large BF16 matrices
 SCALE_STD = 0.05          # e4m3 block scale = |N(0,1)| * SCALE_STD
@@ -147,13 +151,17 @@ class Workload:
     kind: str = "routed"        # "routed" or "dense"
     Id: int = 0                 # dense FFN intermediate (kind == "dense")
     prefill: bool = False       # which entry point the workload exercises
+    fmt: str = "nvfp4"          # routed expert weights: "nvfp4" or "fp8" (128 x 128 block scales)
 
     def with_(self, **kw) -> "Workload":
         return dataclasses.replace(self, **kw)
 
     @property
     def expert_bytes(self) -> int:
-        """NVFP4 bytes of one routed expert (codes + e4m3 scales, both projections)."""
+        """Bytes of one routed expert, both projections: NVFP4 codes + e4m3 scales, or FP8
+        bytes + fp32 block scales."""
+        if self.fmt == "fp8":
+            return 3 * self.I * self.H + 4 * 3 * (self.I // 128) * (self.H // 128)
         return 3 * self.I * self.H // 2 + 3 * self.I * self.H // 16
 
 
@@ -192,6 +200,21 @@ for _n in ("flash_decode_t1", "flash_decode_t16", "flash_decode_t64", "prefill_t
     _add(_w.with_(name=_n + "_literal_bias", seed=_w.seed + 100, bias_amp=0.1))
 
 
+# FP8 block-scaled experts (E4M3 weights, one fp32 scale per 128 x 128
+# block): the GLM-Flash shapes, and small shapes whose H and I are multiples
+# of the 128-wide scale blocks but not of the GEMM tiles.
+for _n in ("flash_decode_t1", "flash_decode_t16", "prefill_t4096"):
+    _w = WORKLOADS[_n]
+    _add(_w.with_(name=_n + "_fp8", seed=_w.seed + 200, fmt="fp8"))
+_X_SCALE_H384 = X_SCALE_H256 * math.sqrt(256 / 384)
+_add(Workload("tiny_decode_fp8", T=1, H=256, I=128, E=16, K=4, Is=128, seed=1200,
+              x_scale=X_SCALE_H256, bias_amp=0.1, fmt="fp8"))
+_add(Workload("ragged_prefill_fp8", T=700, H=384, I=256, E=8, K=2, Is=128, seed=2201,
+              x_scale=_X_SCALE_H384, bias_amp=0.05, prefill=True, fmt="fp8"))
+_add(Workload("ragged_decode_fp8", T=40, H=384, I=256, E=8, K=2, Is=128, seed=2202,
+              x_scale=_X_SCALE_H384, bias_amp=0.05, fmt="fp8"))
+
+
 # Small parity workloads that still span several GEMM tiles and ragged tails:
 # H = 416 and I = 160 are not multiples of the 128-wide k blocks and output
 # tiles; T*K/E = 250 rows per expert crosses the 128-row M tiles.
@@ -219,13 +242,45 @@ def _nvfp4_matrix(seed: int, tid_q: int, tid_s: int, e: int, rows: int, cols: in
     return q, s
 
 
+# FP8 expert weights: the E4M3 byte of each weight is one of the 256
+# equiprobable quantiles of N(0, FP8_CODE_SIGMA^2) (rounded to E4M3), picked
+# by a uniform byte, so a 128 x 128 block spans most of the E4M3 range as a
+# max-scaled block would; each block's fp32 scale is
+# (SHARED_SIGMA / FP8_CODE_SIGMA) * U(0.5, 1.5), which keeps the RMS weight
+# near that of an NVFP4 expert.
+FP8_CODE_SIGMA = 64.0
+_FP8_TABLE: Optional[np.ndarray] = None
+
+
+def fp8_code_table() -> np.ndarray:
+    global _FP8_TABLE
+    if _FP8_TABLE is None:
+        from statistics import NormalDist
+        v = np.array([NormalDist().inv_cdf((i + 0.5) / 256.0) for i in range(256)]) * FP8_CODE_SIGMA
+        _FP8_TABLE = (encode_e4m3(np.abs(v)) | np.where(v < 0, 0x80, 0).astype(np.uint8)).astype(np.uint8)
+    return _FP8_TABLE
+
+
+def _fp8_matrix(seed: int, tid_q: int, tid_s: int, e: int, rows: int, cols: int):
+    if rows % 128 or cols % 128:
+        raise ValueError("FP8 experts need rows and cols that are multiples of 128")
+    q = fp8_code_table()[_rng(seed, tid_q, e).integers(0, 256, size=(rows, cols), dtype=np.uint8)]
+    s = (SHARED_SIGMA / FP8_CODE_SIGMA) * (0.5 + _rng(seed, tid_s, e).random((rows // 128, cols // 128)))
+    return q, s.astype(np.float32)
+
+
 def expert_w13(w: Workload, e: int) -> Tuple[np.ndarray, np.ndarray]:
-    """Gate/up of expert e: rows [0, I) gate, [I, 2I) up; cols = H."""
+    """Gate/up of expert e: rows [0, I) gate, [I, 2I) up; cols = H.  NVFP4 (codes, e4m3
+    scales) or FP8 (e4m3 bytes, fp32 128 x 128 block scales) by w.fmt."""
+    if w.fmt == "fp8":
+        return _fp8_matrix(w.seed, _TID_W13_F8Q, _TID_W13_F8S, e, 2 * w.I, w.H)
     return _nvfp4_matrix(w.seed, _TID_W13_Q, _TID_W13_S, e, 2 * w.I, w.H)
 
 
 def expert_w2(w: Workload, e: int) -> Tuple[np.ndarray, np.ndarray]:
-    """Down projection of expert e: rows = H, cols = I."""
+    """Down projection of expert e: rows = H, cols = I (format by w.fmt)."""
+    if w.fmt == "fp8":
+        return _fp8_matrix(w.seed, _TID_W2_F8Q, _TID_W2_F8S, e, w.H, w.I)
     return _nvfp4_matrix(w.seed, _TID_W2_Q, _TID_W2_S, e, w.H, w.I)
 
 

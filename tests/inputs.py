@@ -54,7 +54,7 @@ class RoutedInputs:
 
     def oracle_weights(self):
         return O.RoutedWeights(self.router_w, self.router_bias, self.w13_g, self.w2_g, self.expert,
-                               self.shared_w13, self.shared_w2)
+                               self.shared_w13, self.shared_w2, fmt=self.w.fmt)
 
     def oracle(self, tokens=None, mode="contract", parallel=False):
         """The oracle's layer output on these inputs.  parallel=True runs the
@@ -64,6 +64,6 @@ class RoutedInputs:
                                mode=mode, tokens=tokens)
         from oracle_pool import SynthExpert, pool_map
         wts = O.RoutedWeights(self.router_w, self.router_bias, self.w13_g, self.w2_g, SynthExpert(self.w),
-                              self.shared_w13, self.shared_w2)
+                              self.shared_w13, self.shared_w2, fmt=self.w.fmt)
         return O.moe_layer(self.x, wts, self.w.K, self.w.rsf, self.w.swiglu_limit, mode=mode, tokens=tokens,
                            map_fn=pool_map)

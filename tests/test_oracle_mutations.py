@@ -6,6 +6,7 @@ import pytest
 import oracle
 import oracle.moe_oracle as M
 import test_oracle_formats as TF
+import test_oracle_fp8 as TF8
 import test_oracle_layer as TL
 import test_oracle_router as TR
 
@@ -92,7 +93,37 @@ def _no_global_after_dot(x, q, s, g):
     return np.asarray(x, np.float64) @ M.dequant_nvfp4(q, s).T
 
 
+def _fp8_scale_transposed(q, s, block=128):
+    return _orig_dequant_fp8(q, np.asarray(s).T, block)
+
+
+def _fp8_scale_per_row_block(q, s, block=128):
+    s = np.asarray(s, np.float64)
+    return _orig_dequant_fp8(q, np.repeat(s[:, :1], s.shape[1], axis=1), block)
+
+
+_orig_dequant_fp8 = M.dequant_fp8_block
+_orig_routed_expert_fp8 = M.routed_expert_fp8
+
+
+def _routed_expert_fp8_swapped(x, q13, s13, q2, s2, limit, mode="contract"):
+    q13, s13 = np.asarray(q13), np.asarray(s13)
+    I, Ib = q13.shape[0] // 2, s13.shape[0] // 2
+    return _orig_routed_expert_fp8(x, np.concatenate([q13[I:], q13[:I]]), np.concatenate([s13[Ib:], s13[:Ib]]),
+                                   q2, s2, limit, mode)
+
+
+def _expert_rows_ignores_format(job):
+    expert, e, xr, g13, g2, limit, mode, fmt = job
+    q13, s13, q2, s2 = expert(e)
+    return M.routed_expert(xr, q13, s13, g13, q2, s2, g2, limit, mode)
+
+
 MUTATIONS = [
+    ("dequant_fp8_block", _fp8_scale_transposed, [TF8.test_fp8_block_index]),
+    ("dequant_fp8_block", _fp8_scale_per_row_block, [TF8.test_fp8_block_index]),
+    ("routed_expert_fp8", _routed_expert_fp8_swapped, [TF8.test_fp8_expert_closed_form]),
+    ("expert_rows", _expert_rows_ignores_format, [TF8.test_fp8_layer_equals_dense_routing_matrix_formulation]),
     ("unpack_codes", _unpack_swapped, [TF.test_nibble_order_and_block_index]),
     ("decode_e4m3", _e4m3_bias8, [TF.test_e4m3_samples_match_hand_table]),
     ("dequant_nvfp4", _dequant_scale_per_row_block, [TF.test_nibble_order_and_block_index]),
