@@ -86,6 +86,9 @@ extern "C" {
 
 #define MOE_MLP_KIND_ROUTED 0   /* router + routed NVFP4 experts + optional shared expert */
 #define MOE_MLP_KIND_DENSE  1   /* dense BF16 FFN (layers before first_k_dense_replace) */
+#define MOE_MLP_KIND_ROUTED_FP8 2 /* router + routed FP8 block-scaled experts + optional shared expert
+                                     (H and I multiples of MOE_MLP_FP8_BLOCK) */
+#define MOE_MLP_FP8_BLOCK   128 /* FP8 expert weights: one fp32 scale per 128 x 128 block */
 
 /*
  * Layer geometry and constants.  Every field is read from the caller; none
@@ -93,7 +96,7 @@ extern "C" {
  * checkpoint's own config and is never filled in by the library).
  */
 typedef struct moe_mlp_config {
-  int32_t kind;                  /* MOE_MLP_KIND_ROUTED or MOE_MLP_KIND_DENSE */
+  int32_t kind;                  /* MOE_MLP_KIND_ROUTED, _DENSE or _ROUTED_FP8 */
   int32_t hidden;                /* H; multiple of 32 */
   int32_t moe_intermediate;      /* I, routed experts; multiple of 32 (ROUTED) */
   int32_t num_experts;           /* E, the FULL expert count; 1..MOE_MLP_MAX_EXPERTS (ROUTED) */
@@ -133,6 +136,15 @@ typedef struct moe_mlp_weights {
   const uint8_t*  w13_s_tiled;  /* ... and scales */
   const uint8_t*  w2_q_tiled;   /* moe_nvfp4_tile_pack(w2_q, w2_s, E, H, I, ...) codes */
   const uint8_t*  w2_s_tiled;   /* ... and scales */
+  /* MOE_MLP_KIND_ROUTED_FP8 experts (the FP8 checkpoint named on the
+   * TensorRT-LLM page "Add GLM-5.3-Flash (glm5_next) support"; NULL for the
+   * other kinds): OCP E4M3 ("fn") bytes [out, in] row-major and one fp32
+   * scale per 128 x 128 block, W = e4m3 * scale; no global scale (w13_g /
+   * w2_g and the NVFP4 fields are not read). */
+  const uint8_t*  w13_f8;       /* [E, 2I, H] E4M3; rows [0,I) gate, [I,2I) up */
+  const float*    w13_f8_scale; /* [E, 2I/128, H/128] fp32 */
+  const uint8_t*  w2_f8;        /* [E, H, I] E4M3 */
+  const float*    w2_f8_scale;  /* [E, H/128, I/128] fp32 */
 } moe_mlp_weights;
 
 /*
@@ -229,8 +241,8 @@ const char* moe_mlp_stage_name(const moe_mlp_config* cfg, int64_t T, int prefill
  * selection and weight rules of "Traps this module exists to hold"):
  * logits = x . router_w^T (fp32), sigmoid scores, top-K of score + bias,
  * weights = rsf * score / sum of chosen scores.
- * Uses cfg->kind == ROUTED fields hidden, num_experts, top_k and
- * routed_scaling_factor.  ids [T, K] int32, w [T, K] fp32 (both required).
+ * Uses the routed config fields hidden, num_experts, top_k and
+ * routed_scaling_factor (kind ROUTED or ROUTED_FP8).  ids [T, K] int32, w [T, K] fp32 (both required).
  * Workspace: moe_mlp_workspace_size(cfg, T, 1) bytes (prefill sizing).
  */
 int moe_router_topk(const moe_mlp_config* cfg, const float* router_w, const float* router_bias,

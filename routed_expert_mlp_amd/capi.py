@@ -36,6 +36,8 @@ DECODE_MAX_T = 256
 NOALLOC_SCRATCH_BYTES = 32 << 20
 KIND_ROUTED = 0
 KIND_DENSE = 1
+KIND_ROUTED_FP8 = 2
+FP8_BLOCK = 128
 
 EXPORTED = ("moe_mlp_workspace_size", "moe_mlp_decode", "moe_mlp_prefill", "moe_mlp_forward_profiled",
             "moe_mlp_stage_name", "moe_router_topk", "moe_nvfp4_dequant", "moe_nvfp4_tile_pack",
@@ -59,7 +61,8 @@ class moe_mlp_weights(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
         "router_w", "router_bias", "w13_q", "w13_s", "w13_g", "w2_q", "w2_s", "w2_g",
         "shared_w13", "shared_w2", "dense_w13", "dense_w2",
-        "w13_q_tiled", "w13_s_tiled", "w2_q_tiled", "w2_s_tiled")]
+        "w13_q_tiled", "w13_s_tiled", "w2_q_tiled", "w2_s_tiled",
+        "w13_f8", "w13_f8_scale", "w2_f8", "w2_f8_scale")]
 
 
 _LIB = None
@@ -147,14 +150,27 @@ class Weights:
     w13_s_tiled: Optional[torch.Tensor] = None   # [E, 2I, H/16] u8
     w2_q_tiled: Optional[torch.Tensor] = None    # [E, H, I/2] u8
     w2_s_tiled: Optional[torch.Tensor] = None    # [E, H, I/16] u8
+    # FP8 block-scaled experts (KIND_ROUTED_FP8): E4M3 bytes and fp32 128 x 128 block scales
+    w13_f8: Optional[torch.Tensor] = None        # [E, 2I, H] u8
+    w13_f8_scale: Optional[torch.Tensor] = None  # [E, 2I/128, H/128] f32
+    w2_f8: Optional[torch.Tensor] = None         # [E, H, I] u8
+    w2_f8_scale: Optional[torch.Tensor] = None   # [E, H/128, I/128] f32
 
     def check(self, cfg: Config) -> None:
         H, I, E = cfg.hidden, cfg.moe_intermediate, cfg.num_experts
         Is, Id = cfg.shared_intermediate, cfg.dense_intermediate
         want = {}
+        B = FP8_BLOCK
         if cfg.kind == KIND_DENSE:
             want["dense_w13"] = ((2 * Id, H), torch.bfloat16)
             want["dense_w2"] = ((H, Id), torch.bfloat16)
+        elif cfg.kind == KIND_ROUTED_FP8:
+            want.update(router_w=((E, H), torch.float32), router_bias=((E,), torch.float32),
+                        w13_f8=((E, 2 * I, H), torch.uint8), w13_f8_scale=((E, 2 * I // B, H // B), torch.float32),
+                        w2_f8=((E, H, I), torch.uint8), w2_f8_scale=((E, H // B, I // B), torch.float32))
+            if cfg.n_shared_experts:
+                want["shared_w13"] = ((2 * Is, H), torch.bfloat16)
+                want["shared_w2"] = ((H, Is), torch.bfloat16)
         else:
             want.update(router_w=((E, H), torch.float32), router_bias=((E,), torch.float32),
                         w13_q=((E, 2 * I, H // 2), torch.uint8), w13_s=((E, 2 * I, H // 16), torch.uint8),

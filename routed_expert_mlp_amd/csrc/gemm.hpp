@@ -47,6 +47,8 @@ struct GemmArgs {
   const uint16_t* bb;        // BF16 weights [rows][kdim]
   const uint8_t* bq_t;       // NVFP4 codes and scales in the tile layout (tile
   const uint8_t* bs_t;       //   kernel only; null = read bq / bs)
+  const float* bsf;          // FP8 experts: fp32 128 x 128 block scales [E][rows/128][kdim/128]
+                             //   (bq then holds E4M3 bytes [E][rows][kdim])
   int64_t stride_q, stride_s;
   const float* gscale;       // routed globals (gate/up: [E,2]; down: [E]); null = 1
   int half_n;                // gate/up: I (gate rows, up rows = I + j); down: output columns

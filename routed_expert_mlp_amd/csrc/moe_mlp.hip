@@ -17,9 +17,11 @@
 #include "../../include/moe_mlp.h"
 #include "common.hpp"
 #include "decode1.hpp"
+#include "decode_fp8.hpp"
 #include "gemm.hpp"
 #include "gemm_bf16.hpp"
 #include "gemm_fp4.hpp"
+#include "gemm_fp8.hpp"
 #include "gemv.hpp"
 #include "permute.hpp"
 #include "router.hpp"
@@ -43,9 +45,12 @@ bool finite_pos(float v) { return std::isfinite(v) && v > 0.0f; }
 bool aligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool bad_dim(int64_t d) { return d <= 0 || d % 32 != 0 || d > kMaxDim; }
 
+bool is_fp8(const moe_mlp_config* c) { return c->kind == MOE_MLP_KIND_ROUTED_FP8; }
+bool is_routed(const moe_mlp_config* c) { return c->kind == MOE_MLP_KIND_ROUTED || is_fp8(c); }
+
 int validate_cfg(const moe_mlp_config* c, int64_t T, int prefill) {
   if (!c) return MOE_MLP_ERR_NULL_ARG;
-  if (c->kind != MOE_MLP_KIND_ROUTED && c->kind != MOE_MLP_KIND_DENSE) return MOE_MLP_ERR_BAD_VALUE;
+  if (!is_routed(c) && c->kind != MOE_MLP_KIND_DENSE) return MOE_MLP_ERR_BAD_VALUE;
   if (T < 0 || (!prefill && T > MOE_MLP_DECODE_MAX_T)) return MOE_MLP_ERR_BAD_SHAPE;
   if (bad_dim(c->hidden)) return MOE_MLP_ERR_BAD_SHAPE;
   if (!finite_pos(c->swiglu_limit)) return MOE_MLP_ERR_BAD_VALUE;
@@ -54,6 +59,8 @@ int validate_cfg(const moe_mlp_config* c, int64_t T, int prefill) {
     return MOE_MLP_OK;
   }
   if (bad_dim(c->moe_intermediate)) return MOE_MLP_ERR_BAD_SHAPE;
+  if (is_fp8(c) && (c->hidden % MOE_MLP_FP8_BLOCK != 0 || c->moe_intermediate % MOE_MLP_FP8_BLOCK != 0))
+    return MOE_MLP_ERR_BAD_SHAPE;
   if (c->n_shared_experts != 0 && c->n_shared_experts != 1) return MOE_MLP_ERR_BAD_VALUE;
   if (c->n_shared_experts == 1 && bad_dim(c->shared_intermediate)) return MOE_MLP_ERR_BAD_SHAPE;
   if (c->num_experts < 1 || c->num_experts > MOE_MLP_MAX_EXPERTS) return MOE_MLP_ERR_BAD_VALUE;
@@ -92,8 +99,10 @@ struct Alloc {
 // overtakes the GEMVs from T = 64, by 2.2x at T = 256).
 constexpr int64_t kDecodeGemmMinT = 64;
 
+// FP8 experts have no expert-GEMV decode path: past the few-token kernels
+// their decode runs the grouped GEMM.
 int gemm_form(const moe_mlp_config* c, int64_t T, int prefill) {
-  return (prefill || T >= kDecodeGemmMinT) ? 1 : 0;
+  return (prefill || T >= kDecodeGemmMinT || is_fp8(c)) ? 1 : 0;
 }
 
 // Prefill router logits on the matrix cores (split fp32 weight, see router.hpp)
@@ -163,6 +172,17 @@ int validate_weights(const moe_mlp_config* c, const moe_mlp_weights* w) {
   if (c->kind == MOE_MLP_KIND_DENSE) {
     need[n++] = w->dense_w13;
     need[n++] = w->dense_w2;
+  } else if (is_fp8(c)) {
+    need[n++] = w->router_w;
+    need[n++] = w->router_bias;
+    need[n++] = w->w13_f8;
+    need[n++] = w->w13_f8_scale;
+    need[n++] = w->w2_f8;
+    need[n++] = w->w2_f8_scale;
+    if (c->n_shared_experts) {
+      need[n++] = w->shared_w13;
+      need[n++] = w->shared_w2;
+    }
   } else {
     need[n++] = w->router_w;
     need[n++] = w->router_bias;
@@ -387,7 +407,7 @@ constexpr int64_t kDecFewMaxT = 4;
 static_assert(kDecFewMaxT <= DEC_MAX_T, "k_dec_down_combine keeps the shared rows' sums of DEC_MAX_T tokens");
 
 bool decode1_ok(const moe_mlp_config* c, int64_t T, int prefill) {
-  if (prefill || T < 1 || T > kDecFewMaxT || c->kind != MOE_MLP_KIND_ROUTED) return false;
+  if (prefill || T < 1 || T > kDecFewMaxT || !is_routed(c)) return false;
   if (T * c->top_k > 64) return false;
   const int Is = c->n_shared_experts ? c->shared_intermediate : 0;
   return c->hidden <= kDec1MaxH && c->moe_intermediate <= 2048 && Is <= 2048;
@@ -404,11 +424,13 @@ int n_stages(const moe_mlp_config* c, int64_t T, int prefill) {
 // kernel instances of its own with the geometry compiled in.
 using DecGeoFlash = DecGeo<4096, 1536, 288, 8, 1536>;
 
-bool glm_flash_geometry(const moe_mlp_config* c) {
+bool flash_shape(const moe_mlp_config* c) {
   return c->hidden == DecGeoFlash::H && c->moe_intermediate == DecGeoFlash::I &&
          c->num_experts == DecGeoFlash::E && c->top_k == DecGeoFlash::K && c->n_shared_experts == 1 &&
          c->shared_intermediate == DecGeoFlash::IS;
 }
+bool glm_flash_geometry(const moe_mlp_config* c) { return c->kind == MOE_MLP_KIND_ROUTED && flash_shape(c); }
+bool glm_flash_geometry_fp8(const moe_mlp_config* c) { return is_fp8(c) && flash_shape(c); }
 
 // Routed gate/up: RJ (gate, up) row pairs per wavefront (16 KB of codes at H = 4096).
 constexpr int kDecRJ = 4;
@@ -458,6 +480,60 @@ void launch_down_combine(const moe_mlp_config* c, const moe_mlp_weights* w, cons
   }
 }
 
+// Few-token decode with FP8 experts: launches 2 and 3 of decode_fp8.hpp.
+template <class G, int NJ, int NSC, int NW, int NP>
+void dec_fp8_launch(const moe_mlp_config* c, const moe_mlp_weights* w, const uint16_t* x, const float* logits,
+                    int32_t* ids, float* wts, int32_t* ids_out, float* w_out, uint16_t* h, const uint16_t* hs,
+                    uint16_t* out, int T, hipStream_t s, Ev e1, Ev e2) {
+  constexpr int RJ = 2, R = 4;
+  const int H = c->hidden, I = c->moe_intermediate, K = c->top_k;
+  const int Is = c->n_shared_experts ? c->shared_intermediate : 0;
+  const unsigned grid = static_cast<unsigned>(T * K * cdiv(I, 4 * RJ));
+  // H <= 4096: at most 4 chunks of 16 bytes per lane and row; H == 4096 fills them all
+  if (H == 4096)
+    launch(k_dec_gateup_f8<RJ, 4, true, NJ, G>, dim3(grid), dim3(256), s, e1.a, e1.b, x, w->w13_f8,
+           w->w13_f8_scale, logits, w->router_bias, K, c->routed_scaling_factor, ids, wts, ids_out, w_out,
+           c->num_experts, H, I, c->swiglu_limit, h);
+  else
+    launch(k_dec_gateup_f8<RJ, 4, false, NJ, G>, dim3(grid), dim3(256), s, e1.a, e1.b, x, w->w13_f8,
+           w->w13_f8_scale, logits, w->router_bias, K, c->routed_scaling_factor, ids, wts, ids_out, w_out,
+           c->num_experts, H, I, c->swiglu_limit, h);
+  // I <= 2048: at most 2 chunks of 16 bytes per lane and down row
+  launch(k_dec_down_combine_f8<R, NW, NP, NSC, 2, G>, dim3(static_cast<unsigned>(cdiv(H, R))), dim3(NW * 64), s,
+         e2.a, e2.b, h, w->w2_f8, w->w2_f8_scale, w->shared_w2, hs, Is, ids, wts, c->num_experts, K, H, I, out, T);
+}
+
+template <class G, int NJ, int NSC>
+void dec_fp8_nw(const moe_mlp_config* c, const moe_mlp_weights* w, const uint16_t* x, const float* logits,
+                int32_t* ids, float* wts, int32_t* ids_out, float* w_out, uint16_t* h, const uint16_t* hs,
+                uint16_t* out, int T, hipStream_t s, Ev e1, Ev e2) {
+  const int S = T * c->top_k;
+  if (S <= 4) dec_fp8_launch<G, NJ, NSC, 4, 1>(c, w, x, logits, ids, wts, ids_out, w_out, h, hs, out, T, s, e1, e2);
+  else if (S <= 8) dec_fp8_launch<G, NJ, NSC, 8, 1>(c, w, x, logits, ids, wts, ids_out, w_out, h, hs, out, T, s, e1, e2);
+  else if (S <= 16) dec_fp8_launch<G, NJ, NSC, 16, 1>(c, w, x, logits, ids, wts, ids_out, w_out, h, hs, out, T, s, e1, e2);
+  else if (S <= 32) dec_fp8_launch<G, NJ, NSC, 16, 2>(c, w, x, logits, ids, wts, ids_out, w_out, h, hs, out, T, s, e1, e2);
+  else dec_fp8_launch<G, NJ, NSC, 16, 4>(c, w, x, logits, ids, wts, ids_out, w_out, h, hs, out, T, s, e1, e2);
+}
+
+void dec_fp8(const moe_mlp_config* c, const moe_mlp_weights* w, const uint16_t* x, const float* logits, int32_t* ids,
+             float* wts, int32_t* ids_out, float* w_out, uint16_t* h, const uint16_t* hs, uint16_t* out, int T,
+             hipStream_t s, Ev e1, Ev e2) {
+  const int Is = c->n_shared_experts ? c->shared_intermediate : 0;
+  if (glm_flash_geometry_fp8(c)) {
+    dec_fp8_nw<DecGeoFlash, 5, 3>(c, w, x, logits, ids, wts, ids_out, w_out, h, hs, out, T, s, e1, e2);
+    return;
+  }
+  with_nj(c->num_experts, [&](auto nj) {
+    constexpr int NJ = decltype(nj)::value;
+    switch (static_cast<int>(cdiv(Is / 8, 64))) {
+      case 0: case 1: dec_fp8_nw<DecGeoAny, NJ, 1>(c, w, x, logits, ids, wts, ids_out, w_out, h, hs, out, T, s, e1, e2); break;
+      case 2: dec_fp8_nw<DecGeoAny, NJ, 2>(c, w, x, logits, ids, wts, ids_out, w_out, h, hs, out, T, s, e1, e2); break;
+      case 3: dec_fp8_nw<DecGeoAny, NJ, 3>(c, w, x, logits, ids, wts, ids_out, w_out, h, hs, out, T, s, e1, e2); break;
+      default: dec_fp8_nw<DecGeoAny, NJ, 4>(c, w, x, logits, ids, wts, ids_out, w_out, h, hs, out, T, s, e1, e2); break;
+    }
+  });
+}
+
 void decode1(const moe_mlp_config* c, const moe_mlp_weights* w, const uint16_t* x, int T, uint16_t* out,
              int32_t* ids_out, float* w_out, float* logits, int32_t* ids, float* wts, uint16_t* h, uint16_t* hs,
              hipStream_t s, Ev e0, Ev e1, Ev e2) {
@@ -473,6 +549,10 @@ void decode1(const moe_mlp_config* c, const moe_mlp_weights* w, const uint16_t* 
   else
     launch(k_dec_logits_shared_t<16, 8>, dim3(nlb + nsb), dim3(256), s, e0.a, e0.b, x, w->router_w, logits, E, H,
            w->shared_w13, Is, hs, c->swiglu_limit, nlb, T);
+  if (is_fp8(c)) {
+    dec_fp8(c, w, x, logits, ids, wts, ids_out, w_out, h, hs, out, T, s, e1, e2);
+    return;
+  }
   dec_gateup(c, w, x, logits, ids, wts, ids_out, w_out, h, T, s, e1);
   // one slot per wavefront up to 8 slots (4 or 8 wavefronts), else 16 wavefronts with up to 4 slots each
   const int S = T * K;
@@ -493,7 +573,7 @@ int run_layer(const moe_mlp_config* c, const moe_mlp_weights* w, const uint16_t*
   if ((st = validate_weights(c, w))) return st;
   if (!x || !out || !ws) return MOE_MLP_ERR_NULL_ARG;
   if (!aligned(x) || !aligned(out) || !aligned(ws)) return MOE_MLP_ERR_MISALIGNED;
-  if (c->kind == MOE_MLP_KIND_ROUTED && ((ids_out && !aligned(ids_out)) || (w_out && !aligned(w_out))))
+  if (is_routed(c) && ((ids_out && !aligned(ids_out)) || (w_out && !aligned(w_out))))
     return MOE_MLP_ERR_MISALIGNED;
   if (!decode1_ok(c, T, prefill)) prefill = gemm_form(c, T, prefill);   // from here on: the form that runs
   const Plan p = make_plan(c, T, prefill);
@@ -599,7 +679,19 @@ int run_layer(const moe_mlp_config* c, const moe_mlp_weights* w, const uint16_t*
     gu.T = static_cast<int>(T);              // activation rows (tokens)
     gu.out = h;
     gu.ldo = I;
-    gemm<true, GEMM_GATEUP, true>(gu, p.max_tiles, s, ev(3));
+    if (is_fp8(c)) {
+      gu.bq = w->w13_f8;
+      gu.bs = nullptr;
+      gu.bq_t = gu.bs_t = nullptr;
+      gu.bsf = w->w13_f8_scale;
+      gu.stride_q = int64_t(2) * I * H;
+      gu.stride_s = int64_t(2) * (I / MOE_MLP_FP8_BLOCK) * (H / MOE_MLP_FP8_BLOCK);
+      gu.gscale = nullptr;
+      launch(k_gemm_f8<GEMM_GATEUP>, dim3(static_cast<unsigned>(p.max_tiles), static_cast<unsigned>(cdiv(I, 128))),
+             dim3(256), s, ev(3).a, ev(3).b, gu);
+    } else {
+      gemm<true, GEMM_GATEUP, true>(gu, p.max_tiles, s, ev(3));
+    }
     // routed down -> y (slot rows)
     GemmArgs gd = g;
     gd.a = h;
@@ -617,7 +709,20 @@ int run_layer(const moe_mlp_config* c, const moe_mlp_weights* w, const uint16_t*
     gd.T = static_cast<int>(S);              // activation rows (slots)
     gd.out = y;
     gd.ldo = H;
-    gemm<true, GEMM_DOWN_SLOT_F32, true>(gd, p.max_tiles, s, ev(4));
+    if (is_fp8(c)) {
+      gd.bq = w->w2_f8;
+      gd.bs = nullptr;
+      gd.bq_t = gd.bs_t = nullptr;
+      gd.bsf = w->w2_f8_scale;
+      gd.stride_q = int64_t(H) * I;
+      gd.stride_s = int64_t(H / MOE_MLP_FP8_BLOCK) * (I / MOE_MLP_FP8_BLOCK);
+      gd.gscale = nullptr;
+      launch(k_gemm_f8<GEMM_DOWN_SLOT_F32>,
+             dim3(static_cast<unsigned>(p.max_tiles), static_cast<unsigned>(cdiv(H, 256))), dim3(256), s, ev(4).a,
+             ev(4).b, gd);
+    } else {
+      gemm<true, GEMM_DOWN_SLOT_F32, true>(gd, p.max_tiles, s, ev(4));
+    }
     const int64_t mt = cdiv(T, GM_BM);
     if (Is) {
       gemm<false, GEMM_GATEUP, false>(bf16_gemm_args(x, H, w->shared_w13, Is, Ti, hs, Is, L), mt, s, ev(5));
@@ -762,7 +867,7 @@ int moe_router_topk(const moe_mlp_config* cfg, const float* router_w, const floa
                     void* stream) {
   int st = validate_cfg(cfg, T, 1);
   if (st) return st;
-  if (cfg->kind != MOE_MLP_KIND_ROUTED) return MOE_MLP_ERR_KIND_MISMATCH;
+  if (!is_routed(cfg)) return MOE_MLP_ERR_KIND_MISMATCH;
   if (T == 0) return MOE_MLP_OK;
   if (!router_w || !router_bias || !x || !ids || !w || !workspace) return MOE_MLP_ERR_NULL_ARG;
   if (!aligned(router_w) || !aligned(router_bias) || !aligned(x) || !aligned(ids) || !aligned(w) ||

@@ -32,7 +32,8 @@ def config_of(w: synth.Workload) -> capi.Config:
         return capi.Config(kind=capi.KIND_DENSE, hidden=w.H, moe_intermediate=0, num_experts=0, top_k=0,
                            n_shared_experts=0, shared_intermediate=0, dense_intermediate=w.Id,
                            routed_scaling_factor=w.rsf, swiglu_limit=w.swiglu_limit)
-    return capi.Config(kind=capi.KIND_ROUTED, hidden=w.H, moe_intermediate=w.I, num_experts=w.E, top_k=w.K,
+    kind = capi.KIND_ROUTED_FP8 if w.fmt == "fp8" else capi.KIND_ROUTED
+    return capi.Config(kind=kind, hidden=w.H, moe_intermediate=w.I, num_experts=w.E, top_k=w.K,
                        n_shared_experts=1 if w.Is else 0, shared_intermediate=w.Is, dense_intermediate=0,
                        routed_scaling_factor=w.rsf, swiglu_limit=w.swiglu_limit)
 
@@ -46,23 +47,30 @@ class DeviceRouted:
         E, H, I = w.E, w.H, w.I
         wt = capi.Weights(
             router_w=torch.from_numpy(inp.router_w).to(DEV),
-            router_bias=torch.from_numpy(inp.router_bias).to(DEV),
-            w13_q=torch.empty((E, 2 * I, H // 2), dtype=torch.uint8, device=DEV),
-            w13_s=torch.empty((E, 2 * I, H // 16), dtype=torch.uint8, device=DEV),
-            w13_g=torch.from_numpy(inp.w13_g if w13_g is None else np.asarray(w13_g, np.float32)).to(DEV),
-            w2_q=torch.empty((E, H, I // 2), dtype=torch.uint8, device=DEV),
-            w2_s=torch.empty((E, H, I // 16), dtype=torch.uint8, device=DEV),
-            w2_g=torch.from_numpy(inp.w2_g if w2_g is None else np.asarray(w2_g, np.float32)).to(DEV))
+            router_bias=torch.from_numpy(inp.router_bias).to(DEV))
+        if w.fmt == "fp8":
+            B = capi.FP8_BLOCK
+            wt.w13_f8 = torch.empty((E, 2 * I, H), dtype=torch.uint8, device=DEV)
+            wt.w13_f8_scale = torch.empty((E, 2 * I // B, H // B), dtype=torch.float32, device=DEV)
+            wt.w2_f8 = torch.empty((E, H, I), dtype=torch.uint8, device=DEV)
+            wt.w2_f8_scale = torch.empty((E, H // B, I // B), dtype=torch.float32, device=DEV)
+            dst = (wt.w13_f8, wt.w13_f8_scale, wt.w2_f8, wt.w2_f8_scale)
+        else:
+            wt.w13_q = torch.empty((E, 2 * I, H // 2), dtype=torch.uint8, device=DEV)
+            wt.w13_s = torch.empty((E, 2 * I, H // 16), dtype=torch.uint8, device=DEV)
+            wt.w13_g = torch.from_numpy(inp.w13_g if w13_g is None else np.asarray(w13_g, np.float32)).to(DEV)
+            wt.w2_q = torch.empty((E, H, I // 2), dtype=torch.uint8, device=DEV)
+            wt.w2_s = torch.empty((E, H, I // 16), dtype=torch.uint8, device=DEV)
+            wt.w2_g = torch.from_numpy(inp.w2_g if w2_g is None else np.asarray(w2_g, np.float32)).to(DEV)
+            dst = (wt.w13_q, wt.w13_s, wt.w2_q, wt.w2_s)
         if w13_g is not None:
             inp.w13_g = np.asarray(w13_g, np.float32)
         if w2_g is not None:
             inp.w2_g = np.asarray(w2_g, np.float32)
 
         def put(e, q13, s13, q2, s2):
-            wt.w13_q[e].copy_(torch.from_numpy(q13))
-            wt.w13_s[e].copy_(torch.from_numpy(s13))
-            wt.w2_q[e].copy_(torch.from_numpy(q2))
-            wt.w2_s[e].copy_(torch.from_numpy(s2))
+            for d, v in zip(dst, (q13, s13, q2, s2)):
+                d[e].copy_(torch.from_numpy(v))
 
         synth.for_each_expert(w, put)
         if w.Is:

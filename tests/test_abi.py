@@ -243,3 +243,22 @@ def test_noalloc_decode_validation():
     assert ws_size(flash, capi.DECODE_MAX_T, 0)[1] > capi.NOALLOC_SCRATCH_BYTES
     assert noalloc(flash, capi.DECODE_MAX_T) == capi.ERR_SCRATCH_LIMIT
     assert "SCRATCH_LIMIT" in R.moe_mlp_status_string(capi.ERR_SCRATCH_LIMIT)
+
+
+def test_fp8_kind_validation():
+    """MOE_MLP_KIND_ROUTED_FP8: H and I multiples of 128, the FP8 weight fields required
+    (the NVFP4 ones are not)."""
+    fp8 = dict(kind=capi.KIND_ROUTED_FP8)
+    assert ws_size(cfg(**fp8), 1, 0)[0] == capi.OK
+    assert ws_size(cfg(hidden=416, **fp8), 1, 0)[0] == capi.ERR_BAD_SHAPE
+    assert ws_size(cfg(moe_intermediate=160, **fp8), 1, 1)[0] == capi.ERR_BAD_SHAPE
+    for missing in ("w13_f8", "w13_f8_scale", "w2_f8", "w2_f8_scale", "router_w", "shared_w2"):
+        for entry in ENTRIES:
+            assert call(entry, cfg(**fp8), full_weights(**{missing: None})) == capi.ERR_KIND_MISMATCH, missing
+    no_nvfp4 = full_weights(w13_q=None, w13_s=None, w13_g=None, w2_q=None, w2_s=None, w2_g=None)
+    for entry in ENTRIES:
+        assert call(entry, cfg(**fp8), no_nvfp4, wsb=0) == capi.ERR_WORKSPACE_TOO_SMALL
+    # the stage names follow the routed forms
+    L = R.lib()
+    assert L.moe_mlp_stage_name(ctypes.byref(cfg(**fp8)), 1, 0, 2).decode() == "shared_routed_down_combine"
+    assert L.moe_mlp_stage_name(ctypes.byref(cfg(**fp8)), 16, 0, 3).decode() == "routed_gateup"
