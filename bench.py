@@ -106,21 +106,27 @@ def upload_routed(w, device):
     import synth
     from routed_expert_mlp_amd import capi
     E, H, I = w.E, w.H, w.I
-    wt = capi.Weights(
-        router_w=torch.from_numpy(synth.router_weight(w)).to(device),
-        router_bias=torch.from_numpy(synth.router_bias(w)).to(device),
-        w13_q=torch.empty((E, 2 * I, H // 2), dtype=torch.uint8, device=device),
-        w13_s=torch.empty((E, 2 * I, H // 16), dtype=torch.uint8, device=device),
-        w13_g=torch.from_numpy(synth.w13_globals(w)).to(device),
-        w2_q=torch.empty((E, H, I // 2), dtype=torch.uint8, device=device),
-        w2_s=torch.empty((E, H, I // 16), dtype=torch.uint8, device=device),
-        w2_g=torch.from_numpy(synth.w2_globals(w)).to(device))
+    wt = capi.Weights(router_w=torch.from_numpy(synth.router_weight(w)).to(device),
+                      router_bias=torch.from_numpy(synth.router_bias(w)).to(device))
+    if w.fmt == "fp8":
+        B = capi.FP8_BLOCK
+        wt.w13_f8 = torch.empty((E, 2 * I, H), dtype=torch.uint8, device=device)
+        wt.w13_f8_scale = torch.empty((E, 2 * I // B, H // B), dtype=torch.float32, device=device)
+        wt.w2_f8 = torch.empty((E, H, I), dtype=torch.uint8, device=device)
+        wt.w2_f8_scale = torch.empty((E, H // B, I // B), dtype=torch.float32, device=device)
+        dst = (wt.w13_f8, wt.w13_f8_scale, wt.w2_f8, wt.w2_f8_scale)
+    else:
+        wt.w13_q = torch.empty((E, 2 * I, H // 2), dtype=torch.uint8, device=device)
+        wt.w13_s = torch.empty((E, 2 * I, H // 16), dtype=torch.uint8, device=device)
+        wt.w13_g = torch.from_numpy(synth.w13_globals(w)).to(device)
+        wt.w2_q = torch.empty((E, H, I // 2), dtype=torch.uint8, device=device)
+        wt.w2_s = torch.empty((E, H, I // 16), dtype=torch.uint8, device=device)
+        wt.w2_g = torch.from_numpy(synth.w2_globals(w)).to(device)
+        dst = (wt.w13_q, wt.w13_s, wt.w2_q, wt.w2_s)
 
     def put(e, q13, s13, q2, s2):
-        wt.w13_q[e].copy_(torch.from_numpy(q13))
-        wt.w13_s[e].copy_(torch.from_numpy(s13))
-        wt.w2_q[e].copy_(torch.from_numpy(q2))
-        wt.w2_s[e].copy_(torch.from_numpy(s2))
+        for d, v in zip(dst, (q13, s13, q2, s2)):
+            d[e].copy_(torch.from_numpy(v))
 
     synth.for_each_expert(w, put)
     if w.Is:
@@ -139,7 +145,7 @@ def clone_weights(wt):
 
 def config_of(w):
     from routed_expert_mlp_amd import capi
-    return capi.Config(kind=capi.KIND_ROUTED, hidden=w.H, moe_intermediate=w.I, num_experts=w.E, top_k=w.K,
+    return capi.Config(kind=capi.KIND_ROUTED_FP8 if w.fmt == "fp8" else capi.KIND_ROUTED, hidden=w.H, moe_intermediate=w.I, num_experts=w.E, top_k=w.K,
                        n_shared_experts=1 if w.Is else 0, shared_intermediate=w.Is, dense_intermediate=0,
                        routed_scaling_factor=w.rsf, swiglu_limit=w.swiglu_limit)
 
@@ -594,19 +600,32 @@ def main():
             extra[name] = line
             del wts_v, bv, xs_v
             torch.cuda.empty_cache()
+        # FP8 block-scaled experts (E4M3, fp32 scale per 128 x 128 block): one-token decode
+        wv = synth.workload("flash_decode_t1_fp8")
+        cfgv = config_of(wv)
+        log(f"[bench] generating + uploading {wv.name}: {wv.E * wv.expert_bytes / 1e9:.2f} GB FP8")
+        bv = upload_routed(wv, dev)
+        wts_v = [bv] + [clone_weights(bv) for _ in range(RV - 1)]
+        xs_v = [x_dev(wv, [r], dev) for r in range(RV)]
+        line = decode_line(cfgv, wv, wts_v, xs_v, 1, dev, max(40, args.steps // 4))
+        line["workload"] = (f"T=1, H={wv.H}, I={wv.I}, E={wv.E}, K={wv.K}, routed experts FP8 E4M3 with fp32 "
+                            f"128x128 block scales ({wv.expert_bytes} B per expert), BF16 shared expert")
+        extra["flash_decode_t1_fp8"] = line
+        del wts_v, bv, xs_v
+        torch.cuda.empty_cache()
 
     # ---------------- prefill T=4096 ----------------
     if not args.no_prefill:
         del wts
         torch.cuda.empty_cache()
-        for pname in ("prefill_t4096", "prefill_t4096_literal_bias"):
+        for pname in ("prefill_t4096", "prefill_t4096_literal_bias", "prefill_t4096_fp8"):
             wp = synth.workload(pname)
             cfgp = config_of(wp)
             log(f"[bench] generating + uploading {wp.name}")
             wt_rm = upload_routed(wp, dev)
-            # the grouped GEMM reads the routed weights in the tile layout, packed
-            # once at load (the row-major arrays stay for the GEMV forms)
-            wtp = capi.with_tiled_weights(wt_rm)
+            # the NVFP4 grouped GEMM reads the routed weights in the tile layout,
+            # packed once at load (the row-major arrays stay for the GEMV forms)
+            wtp = wt_rm if wp.fmt == "fp8" else capi.with_tiled_weights(wt_rm)
             xp = torch.from_numpy(synth.x_rows(wp).view(np.int16)).to(dev).view(torch.bfloat16)
             outp = torch.empty((wp.T, wp.H), dtype=torch.bfloat16, device=dev)
             wsp = capi.workspace(cfgp, wp.T, True, dev)
@@ -620,14 +639,20 @@ def main():
             fl_routed = 2.0 * T * K * 3 * H * I
             fl_total = fl_routed + 2.0 * T * 3 * H * Is + 2.0 * T * H * E
             gg_ms = stp["routed_gateup"] + stp["routed_down"]
-            rm_bytes = sum(t.numel() for t in (wt_rm.w13_q, wt_rm.w13_s, wt_rm.w2_q, wt_rm.w2_s))
+            if wp.fmt == "fp8":
+                res = {"weights": "routed FP8 E4M3, fp32 128x128 block scales (row-major)",
+                       "resident_routed_weight_bytes": {"row_major": int(wp.E * wp.expert_bytes)}}
+            else:
+                rm_bytes = sum(t.numel() for t in (wt_rm.w13_q, wt_rm.w13_s, wt_rm.w2_q, wt_rm.w2_s))
+                res = {"weights": "routed NVFP4 in the tile layout (packed once at load)",
+                       "resident_routed_weight_bytes": {"row_major": int(rm_bytes), "tile_layout": int(rm_bytes),
+                                                        "note": "both copies stay resident: the GEMV forms read "
+                                                                "the row-major arrays, the grouped GEMM the tile "
+                                                                "layout"},
+                       "ms_per_step_row_major_weights": round(s_rm * 1e3, 3)}
             extra[pname] = {
                 "ms_per_step": round(s_p * 1e3, 3), "layer_tflops": round(fl_total / s_p / 1e12, 1),
-                "weights": "routed NVFP4 in the tile layout (packed once at load)",
-                "resident_routed_weight_bytes": {"row_major": int(rm_bytes), "tile_layout": int(rm_bytes),
-                                                 "note": "both copies stay resident: the GEMV forms read the "
-                                                         "row-major arrays, the grouped GEMM the tile layout"},
-                "ms_per_step_row_major_weights": round(s_rm * 1e3, 3),
+                **res,
                 "grouped_gemm_tflops": round(fl_routed / (gg_ms * 1e-3) / 1e12, 1),
                 "grouped_gemm_frac_bf16_peak": round(fl_routed / (gg_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
                 "stage_us": {k: round(v * 1e3, 1) for k, v in stp.items()}}
