@@ -4,18 +4,19 @@
 //   1. k_dec_logits_shared: router logits (fp32 rows of gate.weight) and the
 //      BF16 shared expert's gate/up + clamped SwiGLU, both of which only need
 //      x, in one grid;
-//   2. k_dec_gateup: every wavefront first redoes the router top-k from the
-//      E logits (router.hpp topk_wave; "Traps": bias steers selection only,
-//      weights are the renormalised unbiased scores times rsf) to learn which
-//      expert it serves, then streams its NVFP4 gate/up rows + clamped SwiGLU
-//      -> h (bf16).  One wavefront also writes ids and weights.  Redoing the
-//      selection (~1 KB of logits per wavefront) is cheaper than a launch of
-//      its own;
-//   3. k_dec_down_combine: for a block of output rows, the shared expert's
-//      BF16 down rows (issued first: they need nothing from the router, so
-//      they stream while the expert ids arrive), the routed NVFP4 down rows of
-//      all K experts, and the combine out = bf16(ys + sum_k w_k y_k) (fixed k
-//      order) from the block's own partial sums.
+//   2. k_dec_gateup: wavefront 0 of every block redoes the router top-k from
+//      the E logits (router.hpp topk_wave; "Traps": bias steers selection
+//      only, weights are the renormalised unbiased scores times rsf) and hands
+//      the block's expert to the other wavefronts through LDS; the block then
+//      streams its NVFP4 gate/up rows + clamped SwiGLU -> h (bf16).  One block
+//      also writes ids and weights.  Redoing the selection per block (~2 KB of
+//      logits and bias) is cheaper than a launch of its own;
+//   3. k_dec_down_combine (k_dec_down_combine1 for one token): for a block of
+//      output rows, the shared expert's BF16 down rows (they need nothing
+//      from the router, so they stream while the expert ids arrive), the
+//      routed NVFP4 down rows of all K experts, and the combine
+//      out = bf16(ys + sum_k w_k y_k) (fixed k order) from the block's own
+//      partial sums.
 //
 // Each wavefront issues all loads of its rows before using any of them, so a
 // wavefront has its whole share of the weight stream in flight at once.
@@ -445,6 +446,124 @@ __global__ __launch_bounds__(NW * 64) void k_dec_down_combine(
       for (int k = 0; k < K; ++k) o += part[t * K + k][r];
       out[static_cast<int64_t>(t) * H + r0 + r] = f32_to_bf16(o);
     }
+  }
+}
+
+// -------------------------------------------------------------------------
+// 3'. The same layer output for one token with R output rows per block and
+// the work split by kind: wavefronts 0..K-1 each take one routed slot's R
+// down rows (lane l: the 16-byte chunk l of every row, as above), wavefronts
+// K..K+NSW-1 each take R/NSW shared down rows.  Each wavefront reads its
+// input vector (h_k, or hs) once for all of its rows, so the vectors cost a
+// quarter of the cache traffic of 4-row blocks.  Per (slot, row) and per
+// shared row the products, their order and the combine order are those of
+// k_dec_down_combine, so the two kernels agree bit for bit.
+//   requires K + NSW <= 16, I <= 2048 (one chunk per lane and row)
+// -------------------------------------------------------------------------
+template <int R, int NSW, int NSC, class G>
+__global__ __launch_bounds__(1024) void k_dec_down_combine1(
+    const uint16_t* __restrict__ h, const uint8_t* __restrict__ q2, const uint8_t* __restrict__ s2,
+    const float* __restrict__ g2, const uint16_t* __restrict__ sw2, const uint16_t* __restrict__ hs, int Is_,
+    const int32_t* __restrict__ ids, const float* __restrict__ wts, int E_, int K_, int H_, int I_,
+    uint16_t* __restrict__ out) {
+  static_assert(R % NSW == 0, "whole shared rows per wavefront");
+  constexpr int SR = R / NSW;
+  const int K = G::K ? G::K : K_, E = G::E ? G::E : E_, H = G::H ? G::H : H_, I = G::I ? G::I : I_;
+  const int Is = G::IS >= 0 ? G::IS : Is_;
+  __shared__ float part[16][R];
+  __shared__ float ysp[R];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int r0 = blockIdx.x * R;
+  if (wv < K) {
+    // routed slot wv: ids first; then h_k (independent of the ids); then the R down rows
+    const int nd = I >> 5;
+    const bool dlane = lane < nd;
+    const int dl = dlane ? lane : nd - 1;
+    const int idv = ids[wv];
+    const float wsl = wts[wv];
+    uint32_t xp[16];
+    const uint4* hp = reinterpret_cast<const uint4*>(h + static_cast<int64_t>(wv) * I + 32 * dl);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint4 v = hp[q];
+      xp[4 * q] = v.x; xp[4 * q + 1] = v.y; xp[4 * q + 2] = v.z; xp[4 * q + 3] = v.w;
+    }
+    const int64_t rq = I >> 1, rs = I >> 4;
+    const int e = min(max(idv, 0), E - 1);
+    uint4 cw[R];
+    uint32_t sc[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int64_t base = static_cast<int64_t>(e) * H + min(r0 + r, H - 1);
+      cw[r] = *reinterpret_cast<const uint4*>(q2 + base * rq + 16 * dl);
+      sc[r] = *reinterpret_cast<const uint16_t*>(s2 + base * rs + 2 * dl);
+    }
+    const float gk = g2[e];
+    __builtin_amdgcn_sched_barrier(0);
+    if (!dlane) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        cw[r] = make_uint4(0, 0, 0, 0);
+        sc[r] = 0u;
+      }
+    }
+    float acc[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      acc[r] = fmaf(e2m1x16_dot(cw[r].x, cw[r].y, xp), e4m3_to_f32<0>(sc[r]), 0.0f);
+      acc[r] = fmaf(e2m1x16_dot(cw[r].z, cw[r].w, xp + 8), e4m3_to_f32<1>(sc[r]), acc[r]);
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) acc[r] = wave_sum(acc[r]);
+    if (lane == 0) {
+      const float wk = wsl * gk;
+#pragma unroll
+      for (int r = 0; r < R; ++r) part[wv][r] = wk * acc[r];
+    }
+  } else if (wv < K + NSW && Is > 0) {
+    // shared rows r0 + sr0 .. + SR - 1 against hs
+    const int sr0 = (wv - K) * SR;
+    const int nsc = Is >> 3;
+    uint4 sw[SR][NSC];
+    uint32_t hv[NSC][4];
+#pragma unroll
+    for (int i = 0; i < SR; ++i) {
+      const uint4* row = reinterpret_cast<const uint4*>(sw2 + static_cast<int64_t>(min(r0 + sr0 + i, H - 1)) * Is);
+#pragma unroll
+      for (int c = 0; c < NSC; ++c) sw[i][c] = row[min(lane + 64 * c, nsc - 1)];
+    }
+#pragma unroll
+    for (int c = 0; c < NSC; ++c) {
+      const uint4 v = reinterpret_cast<const uint4*>(hs)[min(lane + 64 * c, nsc - 1)];
+      hv[c][0] = v.x; hv[c][1] = v.y; hv[c][2] = v.z; hv[c][3] = v.w;
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int c = 0; c < NSC; ++c)
+      if (lane + 64 * c >= nsc) {
+#pragma unroll
+        for (int i = 0; i < SR; ++i) sw[i][c] = make_uint4(0, 0, 0, 0);
+      }
+    float acc[SR];
+#pragma unroll
+    for (int i = 0; i < SR; ++i) {
+      acc[i] = 0.0f;
+#pragma unroll
+      for (int c = 0; c < NSC; ++c) acc[i] = bf16_chunk_dot(sw[i][c], hv[c], acc[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < SR; ++i) acc[i] = wave_sum(acc[i]);
+    if (lane == 0) {
+#pragma unroll
+      for (int i = 0; i < SR; ++i) ysp[sr0 + i] = acc[i];
+    }
+  }
+  __syncthreads();
+  const int tid = threadIdx.x;
+  if (tid < R && r0 + tid < H) {
+    float o = Is > 0 ? ysp[tid] : 0.0f;
+    for (int k = 0; k < K; ++k) o += part[k][tid];
+    out[r0 + tid] = f32_to_bf16(o);
   }
 }
 

@@ -480,6 +480,32 @@ void launch_down_combine(const moe_mlp_config* c, const moe_mlp_weights* w, cons
   }
 }
 
+// One token: 16 output rows per block, a wavefront per routed slot and 4 for
+// the shared rows (k_dec_down_combine1).
+constexpr int kDown1Rows = 16, kDown1Shared = 4;
+
+void launch_down_combine1(const moe_mlp_config* c, const moe_mlp_weights* w, const uint16_t* h, const uint16_t* hs,
+                          const int32_t* ids, const float* wts, uint16_t* out, hipStream_t s, Ev ev) {
+  constexpr int R = kDown1Rows, NSW = kDown1Shared;
+  const int H = c->hidden, K = c->top_k;
+  const int Is = c->n_shared_experts ? c->shared_intermediate : 0;
+  const dim3 grid(static_cast<unsigned>(cdiv(H, R))), block(static_cast<unsigned>((K + NSW) * 64));
+  auto go = [&](auto kern) {
+    launch(kern, grid, block, s, ev.a, ev.b, h, w->w2_q, w->w2_s, w->w2_g, w->shared_w2, hs, Is, ids, wts,
+           c->num_experts, K, H, c->moe_intermediate, out);
+  };
+  if (glm_flash_geometry(c)) {
+    go(k_dec_down_combine1<R, NSW, 3, DecGeoFlash>);
+    return;
+  }
+  switch (static_cast<int>(cdiv(Is / 8, 64))) {
+    case 0: case 1: go(k_dec_down_combine1<R, NSW, 1, DecGeoAny>); break;
+    case 2: go(k_dec_down_combine1<R, NSW, 2, DecGeoAny>); break;
+    case 3: go(k_dec_down_combine1<R, NSW, 3, DecGeoAny>); break;
+    default: go(k_dec_down_combine1<R, NSW, 4, DecGeoAny>); break;
+  }
+}
+
 // Few-token decode with FP8 experts: launches 2 and 3 of decode_fp8.hpp.
 template <class G, int NJ, int NSC, int NW, int NP>
 void dec_fp8_launch(const moe_mlp_config* c, const moe_mlp_weights* w, const uint16_t* x, const float* logits,
@@ -554,6 +580,10 @@ void decode1(const moe_mlp_config* c, const moe_mlp_weights* w, const uint16_t* 
     return;
   }
   dec_gateup(c, w, x, logits, ids, wts, ids_out, w_out, h, T, s, e1);
+  if (T == 1 && K + kDown1Shared <= 16) {
+    launch_down_combine1(c, w, h, hs, ids, wts, out, s, e2);
+    return;
+  }
   // one slot per wavefront up to 8 slots (4 or 8 wavefronts), else 16 wavefronts with up to 4 slots each
   const int S = T * K;
   if (S <= 4) launch_down_combine<4, 1>(c, w, h, hs, ids, wts, out, T, s, e2);

@@ -144,11 +144,12 @@ __global__ __launch_bounds__(256) void k_logits_gemm(const uint16_t* __restrict_
 //     (order-preserving bits of its biased score) << 32 | (0xFFFFFFFF - e),
 // so a larger key is a larger score and, between equal scores, the lower id
 // (keys are distinct).  Each lane sorts its NJ keys (experts lane + 64 j,
-// E <= 64 * NJ) descending once; a round is the wavefront max of the lanes'
-// first keys (DPP within rows of 16, then the 4 row winners) and the owning
-// lane drops its first key.  One 64-bit value per reduction step keeps a
-// round's dependent chain short: the wavefront sits on the decode critical
-// path.  Returns the id in slot `want`.  With ids != null all K rounds run
+// E <= 64 * NJ) descending once; a round finds the largest of the lanes'
+// first keys and the owning lane drops its first key.  The round reduces the
+// 32-bit score halves only (DPP max within rows of 16, then the 4 row
+// winners) and takes the id half into account only when several lanes hold
+// the top score, which keeps the dependent chain short: the wavefront sits on
+// the decode critical path.  Returns the id in slot `want`.  With ids != null all K rounds run
 // and ids/wts (and ids2/wts2 when not null) are written: the weight of slot k
 // is its unbiased sigmoid score over the sum of the K chosen scores (added in
 // slot order) times rsf.
@@ -163,29 +164,22 @@ __device__ __forceinline__ uint64_t u64_of(uint32_t lo, uint32_t hi) {
 }
 
 template <int CTRL>
-__device__ __forceinline__ uint64_t dpp_max_u64(uint64_t v) {
-  const uint32_t lo = static_cast<uint32_t>(dpp_mov<CTRL>(static_cast<int>(static_cast<uint32_t>(v))));
-  const uint32_t hi = static_cast<uint32_t>(dpp_mov<CTRL>(static_cast<int>(static_cast<uint32_t>(v >> 32))));
-  const uint64_t o = u64_of(lo, hi);
+__device__ __forceinline__ uint32_t dpp_max_u32(uint32_t v) {
+  const uint32_t o = static_cast<uint32_t>(dpp_mov<CTRL>(static_cast<int>(v)));
   return o > v ? o : v;
 }
 
-__device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int l) {
-  const uint32_t lo = __builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(v)), l);
-  const uint32_t hi = __builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(v >> 32)), l);
-  return u64_of(lo, hi);
-}
-
-// Wave-wide max of a 64-bit value; every lane returns it.  All lanes active.
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-  v = dpp_max_u64<DPP_QUAD_1032>(v);
-  v = dpp_max_u64<DPP_QUAD_2301>(v);
-  v = dpp_max_u64<DPP_ROW_HALF_MIRROR>(v);
-  v = dpp_max_u64<DPP_ROW_MIRROR>(v);
-  const uint64_t a = readlane_u64(v, 0), b = readlane_u64(v, 16);
-  const uint64_t c = readlane_u64(v, 32), d = readlane_u64(v, 48);
-  const uint64_t ab = a > b ? a : b, cd = c > d ? c : d;
-  return ab > cd ? ab : cd;
+// Wave-wide max of a 32-bit value (wave-uniform result).  All lanes active.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = dpp_max_u32<DPP_QUAD_1032>(v);
+  v = dpp_max_u32<DPP_QUAD_2301>(v);
+  v = dpp_max_u32<DPP_ROW_HALF_MIRROR>(v);
+  v = dpp_max_u32<DPP_ROW_MIRROR>(v);
+  const uint32_t a = __builtin_amdgcn_readlane(static_cast<int>(v), 0);
+  const uint32_t b = __builtin_amdgcn_readlane(static_cast<int>(v), 16);
+  const uint32_t c = __builtin_amdgcn_readlane(static_cast<int>(v), 32);
+  const uint32_t d = __builtin_amdgcn_readlane(static_cast<int>(v), 48);
+  return max(max(a, b), max(c, d));
 }
 
 // Logit e of a row: one fp32 value, or (planes == 3, the split-weight router
@@ -225,15 +219,34 @@ __device__ __forceinline__ int topk_wave(const float* __restrict__ lrow, const f
       key[j] = sw ? b : a;
       key[j + 1] = sw ? a : b;
     }
+  // Each round takes the largest head key.  The score half decides first (a
+  // 32-bit wave max); only when several lanes hold that score does the id half
+  // (larger ~id = smaller id) decide, in a second 32-bit max over those lanes.
+  uint32_t kh[NJ], kl[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    kh[j] = static_cast<uint32_t>(key[j] >> 32);
+    kl[j] = static_cast<uint32_t>(key[j]);
+  }
   const int nr = ids ? K : want + 1;
   int want_id = 0, my_id = 0;
   for (int k = 0; k < nr; ++k) {
-    const uint64_t w = wave_max_u64(key[0]);
-    const int id = static_cast<int>(0xFFFFFFFFu - static_cast<uint32_t>(w));
-    if (key[0] == w) {
+    const uint32_t m = wave_max_u32(kh[0]);
+    uint64_t top = __builtin_amdgcn_ballot_w64(kh[0] == m);
+    if (__popcll(top) > 1) {
+      const uint32_t c = wave_max_u32(kh[0] == m ? kl[0] : 0u);
+      top = __builtin_amdgcn_ballot_w64(kh[0] == m && kl[0] == c);
+    }
+    const int win = static_cast<int>(__builtin_ctzll(top));
+    const int id = static_cast<int>(0xFFFFFFFFu - static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(kl[0]), win)));
+    if (lane == win) {
 #pragma unroll
-      for (int j = 0; j < NJ - 1; ++j) key[j] = key[j + 1];
-      key[NJ - 1] = 0;
+      for (int j = 0; j < NJ - 1; ++j) {
+        kh[j] = kh[j + 1];
+        kl[j] = kl[j + 1];
+      }
+      kh[NJ - 1] = 0;
+      kl[NJ - 1] = 0;
     }
     if (k == want) want_id = id;
     if (lane == k) my_id = id;
