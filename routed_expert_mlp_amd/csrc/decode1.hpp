@@ -114,12 +114,17 @@ __global__ __launch_bounds__(256) void k_dec_logits_shared(const uint16_t* __res
 }
 
 // -------------------------------------------------------------------------
-// 1'. The same grid for T <= 16 tokens (general decode): each wavefront
-// loads its router row (or shared gate/up row pair) once, then runs every
-// token's dot product against it; x rows are re-read per token (they stay in
-// the caches).  Per token the arithmetic and reduction order are those of
-// k_dec_logits_shared.  Writes logits [T][E] and hs [T][Is].
+// 1'. The same grid for T <= 16 tokens (general decode), with the tokens in
+// groups of DEC_TG over grid.y: each wavefront loads its router row (or
+// shared gate/up row pair) once, then runs the dot products of its group's
+// tokens against it; x rows are re-read per token (they stay in the caches).
+// With gridDim.x a multiple of 8 every group of a row block runs on the same
+// XCD (blocks go to the XCDs round-robin), so the groups after the first read
+// the rows from that XCD's L2.  Per token the arithmetic and reduction order
+// are those of k_dec_logits_shared.  Writes logits [T][E] and hs [T][Is].
 // -------------------------------------------------------------------------
+constexpr int DEC_TG = 4;
+
 template <int NR, int NS>
 __global__ __launch_bounds__(256) void k_dec_logits_shared_t(const uint16_t* __restrict__ x,
                                                              const float* __restrict__ wr,
@@ -128,6 +133,7 @@ __global__ __launch_bounds__(256) void k_dec_logits_shared_t(const uint16_t* __r
                                                              uint16_t* __restrict__ hs, float L, int n_logit_blocks,
                                                              int T) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int ta = blockIdx.y * DEC_TG, tb = min(T, ta + DEC_TG);
   if (static_cast<int>(blockIdx.x) < n_logit_blocks) {
     const int e = blockIdx.x * 4 + wv;
     if (e >= E) return;
@@ -139,7 +145,7 @@ __global__ __launch_bounds__(256) void k_dec_logits_shared_t(const uint16_t* __r
       const int c = lane + 64 * i;
       w[i] = c < nch ? row[c] : make_float4(0, 0, 0, 0);
     }
-    for (int t = 0; t < T; ++t) {
+    for (int t = ta; t < tb; ++t) {
       const uint2* xv = reinterpret_cast<const uint2*>(x + static_cast<int64_t>(t) * H);
       uint2 xs[NR];
 #pragma unroll
@@ -172,7 +178,7 @@ __global__ __launch_bounds__(256) void k_dec_logits_shared_t(const uint16_t* __r
       wg[i] = ok ? g[c] : make_uint4(0, 0, 0, 0);
       wu[i] = ok ? u[c] : make_uint4(0, 0, 0, 0);
     }
-    for (int t = 0; t < T; ++t) {
+    for (int t = ta; t < tb; ++t) {
       const uint4* xv = reinterpret_cast<const uint4*>(x + static_cast<int64_t>(t) * H);
       float ag = 0.0f, au = 0.0f;
 #pragma unroll

@@ -64,7 +64,8 @@ __device__ __forceinline__ float bf16_chunk_dot(uint4 w, const uint32_t* xp, flo
   return dot2_bf16(w.w, xp[3], acc);
 }
 
-// Grid: x = row blocks of 4*RW (gate/up: gate rows), y = token groups.
+// Grid: x = row blocks of 4*RW (gate/up: gate rows), y = token groups (routed:
+// the tokens of one expert; otherwise GEMV_TC consecutive tokens).
 // NC > 0: every row has at most 64*NC chunks; a wavefront loads all of its
 // rows' chunks (NC per lane) before any arithmetic and keeps them in
 // registers for every token pass, so it waits for memory once.  NC == 0:
@@ -81,7 +82,11 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
     n_tok = a.g_count[grp];
     slot_base = a.g_offset[grp];
   } else {
-    n_tok = a.T;
+    // one group per GEMV_TC tokens (grid.y); a group's rows stay on one XCD
+    // when gridDim.x is a multiple of 8, so the groups share its L2
+    slot_base = grp * GEMV_TC;
+    n_tok = min(GEMV_TC, a.T - slot_base);
+    if (n_tok <= 0) return;
   }
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int r0 = blockIdx.x * (4 * RW) + wv * RW;            // first (gate) row of this wavefront
@@ -133,7 +138,7 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
 #pragma unroll
     for (int t = 0; t < GEMV_TC; ++t) {
       const int p = t0 + min(t, nt - 1);
-      const int slot = a.n_groups ? a.g_slots[slot_base + p] : p;
+      const int slot = a.n_groups ? a.g_slots[slot_base + p] : slot_base + p;
       out_row[t] = slot;
       in_row[t] = (a.n_groups && MODE == GEMV_GATEUP) ? slot / a.K : slot;
     }

@@ -276,7 +276,12 @@ void router_logits(const uint16_t* x, const float* wr, float* logits, int64_t T,
 // and token) costs more registers than it saves in waits (measured).
 template <bool NVFP4, int MODE, int RW>
 void gemv(const GemvArgs& a, int groups, hipStream_t s, Ev ev) {
-  const dim3 grid(static_cast<unsigned>(cdiv(a.half_rows, 4 * RW)), static_cast<unsigned>(groups));
+  // without expert groups the tokens go in groups of GEMV_TC over grid.y, and
+  // grid.x is a multiple of 8: blocks go to the 8 XCDs round-robin, so every
+  // token group of a row block runs on the same XCD and reads its rows from L2
+  if (!a.n_groups) groups = static_cast<int>(cdiv(a.T, GEMV_TC));
+  const int64_t nrb = cdiv(a.half_rows, 4 * RW);
+  const dim3 grid(static_cast<unsigned>(a.n_groups ? nrb : cdiv(nrb, 8) * 8), static_cast<unsigned>(groups));
   const int nch = NVFP4 ? (a.cols >> 5) : (a.cols >> 3);
   if constexpr (NVFP4) {
     launch(k_gemv<NVFP4, MODE, RW, 0>, grid, dim3(256), s, ev.a, ev.b, a);
@@ -432,6 +437,12 @@ bool flash_shape(const moe_mlp_config* c) {
 bool glm_flash_geometry(const moe_mlp_config* c) { return c->kind == MOE_MLP_KIND_ROUTED && flash_shape(c); }
 bool glm_flash_geometry_fp8(const moe_mlp_config* c) { return is_fp8(c) && flash_shape(c); }
 
+// k_dec_logits_shared_t: row blocks (padded to a multiple of 8, the extra
+// blocks exit) x token groups.
+dim3 logits_shared_t_grid(int row_blocks, int64_t T) {
+  return dim3(static_cast<unsigned>(cdiv(row_blocks, 8) * 8), static_cast<unsigned>(cdiv(T, DEC_TG)));
+}
+
 // Routed gate/up: RJ (gate, up) row pairs per wavefront (16 KB of codes at H = 4096).
 constexpr int kDecRJ = 4;
 
@@ -573,7 +584,7 @@ void decode1(const moe_mlp_config* c, const moe_mlp_weights* w, const uint16_t* 
     launch(k_dec_logits_shared<16, 8, DecGeoAny>, dim3(nlb + nsb), dim3(256), s, e0.a, e0.b, x, w->router_w, logits,
            E, H, w->shared_w13, Is, hs, c->swiglu_limit, nlb);
   else
-    launch(k_dec_logits_shared_t<16, 8>, dim3(nlb + nsb), dim3(256), s, e0.a, e0.b, x, w->router_w, logits, E, H,
+    launch(k_dec_logits_shared_t<16, 8>, logits_shared_t_grid(nlb + nsb, T), dim3(256), s, e0.a, e0.b, x, w->router_w, logits, E, H,
            w->shared_w13, Is, hs, c->swiglu_limit, nlb, T);
   if (is_fp8(c)) {
     dec_fp8(c, w, x, logits, ids, wts, ids_out, w_out, h, hs, out, T, s, e1, e2);
@@ -664,7 +675,7 @@ int run_layer(const moe_mlp_config* c, const moe_mlp_weights* w, const uint16_t*
   const bool fused_k1 = !prefill && T <= 16 && H <= kDec1MaxH && Is <= 2048;
   if (fused_k1) {
     const int nlb = static_cast<int>(cdiv(E, 4)), nsb = static_cast<int>(cdiv(Is, 4));
-    launch(k_dec_logits_shared_t<16, 8>, dim3(nlb + nsb), dim3(256), s, ev(0).a, ev(0).b, x, w->router_w, logits,
+    launch(k_dec_logits_shared_t<16, 8>, logits_shared_t_grid(nlb + nsb, Ti), dim3(256), s, ev(0).a, ev(0).b, x, w->router_w, logits,
            E, H, w->shared_w13, Is, hs, L, nlb, Ti);
   } else {
     router_logits_plan(p, ws, x, w->router_w, logits, T, H, E, s, ev(0));
