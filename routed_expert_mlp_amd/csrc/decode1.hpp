@@ -124,6 +124,7 @@ __global__ __launch_bounds__(256) void k_dec_logits_shared(const uint16_t* __res
 // are those of k_dec_logits_shared.  Writes logits [T][E] and hs [T][Is].
 // -------------------------------------------------------------------------
 constexpr int DEC_TG = 4;
+constexpr int DEC_MAX_H = 4096;   // the decode kernels' largest hidden size
 
 template <int NR, int NS>
 __global__ __launch_bounds__(256) void k_dec_logits_shared_t(const uint16_t* __restrict__ x,
@@ -134,10 +135,18 @@ __global__ __launch_bounds__(256) void k_dec_logits_shared_t(const uint16_t* __r
                                                              int T) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int ta = blockIdx.y * DEC_TG, tb = min(T, ta + DEC_TG);
+  // the group's x rows, staged once per block in LDS (after the weight loads
+  // are issued): each wavefront then reads them at LDS latency, token after token
+  __shared__ uint4 xl[DEC_TG * (DEC_MAX_H / 8)];
+  const int nx = H >> 3;
+  auto stage_x = [&] {
+    const uint4* xg = reinterpret_cast<const uint4*>(x + static_cast<int64_t>(ta) * H);
+    for (int q = threadIdx.x; q < (tb - ta) * nx; q += 256) xl[q] = xg[q];
+    __syncthreads();
+  };
   if (static_cast<int>(blockIdx.x) < n_logit_blocks) {
     const int e = blockIdx.x * 4 + wv;
-    if (e >= E) return;
-    const float4* row = reinterpret_cast<const float4*>(wr + static_cast<int64_t>(e) * H);
+    const float4* row = reinterpret_cast<const float4*>(wr + static_cast<int64_t>(min(e, E - 1)) * H);
     float4 w[NR];
     const int nch = H >> 2;
 #pragma unroll
@@ -145,8 +154,10 @@ __global__ __launch_bounds__(256) void k_dec_logits_shared_t(const uint16_t* __r
       const int c = lane + 64 * i;
       w[i] = c < nch ? row[c] : make_float4(0, 0, 0, 0);
     }
+    stage_x();
+    if (e >= E) return;
     for (int t = ta; t < tb; ++t) {
-      const uint2* xv = reinterpret_cast<const uint2*>(x + static_cast<int64_t>(t) * H);
+      const uint2* xv = reinterpret_cast<const uint2*>(xl + (t - ta) * nx);
       uint2 xs[NR];
 #pragma unroll
       for (int i = 0; i < NR; ++i) {
@@ -166,20 +177,22 @@ __global__ __launch_bounds__(256) void k_dec_logits_shared_t(const uint16_t* __r
     }
   } else {
     const int j = (blockIdx.x - n_logit_blocks) * 4 + wv;
-    if (j >= Is) return;
-    const uint4* g = reinterpret_cast<const uint4*>(sw13 + static_cast<int64_t>(j) * H);
-    const uint4* u = reinterpret_cast<const uint4*>(sw13 + static_cast<int64_t>(Is + j) * H);
+    const int jj = min(j, max(Is - 1, 0));
+    const uint4* g = reinterpret_cast<const uint4*>(sw13 + static_cast<int64_t>(jj) * H);
+    const uint4* u = reinterpret_cast<const uint4*>(sw13 + static_cast<int64_t>(Is + jj) * H);
     const int nch = H >> 3;
     uint4 wg[NS], wu[NS];
 #pragma unroll
     for (int i = 0; i < NS; ++i) {
       const int c = lane + 64 * i;
-      const bool ok = c < nch;
+      const bool ok = c < nch && Is > 0;
       wg[i] = ok ? g[c] : make_uint4(0, 0, 0, 0);
       wu[i] = ok ? u[c] : make_uint4(0, 0, 0, 0);
     }
+    stage_x();
+    if (j >= Is) return;
     for (int t = ta; t < tb; ++t) {
-      const uint4* xv = reinterpret_cast<const uint4*>(x + static_cast<int64_t>(t) * H);
+      const uint4* xv = xl + (t - ta) * nx;
       float ag = 0.0f, au = 0.0f;
 #pragma unroll
       for (int i = 0; i < NS; ++i) {

@@ -20,7 +20,7 @@
 
 namespace moe {
 
-constexpr int GEMV_TC = 4;   // tokens per pass over a wavefront's rows
+constexpr int GEMV_TC = 4;   // tokens per pass over a wavefront's rows (default)
 
 enum GemvMode { GEMV_GATEUP = 0, GEMV_DOWN_F32 = 1, GEMV_DOWN_BF16 = 2 };
 
@@ -65,12 +65,16 @@ __device__ __forceinline__ float bf16_chunk_dot(uint4 w, const uint32_t* xp, flo
 }
 
 // Grid: x = row blocks of 4*RW (gate/up: gate rows), y = token groups (routed:
-// the tokens of one expert; otherwise GEMV_TC consecutive tokens).
+// the tokens of one expert; otherwise TC consecutive tokens).
 // NC > 0: every row has at most 64*NC chunks; a wavefront loads all of its
 // rows' chunks (NC per lane) before any arithmetic and keeps them in
 // registers for every token pass, so it waits for memory once.  NC == 0:
 // rows of any length, one chunk per lane per loop iteration.
-template <bool NVFP4, int MODE, int RW, int NC = 0>
+// TC: tokens per pass.  Each pass holds TC tokens' activations and sums in
+// registers; with one or two tokens per expert group (decode of up to 16
+// tokens) TC = 1 leaves room for more wavefronts per SIMD, which hide the
+// load latency better than the shared weight chunks of a wider pass.
+template <bool NVFP4, int MODE, int RW, int NC = 0, int TC = GEMV_TC>
 __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
   constexpr int NR = (MODE == GEMV_GATEUP) ? 2 * RW : RW;   // weight rows per wavefront
   constexpr int XW = NVFP4 ? 16 : 4;                        // activation words per chunk
@@ -82,10 +86,10 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
     n_tok = a.g_count[grp];
     slot_base = a.g_offset[grp];
   } else {
-    // one group per GEMV_TC tokens (grid.y); a group's rows stay on one XCD
+    // one group per TC tokens (grid.y); a group's rows stay on one XCD
     // when gridDim.x is a multiple of 8, so the groups share its L2
-    slot_base = grp * GEMV_TC;
-    n_tok = min(GEMV_TC, a.T - slot_base);
+    slot_base = grp * TC;
+    n_tok = min(TC, a.T - slot_base);
     if (n_tok <= 0) return;
   }
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
@@ -132,24 +136,24 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
       }
     }
   }
-  for (int t0 = 0; t0 < n_tok; t0 += GEMV_TC) {
-    const int nt = min(GEMV_TC, n_tok - t0);
-    int in_row[GEMV_TC], out_row[GEMV_TC];
+  for (int t0 = 0; t0 < n_tok; t0 += TC) {
+    const int nt = min(TC, n_tok - t0);
+    int in_row[TC], out_row[TC];
 #pragma unroll
-    for (int t = 0; t < GEMV_TC; ++t) {
+    for (int t = 0; t < TC; ++t) {
       const int p = t0 + min(t, nt - 1);
       const int slot = a.n_groups ? a.g_slots[slot_base + p] : slot_base + p;
       out_row[t] = slot;
       in_row[t] = (a.n_groups && MODE == GEMV_GATEUP) ? slot / a.K : slot;
     }
-    float acc[NR][GEMV_TC];
+    float acc[NR][TC];
 #pragma unroll
     for (int r = 0; r < NR; ++r)
 #pragma unroll
-      for (int t = 0; t < GEMV_TC; ++t) acc[r][t] = 0.0f;
+      for (int t = 0; t < TC; ++t) acc[r][t] = 0.0f;
     auto chunk = [&](int c, const uint4 (&w)[NR], const uint32_t (&sc)[NR]) {
 #pragma unroll
-      for (int t = 0; t < GEMV_TC; ++t) {
+      for (int t = 0; t < TC; ++t) {
         if (t < nt) {
           uint32_t xp[XW];
           const uint4* xs = reinterpret_cast<const uint4*>(a.in + static_cast<int64_t>(in_row[t]) * a.cols +
@@ -198,7 +202,7 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
       }
     }
 #pragma unroll
-    for (int t = 0; t < GEMV_TC; ++t) {
+    for (int t = 0; t < TC; ++t) {
       if (t < nt) {
 #pragma unroll
         for (int r = 0; r < NR; ++r) acc[r][t] = wave_sum(acc[r][t]);
@@ -206,7 +210,7 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
     }
     if (lane == 0) {
 #pragma unroll
-      for (int t = 0; t < GEMV_TC; ++t) {
+      for (int t = 0; t < TC; ++t) {
         if (t >= nt) continue;
 #pragma unroll
         for (int r = 0; r < RW; ++r) {

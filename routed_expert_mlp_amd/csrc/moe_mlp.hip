@@ -284,7 +284,12 @@ void gemv(const GemvArgs& a, int groups, hipStream_t s, Ev ev) {
   const dim3 grid(static_cast<unsigned>(a.n_groups ? nrb : cdiv(nrb, 8) * 8), static_cast<unsigned>(groups));
   const int nch = NVFP4 ? (a.cols >> 5) : (a.cols >> 3);
   if constexpr (NVFP4) {
-    launch(k_gemv<NVFP4, MODE, RW, 0>, grid, dim3(256), s, ev.a, ev.b, a);
+    // up to 16 tokens an expert group holds at most 16 tokens (1.2 on average
+    // at 16): one token per pass
+    if (a.T <= 16)
+      launch(k_gemv<NVFP4, MODE, RW, 0, 1>, grid, dim3(256), s, ev.a, ev.b, a);
+    else
+      launch(k_gemv<NVFP4, MODE, RW, 0>, grid, dim3(256), s, ev.a, ev.b, a);
     return;
   } else {
   switch (static_cast<int>(cdiv(nch, 64))) {
@@ -404,7 +409,7 @@ const char* const kDenseStages[] = {"dense_gateup", "dense_down"};
 
 // The one-token decode kernels hold a row's chunks in registers: they take
 // H <= 4096 and I, Is <= 2048.
-constexpr int kDec1MaxH = 4096;
+constexpr int kDec1MaxH = DEC_MAX_H;
 
 // The few-token decode kernels (decode1.hpp) take up to 4 tokens (the MTP
 // verify shapes: one token plus up to three drafted ones), T*K <= 64 slots.
