@@ -29,6 +29,7 @@ fp64 CPU oracle timed on bounded samples on the host cores.
 """
 import argparse
 import ctypes
+import dataclasses
 import hashlib
 import json
 import os
@@ -578,7 +579,20 @@ def main():
                 extra[f"decode_t{T}"]["stage_us"] = {k: round(v * 1e3, 1) for k, v in st_t.items()}
             if T >= 64:
                 extra[f"decode_t{T}"]["weights"] = "routed NVFP4 in the tile layout (grouped-GEMM form)"
-        del wts_tiled
+        # one resident copy of the codes: the same copies with the row-major
+        # codes left out, so every kernel reads the tile-layout codes
+        one = [dataclasses.replace(x, w13_q=None, w2_q=None) for x in wts_tiled]
+        codes = w.E * (2 * w.I * w.H // 2 + w.H * w.I // 2)
+        scales = w.E * (2 * w.I * w.H // 16 + w.H * w.I // 16)
+        oc = {"t1": decode_line(cfg, w, one, xs, 1, dev, args.steps)}
+        xs16 = [x_dev(w, range(100 + r * 16, 100 + (r + 1) * 16), dev) for r in range(R)]
+        oc["t16"] = decode_line(cfg, w, one, xs16, 16, dev, max(40, args.steps // 4))
+        oc["resident_routed_weight_bytes"] = {
+            "tile_codes_only": codes + 2 * scales, "row_major_and_tile": 2 * (codes + scales),
+            "note": "tile-layout codes once, scales in both layouts (the decode kernels read row-major scales, "
+                    "the grouped GEMM tile-layout ones)"}
+        extra["decode_tile_codes_only"] = oc
+        del wts_tiled, one
     del calls
     del wts[1:]
     torch.cuda.empty_cache()

@@ -130,8 +130,14 @@ typedef struct moe_mlp_weights {
    * When a projection's codes AND scales are given, the grouped-GEMM form
    * (moe_mlp_prefill, decode from 64 tokens) reads them instead of the
    * row-major arrays wherever its NVFP4 tile kernel runs; the values and the
-   * arithmetic are the same, so the results are bitwise the same.  The
-   * row-major arrays stay required (the GEMV forms read them). */
+   * arithmetic are the same, so the results are bitwise the same.
+   * One resident copy of the codes: a projection's row-major codes (w13_q,
+   * w2_q) may be NULL when its tile-layout codes and scales are given; every
+   * kernel then reads the tile-layout codes (the decode forms with the
+   * row-major scales, which stay required), with bitwise the same results.
+   * This takes a reduction length (H for gate/up, I for down) that is a
+   * multiple of 256 and at least 512, and for the grouped-GEMM form T*H*2 and
+   * T*K*I*2 below 2^31 (else MOE_MLP_ERR_BAD_SHAPE). */
   const uint8_t*  w13_q_tiled;  /* moe_nvfp4_tile_pack(w13_q, w13_s, E, 2I, H, ...) codes */
   const uint8_t*  w13_s_tiled;  /* ... and scales */
   const uint8_t*  w2_q_tiled;   /* moe_nvfp4_tile_pack(w2_q, w2_s, E, H, I, ...) codes */

@@ -392,13 +392,26 @@ def _tileable(q: torch.Tensor) -> bool:
     return q.shape[-2] % 32 == 0 and (2 * q.shape[-1]) % 256 == 0
 
 
-def with_tiled_weights(w: Weights, stream=None) -> Weights:
+def with_tiled_weights(w: Weights, stream=None, drop_row_major_codes: bool = False) -> Weights:
     """A copy of w whose routed codes and scales also come in the tile layout,
     for each projection whose shape has one (rows a multiple of 32, columns a
-    multiple of 256); allocated by torch, the row-major tensors are shared."""
+    multiple of 256); allocated by torch, the row-major tensors are shared.
+
+    drop_row_major_codes: the copy keeps no reference to the row-major codes
+    of each packed projection whose reduction is at least 512 (w13_q / w2_q
+    become None): every kernel then reads the tile-layout codes, and the codes
+    are resident once (the row-major scales stay: the decode kernels read
+    them).  The caller frees the row-major codes by dropping its own
+    references."""
     q13 = s13 = q2 = s2 = None
+    rq13, rq2 = w.w13_q, w.w2_q
     if _tileable(w.w13_q):
         q13, s13 = moe_nvfp4_tile_pack(w.w13_q, w.w13_s, stream=stream)
+        if drop_row_major_codes and 2 * w.w13_q.shape[-1] >= 512:
+            rq13 = None
     if _tileable(w.w2_q):
         q2, s2 = moe_nvfp4_tile_pack(w.w2_q, w.w2_s, stream=stream)
-    return dataclasses.replace(w, w13_q_tiled=q13, w13_s_tiled=s13, w2_q_tiled=q2, w2_s_tiled=s2)
+        if drop_row_major_codes and 2 * w.w2_q.shape[-1] >= 512:
+            rq2 = None
+    return dataclasses.replace(w, w13_q=rq13, w2_q=rq2, w13_q_tiled=q13, w13_s_tiled=s13, w2_q_tiled=q2,
+                               w2_s_tiled=s2)

@@ -175,6 +175,23 @@ __device__ __forceinline__ float swiglu_clamped(float g, float u, float L) {
 
 // s_waitcnt immediate that waits until at most n vector-memory operations are
 // outstanding (expcnt and lgkmcnt left unconstrained).
+// 16-byte position of code piece q (0..3) of weight row p inside a 64-byte
+// row unit of the NVFP4 tile layout: q ^ f4_swz_c(p).
+__host__ __device__ __forceinline__ int f4_swz_c(int p) { return ((p >> 1) & 3) ^ ((p >> 3) & 1); }
+
+// Byte offset of 16-byte code chunk c (columns 32c .. 32c+31) of row R of an
+// NVFP4 code matrix with `cols` columns.  Row-major: R * cols/2 + 16 c.  Tile
+// layout (moe_nvfp4_tile_pack; rows % 32 == 0, cols % 256 == 0): 1 KB blocks
+// of 16 rows x 128 columns, row-group major; inside a block row r's four
+// pieces sit at 16 (4 r + (q ^ f4_swz_c(r))).
+template <bool TILED>
+__device__ __forceinline__ int64_t nvfp4_code_off(int64_t R, int c, int cols) {
+  if (TILED)
+    return ((R >> 4) * (cols >> 7) + (c >> 2)) * 1024 +
+           16 * (4 * static_cast<int>(R & 15) + ((c & 3) ^ f4_swz_c(static_cast<int>(R & 15))));
+  return R * (cols >> 1) + 16 * static_cast<int64_t>(c);
+}
+
 __host__ __device__ constexpr int waitcnt_vm(int n) {
   return (n & 0xF) | (0x7 << 4) | (0xF << 8) | ((n >> 4) << 14);
 }

@@ -20,6 +20,11 @@
 //
 // Each wavefront issues all loads of its rows before using any of them, so a
 // wavefront has its whole share of the weight stream in flight at once.
+//
+// CT (template flag of the NVFP4 kernels): the routed codes are read from the
+// tile layout of moe_nvfp4_tile_pack instead of the row-major array
+// (nvfp4_code_off); a lane still reads the same 16-byte chunk of the same
+// row, so nothing after the load changes.  The scales stay row-major.
 #pragma once
 
 #include "common.hpp"
@@ -224,7 +229,7 @@ __global__ __launch_bounds__(256) void k_dec_logits_shared_t(const uint16_t* __r
 // Wavefront 0 of the first block of each token's slot 0 runs all K rounds
 // and writes ids/wts (and ids_out / w_out when not null).
 // -------------------------------------------------------------------------
-template <int RJ, int NC, bool EXACT, int NJ, class G>
+template <int RJ, int NC, bool EXACT, int NJ, class G, bool CT = false>
 __global__ __launch_bounds__(256) void k_dec_gateup(const uint16_t* __restrict__ x, const uint8_t* __restrict__ q13,
                                                     const uint8_t* __restrict__ s13, const float* __restrict__ g13,
                                                     const float* __restrict__ logits, const float* __restrict__ bias,
@@ -265,8 +270,8 @@ __global__ __launch_bounds__(256) void k_dec_gateup(const uint16_t* __restrict__
     for (int i = 0; i < NC; ++i) {
       const int c = lane + 64 * i;
       const bool ok = EXACT || c < nch;
-      cg[r][i] = ok ? *reinterpret_cast<const uint4*>(qe + j * rq + 16 * c) : make_uint4(0, 0, 0, 0);
-      cu[r][i] = ok ? *reinterpret_cast<const uint4*>(qe + (I + j) * rq + 16 * c) : make_uint4(0, 0, 0, 0);
+      cg[r][i] = ok ? *reinterpret_cast<const uint4*>(qe + nvfp4_code_off<CT>(j, c, H)) : make_uint4(0, 0, 0, 0);
+      cu[r][i] = ok ? *reinterpret_cast<const uint4*>(qe + nvfp4_code_off<CT>(I + j, c, H)) : make_uint4(0, 0, 0, 0);
       sg[r][i] = ok ? *reinterpret_cast<const uint16_t*>(se + j * rs + 2 * c) : 0u;
       su[r][i] = ok ? *reinterpret_cast<const uint16_t*>(se + (I + j) * rs + 2 * c) : 0u;
     }
@@ -329,7 +334,7 @@ __global__ __launch_bounds__(256) void k_dec_gateup(const uint16_t* __restrict__
 // -------------------------------------------------------------------------
 constexpr int DEC_MAX_T = 4;
 
-template <int R, int NW, int NP, int NSC, class G>
+template <int R, int NW, int NP, int NSC, class G, bool CT = false>
 __global__ __launch_bounds__(NW * 64) void k_dec_down_combine(
     const uint16_t* __restrict__ h, const uint8_t* __restrict__ q2, const uint8_t* __restrict__ s2,
     const float* __restrict__ g2, const uint16_t* __restrict__ sw2, const uint16_t* __restrict__ hs, int Is_,
@@ -396,7 +401,8 @@ __global__ __launch_bounds__(NW * 64) void k_dec_down_combine(
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const int64_t base = static_cast<int64_t>(e[p]) * H + min(r0 + r, H - 1);
-      cw[p][r] = *reinterpret_cast<const uint4*>(q2 + base * rq + 16 * dl);
+      cw[p][r] = *reinterpret_cast<const uint4*>(q2 + static_cast<int64_t>(e[p]) * H * rq +
+                                                 nvfp4_code_off<CT>(min(r0 + r, H - 1), dl, I));
       sc[p][r] = *reinterpret_cast<const uint16_t*>(s2 + base * rs + 2 * dl);
     }
   }
@@ -479,7 +485,7 @@ __global__ __launch_bounds__(NW * 64) void k_dec_down_combine(
 // k_dec_down_combine, so the two kernels agree bit for bit.
 //   requires K + NSW <= 16, I <= 2048 (one chunk per lane and row)
 // -------------------------------------------------------------------------
-template <int R, int NSW, int NSC, class G>
+template <int R, int NSW, int NSC, class G, bool CT = false>
 __global__ __launch_bounds__(1024) void k_dec_down_combine1(
     const uint16_t* __restrict__ h, const uint8_t* __restrict__ q2, const uint8_t* __restrict__ s2,
     const float* __restrict__ g2, const uint16_t* __restrict__ sw2, const uint16_t* __restrict__ hs, int Is_,
@@ -514,7 +520,8 @@ __global__ __launch_bounds__(1024) void k_dec_down_combine1(
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const int64_t base = static_cast<int64_t>(e) * H + min(r0 + r, H - 1);
-      cw[r] = *reinterpret_cast<const uint4*>(q2 + base * rq + 16 * dl);
+      cw[r] = *reinterpret_cast<const uint4*>(q2 + static_cast<int64_t>(e) * H * rq +
+                                              nvfp4_code_off<CT>(min(r0 + r, H - 1), dl, I));
       sc[r] = *reinterpret_cast<const uint16_t*>(s2 + base * rs + 2 * dl);
     }
     const float gk = g2[e];

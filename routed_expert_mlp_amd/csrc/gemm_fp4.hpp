@@ -68,8 +68,7 @@ constexpr int F4_THREADS = 512;    // 8 wavefronts
 // lanes (rows r..r+7 get distinct positions, and so do the even and the odd
 // rows among r..r+15).
 __device__ __forceinline__ int f4_swz_a(int r) { return (r & 7) ^ ((r >> 3) & 1); }
-// 16-byte position of code piece q (0..3) of weight row p: q ^ f4_swz_c(p).
-__device__ __forceinline__ int f4_swz_c(int p) { return ((p >> 1) & 3) ^ ((p >> 3) & 1); }
+// (f4_swz_c, the code-piece swizzle, is in common.hpp: the decode kernels read the tile layout too.)
 
 // LDS of one workgroup: every ring slot is an array of its own (activations
 // four, codes two, scales two), so that the compiler's wait insertion can tell

@@ -70,11 +70,12 @@ __device__ __forceinline__ float bf16_chunk_dot(uint4 w, const uint32_t* xp, flo
 // rows' chunks (NC per lane) before any arithmetic and keeps them in
 // registers for every token pass, so it waits for memory once.  NC == 0:
 // rows of any length, one chunk per lane per loop iteration.
+// CT: routed codes in the tile layout (nvfp4_code_off), scales row-major.
 // TC: tokens per pass.  Each pass holds TC tokens' activations and sums in
 // registers; with one or two tokens per expert group (decode of up to 16
 // tokens) TC = 1 leaves room for more wavefronts per SIMD, which hide the
 // load latency better than the shared weight chunks of a wider pass.
-template <bool NVFP4, int MODE, int RW, int NC = 0, int TC = GEMV_TC>
+template <bool NVFP4, int MODE, int RW, int NC = 0, int TC = GEMV_TC, bool CT = false>
 __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
   constexpr int NR = (MODE == GEMV_GATEUP) ? 2 * RW : RW;   // weight rows per wavefront
   constexpr int XW = NVFP4 ? 16 : 4;                        // activation words per chunk
@@ -96,7 +97,6 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
   const int r0 = blockIdx.x * (4 * RW) + wv * RW;            // first (gate) row of this wavefront
   if (r0 >= a.half_rows) return;
   const int nch = NVFP4 ? (a.cols >> 5) : (a.cols >> 3);     // 16-byte chunks per row
-  const int64_t row_q = NVFP4 ? (a.cols >> 1) : 0;           // code bytes per row
   const int64_t row_s = a.cols >> 4;                         // scale bytes per row
   const uint8_t* wq = NVFP4 ? a.wq + e * a.stride_q : nullptr;
   const uint8_t* wsc = NVFP4 ? a.ws + e * a.stride_s : nullptr;
@@ -126,7 +126,7 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
 #pragma unroll
       for (int r = 0; r < NR; ++r) {
         if (NVFP4) {
-          wr[r][i] = ok ? *reinterpret_cast<const uint4*>(wq + rows[r] * row_q + 16 * c) : make_uint4(0, 0, 0, 0);
+          wr[r][i] = ok ? *reinterpret_cast<const uint4*>(wq + nvfp4_code_off<CT>(rows[r], c, a.cols)) : make_uint4(0, 0, 0, 0);
           scr[r][i] = ok ? *reinterpret_cast<const uint16_t*>(wsc + rows[r] * row_s + 2 * c) : 0u;
         } else {
           wr[r][i] = ok ? *reinterpret_cast<const uint4*>(a.wb + static_cast<int64_t>(rows[r]) * a.cols + 8 * c)
@@ -191,7 +191,7 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
 #pragma unroll
         for (int r = 0; r < NR; ++r) {
           if (NVFP4) {
-            w[r] = *reinterpret_cast<const uint4*>(wq + rows[r] * row_q + 16 * c);
+            w[r] = *reinterpret_cast<const uint4*>(wq + nvfp4_code_off<CT>(rows[r], c, a.cols));
             sc[r] = *reinterpret_cast<const uint16_t*>(wsc + rows[r] * row_s + 2 * c);
           } else {
             w[r] = *reinterpret_cast<const uint4*>(a.wb + static_cast<int64_t>(rows[r]) * a.cols + 8 * c);

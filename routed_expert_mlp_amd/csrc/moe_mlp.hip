@@ -184,12 +184,14 @@ int validate_weights(const moe_mlp_config* c, const moe_mlp_weights* w) {
       need[n++] = w->shared_w2;
     }
   } else {
+    // a projection's codes: the row-major array, or the tile-layout codes and
+    // scales (then every kernel reads the tile-layout codes; see codes13)
     need[n++] = w->router_w;
     need[n++] = w->router_bias;
-    need[n++] = w->w13_q;
+    need[n++] = w->w13_q ? w->w13_q : (w->w13_s_tiled ? w->w13_q_tiled : nullptr);
     need[n++] = w->w13_s;
     need[n++] = w->w13_g;
-    need[n++] = w->w2_q;
+    need[n++] = w->w2_q ? w->w2_q : (w->w2_s_tiled ? w->w2_q_tiled : nullptr);
     need[n++] = w->w2_s;
     need[n++] = w->w2_g;
     if (c->n_shared_experts) {
@@ -205,6 +207,11 @@ int validate_weights(const moe_mlp_config* c, const moe_mlp_weights* w) {
     const void* opt[4] = {w->w13_q_tiled, w->w13_s_tiled, w->w2_q_tiled, w->w2_s_tiled};
     for (const void* q : opt)
       if (q && !aligned(q)) return MOE_MLP_ERR_MISALIGNED;
+    // tile-layout codes only: the shapes the tile layout and its grouped GEMM
+    // take (a reduction of at least 512 and a multiple of 256)
+    if ((!w->w13_q && (c->hidden % 256 != 0 || c->hidden < 512)) ||
+        (!w->w2_q && (c->moe_intermediate % 256 != 0 || c->moe_intermediate < 512)))
+      return MOE_MLP_ERR_BAD_SHAPE;
   }
   return MOE_MLP_OK;
 }
@@ -222,6 +229,18 @@ struct Ev {
 template <typename F, typename... Args>
 void launch(F kernel, dim3 grid, dim3 block, hipStream_t s, hipEvent_t e0, hipEvent_t e1, Args... args) {
   hipExtLaunchKernelGGL(kernel, grid, block, 0, s, e0, e1, 0, args...);
+}
+
+// Routed NVFP4 codes that the kernels read: the row-major array, or (when it
+// is not given) the tile-layout copy; the kernels take the layout as a
+// template flag (true = tile layout).
+const uint8_t* codes13(const moe_mlp_weights* w) { return w->w13_q ? w->w13_q : w->w13_q_tiled; }
+const uint8_t* codes2(const moe_mlp_weights* w) { return w->w2_q ? w->w2_q : w->w2_q_tiled; }
+
+template <typename F>
+void with_ct(bool tiled, F&& f) {
+  if (tiled) f(std::true_type{});
+  else f(std::false_type{});
 }
 
 // Calls f(std::integral_constant<int, NJ>) with the smallest supported NJ >= E / 64
@@ -275,7 +294,7 @@ void router_logits(const uint16_t* x, const float* wr, float* logits, int64_t T,
 // occupancy, and holding their chunks (with 16 activation words per chunk
 // and token) costs more registers than it saves in waits (measured).
 template <bool NVFP4, int MODE, int RW>
-void gemv(const GemvArgs& a, int groups, hipStream_t s, Ev ev) {
+void gemv(const GemvArgs& a, int groups, hipStream_t s, Ev ev, bool tiled_codes = false) {
   // without expert groups the tokens go in groups of GEMV_TC over grid.y, and
   // grid.x is a multiple of 8: blocks go to the 8 XCDs round-robin, so every
   // token group of a row block runs on the same XCD and reads its rows from L2
@@ -286,10 +305,13 @@ void gemv(const GemvArgs& a, int groups, hipStream_t s, Ev ev) {
   if constexpr (NVFP4) {
     // up to 16 tokens an expert group holds at most 16 tokens (1.2 on average
     // at 16): one token per pass
-    if (a.T <= 16)
-      launch(k_gemv<NVFP4, MODE, RW, 0, 1>, grid, dim3(256), s, ev.a, ev.b, a);
-    else
-      launch(k_gemv<NVFP4, MODE, RW, 0>, grid, dim3(256), s, ev.a, ev.b, a);
+    with_ct(tiled_codes, [&](auto ctc) {
+      constexpr bool CT = decltype(ctc)::value;
+      if (a.T <= 16)
+        launch(k_gemv<NVFP4, MODE, RW, 0, 1, CT>, grid, dim3(256), s, ev.a, ev.b, a);
+      else
+        launch(k_gemv<NVFP4, MODE, RW, 0, GEMV_TC, CT>, grid, dim3(256), s, ev.a, ev.b, a);
+    });
     return;
   } else {
   switch (static_cast<int>(cdiv(nch, 64))) {
@@ -456,18 +478,22 @@ void dec_gateup(const moe_mlp_config* c, const moe_mlp_weights* w, const uint16_
   constexpr int NC = 2;
   const int H = c->hidden, I = c->moe_intermediate, K = c->top_k;
   const unsigned grid = static_cast<unsigned>(T * K * cdiv(I, 4 * kDecRJ));
+  const uint8_t* q13 = codes13(w);
   auto go = [&](auto kern) {
-    launch(kern, dim3(grid), dim3(256), s, ev.a, ev.b, x, w->w13_q, w->w13_s, w->w13_g, logits, w->router_bias, K,
+    launch(kern, dim3(grid), dim3(256), s, ev.a, ev.b, x, q13, w->w13_s, w->w13_g, logits, w->router_bias, K,
            c->routed_scaling_factor, ids, wts, ids_out, w_out, c->num_experts, H, I, c->swiglu_limit, h);
   };
-  if (glm_flash_geometry(c)) {
-    go(k_dec_gateup<kDecRJ, NC, true, 5, DecGeoFlash>);
-    return;
-  }
-  with_nj(c->num_experts, [&](auto nj) {
-    constexpr int NJ = decltype(nj)::value;
-    if (H == 64 * 32 * NC) go(k_dec_gateup<kDecRJ, NC, true, NJ, DecGeoAny>);     // every lane holds NC chunks
-    else go(k_dec_gateup<kDecRJ, NC, false, NJ, DecGeoAny>);
+  with_ct(!w->w13_q, [&](auto ctc) {
+    constexpr bool CT = decltype(ctc)::value;
+    if (glm_flash_geometry(c)) {
+      go(k_dec_gateup<kDecRJ, NC, true, 5, DecGeoFlash, CT>);
+      return;
+    }
+    with_nj(c->num_experts, [&](auto nj) {
+      constexpr int NJ = decltype(nj)::value;
+      if (H == 64 * 32 * NC) go(k_dec_gateup<kDecRJ, NC, true, NJ, DecGeoAny, CT>);     // every lane holds NC chunks
+      else go(k_dec_gateup<kDecRJ, NC, false, NJ, DecGeoAny, CT>);
+    });
   });
 }
 
@@ -480,20 +506,24 @@ void launch_down_combine(const moe_mlp_config* c, const moe_mlp_weights* w, cons
   const int H = c->hidden;
   const int Is = c->n_shared_experts ? c->shared_intermediate : 0;
   const dim3 grid(static_cast<unsigned>(cdiv(H, R))), block(NW * 64);
+  const uint8_t* q2 = codes2(w);
   auto go = [&](auto kern) {
-    launch(kern, grid, block, s, ev.a, ev.b, h, w->w2_q, w->w2_s, w->w2_g, w->shared_w2, hs, Is, ids, wts,
+    launch(kern, grid, block, s, ev.a, ev.b, h, q2, w->w2_s, w->w2_g, w->shared_w2, hs, Is, ids, wts,
            c->num_experts, c->top_k, H, c->moe_intermediate, out, T);
   };
-  if (glm_flash_geometry(c)) {
-    go(k_dec_down_combine<R, NW, NP, 3, DecGeoFlash>);
-    return;
-  }
-  switch (static_cast<int>(cdiv(Is / 8, 64))) {
-    case 0: case 1: go(k_dec_down_combine<R, NW, NP, 1, DecGeoAny>); break;
-    case 2: go(k_dec_down_combine<R, NW, NP, 2, DecGeoAny>); break;
-    case 3: go(k_dec_down_combine<R, NW, NP, 3, DecGeoAny>); break;
-    default: go(k_dec_down_combine<R, NW, NP, 4, DecGeoAny>); break;
-  }
+  with_ct(!w->w2_q, [&](auto ctc) {
+    constexpr bool CT = decltype(ctc)::value;
+    if (glm_flash_geometry(c)) {
+      go(k_dec_down_combine<R, NW, NP, 3, DecGeoFlash, CT>);
+      return;
+    }
+    switch (static_cast<int>(cdiv(Is / 8, 64))) {
+      case 0: case 1: go(k_dec_down_combine<R, NW, NP, 1, DecGeoAny, CT>); break;
+      case 2: go(k_dec_down_combine<R, NW, NP, 2, DecGeoAny, CT>); break;
+      case 3: go(k_dec_down_combine<R, NW, NP, 3, DecGeoAny, CT>); break;
+      default: go(k_dec_down_combine<R, NW, NP, 4, DecGeoAny, CT>); break;
+    }
+  });
 }
 
 // One token: 16 output rows per block, a wavefront per routed slot and 4 for
@@ -506,20 +536,24 @@ void launch_down_combine1(const moe_mlp_config* c, const moe_mlp_weights* w, con
   const int H = c->hidden, K = c->top_k;
   const int Is = c->n_shared_experts ? c->shared_intermediate : 0;
   const dim3 grid(static_cast<unsigned>(cdiv(H, R))), block(static_cast<unsigned>((K + NSW) * 64));
+  const uint8_t* q2 = codes2(w);
   auto go = [&](auto kern) {
-    launch(kern, grid, block, s, ev.a, ev.b, h, w->w2_q, w->w2_s, w->w2_g, w->shared_w2, hs, Is, ids, wts,
+    launch(kern, grid, block, s, ev.a, ev.b, h, q2, w->w2_s, w->w2_g, w->shared_w2, hs, Is, ids, wts,
            c->num_experts, K, H, c->moe_intermediate, out);
   };
-  if (glm_flash_geometry(c)) {
-    go(k_dec_down_combine1<R, NSW, 3, DecGeoFlash>);
-    return;
-  }
-  switch (static_cast<int>(cdiv(Is / 8, 64))) {
-    case 0: case 1: go(k_dec_down_combine1<R, NSW, 1, DecGeoAny>); break;
-    case 2: go(k_dec_down_combine1<R, NSW, 2, DecGeoAny>); break;
-    case 3: go(k_dec_down_combine1<R, NSW, 3, DecGeoAny>); break;
-    default: go(k_dec_down_combine1<R, NSW, 4, DecGeoAny>); break;
-  }
+  with_ct(!w->w2_q, [&](auto ctc) {
+    constexpr bool CT = decltype(ctc)::value;
+    if (glm_flash_geometry(c)) {
+      go(k_dec_down_combine1<R, NSW, 3, DecGeoFlash, CT>);
+      return;
+    }
+    switch (static_cast<int>(cdiv(Is / 8, 64))) {
+      case 0: case 1: go(k_dec_down_combine1<R, NSW, 1, DecGeoAny, CT>); break;
+      case 2: go(k_dec_down_combine1<R, NSW, 2, DecGeoAny, CT>); break;
+      case 3: go(k_dec_down_combine1<R, NSW, 3, DecGeoAny, CT>); break;
+      default: go(k_dec_down_combine1<R, NSW, 4, DecGeoAny, CT>); break;
+    }
+  });
 }
 
 // Few-token decode with FP8 experts: launches 2 and 3 of decode_fp8.hpp.
@@ -622,6 +656,13 @@ int run_layer(const moe_mlp_config* c, const moe_mlp_weights* w, const uint16_t*
   if (is_routed(c) && ((ids_out && !aligned(ids_out)) || (w_out && !aligned(w_out))))
     return MOE_MLP_ERR_MISALIGNED;
   if (!decode1_ok(c, T, prefill)) prefill = gemm_form(c, T, prefill);   // from here on: the form that runs
+  // with tile-layout codes only, the grouped GEMM must take its tile kernel,
+  // whose 32-bit DMA offsets bound the activation rows (tokens, slots) times
+  // the reduction length
+  if (prefill && c->kind == MOE_MLP_KIND_ROUTED &&
+      ((!w->w13_q && T * c->hidden * 2 >= (int64_t(1) << 31)) ||
+       (!w->w2_q && T * c->top_k * c->moe_intermediate * 2 >= (int64_t(1) << 31))))
+    return MOE_MLP_ERR_BAD_SHAPE;
   const Plan p = make_plan(c, T, prefill);
   if (ws_bytes < p.total) return MOE_MLP_ERR_WORKSPACE_TOO_SMALL;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -794,7 +835,7 @@ int run_layer(const moe_mlp_config* c, const moe_mlp_weights* w, const uint16_t*
     r.K = K;
     r.limit = L;
     GemvArgs gu = r;
-    gu.wq = w->w13_q;
+    gu.wq = codes13(w);
     gu.ws = w->w13_s;
     gu.stride_q = int64_t(2) * I * H / 2;
     gu.stride_s = int64_t(2) * I * H / 16;
@@ -803,11 +844,11 @@ int run_layer(const moe_mlp_config* c, const moe_mlp_weights* w, const uint16_t*
     gu.cols = H;
     gu.in = x;
     gu.out = h;
-    gemv<true, GEMV_GATEUP, 2>(gu, groups, s, ev(3));
+    gemv<true, GEMV_GATEUP, 2>(gu, groups, s, ev(3), !w->w13_q);
     if (Is) gemv<false, GEMV_DOWN_F32, 2>(bf16_gemv_args(w->shared_w2, H, Is, Ti, hs, ys, L), 1, s, ev(4));
     else empty_stage(ev(4));
     GemvArgs gd = r;
-    gd.wq = w->w2_q;
+    gd.wq = codes2(w);
     gd.ws = w->w2_s;
     gd.stride_q = int64_t(H) * I / 2;
     gd.stride_s = int64_t(H) * I / 16;
@@ -816,7 +857,7 @@ int run_layer(const moe_mlp_config* c, const moe_mlp_weights* w, const uint16_t*
     gd.cols = I;
     gd.in = h;
     gd.out = y;
-    gemv<true, GEMV_DOWN_F32, 4>(gd, groups, s, ev(5));
+    gemv<true, GEMV_DOWN_F32, 4>(gd, groups, s, ev(5), !w->w2_q);
   }
   const int64_t nq = T * (H / 4);
   const Ev ce = ev(prefill ? 7 : 6);

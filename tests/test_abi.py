@@ -116,7 +116,26 @@ def test_zero_tokens_is_a_noop(entry):
 @pytest.mark.parametrize("missing", ["router_w", "router_bias", "w13_q", "w13_s", "w13_g", "w2_q", "w2_s",
                                      "w2_g", "shared_w13", "shared_w2"])
 def test_missing_weights(entry, missing):
-    assert call(entry, cfg(), full_weights(**{missing: None})) == capi.ERR_KIND_MISMATCH
+    # without tile-layout codes the row-major codes are required
+    off = {missing: None, "w13_q_tiled": None, "w13_s_tiled": None, "w2_q_tiled": None, "w2_s_tiled": None}
+    assert call(entry, cfg(), full_weights(**off)) == capi.ERR_KIND_MISMATCH
+
+
+@pytest.mark.parametrize("entry", ENTRIES)
+@pytest.mark.parametrize("proj", ["w13", "w2"])
+def test_tiled_only_codes_rules(entry, proj):
+    """Row-major codes may be left out when the projection's tile-layout codes
+    AND scales are given, for reductions (H for gate/up, I for down) that are
+    a multiple of 256 and at least 512; otherwise the call is refused before
+    anything runs."""
+    # tiled codes without tiled scales: the codes count as missing
+    assert call(entry, cfg(hidden=512, moe_intermediate=512),
+                full_weights(**{f"{proj}_q": None, f"{proj}_s_tiled": None})) == capi.ERR_KIND_MISMATCH
+    # reduction below 512 or not a multiple of 256: no tile kernel for it
+    small = dict(hidden=256, moe_intermediate=256)
+    assert call(entry, cfg(**small), full_weights(**{f"{proj}_q": None})) == capi.ERR_BAD_SHAPE
+    odd = dict(hidden=768 + 32, moe_intermediate=768 + 32)
+    assert call(entry, cfg(**odd), full_weights(**{f"{proj}_q": None})) == capi.ERR_BAD_SHAPE
 
 
 @pytest.mark.parametrize("entry", ENTRIES)

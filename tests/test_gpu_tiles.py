@@ -57,10 +57,12 @@ def test_tile_pack_matches_layout(mats, rows, cols):
     assert np.array_equal(st.cpu().numpy(), tiled_scales(s))
 
 
-def _run_both(d: DeviceRouted, what: str, prefill=True):
+def _run_both(d: DeviceRouted, what: str, prefill=True, drop=False):
     out0, ids0, w0 = d.run(prefill)
     plain = d.weights
-    d.weights = capi.with_tiled_weights(plain)
+    d.weights = capi.with_tiled_weights(plain, drop_row_major_codes=drop)
+    if drop:
+        say(f"[case] row-major codes left out: w13_q {d.weights.w13_q is None}, w2_q {d.weights.w2_q is None}")
     try:
         out1, ids1, w1 = d.run(prefill)
     finally:
@@ -101,3 +103,27 @@ def test_tiled_weights_decode_bitwise(T):
     w = synth.workload("ragged_decode", T=T, H=512, I=512, E=16, K=4, Is=128)
     say(f"[case] tiled weights, decode T={w.T} H={w.H} I={w.I} E={w.E} K={w.K}")
     _run_both(DeviceRouted(RoutedInputs(w)), f"decode T={T}", prefill=False)
+
+
+# One resident copy of the codes: the row-major codes left out, every kernel
+# (one-token and few-token decode, GEMV decode, grouped GEMM) reads the
+# tile-layout codes; the bytes and the arithmetic are the same, so the results
+# are bitwise those of the row-major run.  H=512, I=256 leaves out only the
+# gate/up codes (the down reduction is below 512), so the two layouts mix.
+ONE_COPY = [dict(T=1, H=512, I=512), dict(T=3, H=512, I=512), dict(T=16, H=512, I=512),
+            dict(T=40, H=512, I=512), dict(T=64, H=512, I=512), dict(T=16, H=512, I=256),
+            dict(T=1, H=512, I=256)]
+
+
+@pytest.mark.parametrize("o", ONE_COPY, ids=[f"T{o['T']}_H{o['H']}_I{o['I']}" for o in ONE_COPY])
+def test_tiled_codes_only_decode_bitwise(o):
+    w = synth.workload("ragged_decode", T=o["T"], H=o["H"], I=o["I"], E=16, K=4, Is=128)
+    say(f"[case] tile-layout codes only, decode T={w.T} H={w.H} I={w.I} E={w.E} K={w.K}")
+    _run_both(DeviceRouted(RoutedInputs(w)), f"codes tiled only, decode T={o['T']}", prefill=False, drop=True)
+
+
+@pytest.mark.parametrize("name,prefill", [("flash_decode_t1", False), ("flash_decode_t16", False),
+                                          ("prefill_t4096", True)])
+def test_tiled_codes_only_full_size_bitwise(name, prefill):
+    say(f"[case] tile-layout codes only, {name}")
+    _run_both(device_workload(name), f"codes tiled only, {name}", prefill=prefill, drop=True)
