@@ -22,6 +22,7 @@
 #include "gemm_bf16.hpp"
 #include "gemm_fp4.hpp"
 #include "gemm_fp8.hpp"
+#include "gemm_fp8d.hpp"
 #include "gemv.hpp"
 #include "permute.hpp"
 #include "router.hpp"
@@ -324,6 +325,24 @@ void gemv(const GemvArgs& a, int groups, hipStream_t s, Ev ev, bool tiled_codes 
     default: launch(k_gemv<NVFP4, MODE, RW, 0>, grid, dim3(256), s, ev.a, ev.b, a); break;
   }
   }
+}
+
+// Routed FP8 projections: k_gemm_f8d (LDS DMA rings) when its 32-bit DMA
+// offsets hold (activation rows and weight rows times the row length below
+// 2^31) and the reduction is at most 8192; otherwise k_gemm_f8.
+template <int MODE>
+void gemm_fp8(const GemmArgs& a0, int64_t m_tiles, hipStream_t s, Ev ev) {
+  GemmArgs a = a0;
+  const int64_t w_rows = MODE == GEMM_GATEUP ? 2 * int64_t(a.half_n) : int64_t(a.half_n);
+  if (a.kdim <= 8192 && int64_t(a.T) * a.kdim * 2 < (int64_t(1) << 31) && w_rows * a.kdim < (int64_t(1) << 31)) {
+    a.n_blocks = static_cast<int>(cdiv(a.half_n, MODE == GEMM_GATEUP ? F8D_WROWS / 2 : F8D_WROWS));
+    const dim3 grid(static_cast<unsigned>(8 * cdiv(m_tiles * a.n_blocks, 8)));
+    launch(k_gemm_f8d<MODE>, grid, dim3(F8D_THREADS), s, ev.a, ev.b, a);
+    return;
+  }
+  const dim3 grid(static_cast<unsigned>(m_tiles),
+                  static_cast<unsigned>(cdiv(a.half_n, MODE == GEMM_GATEUP ? 128 : 256)));
+  launch(k_gemm_f8<MODE>, grid, dim3(256), s, ev.a, ev.b, a);
 }
 
 // Routed NVFP4 projections with a reduction length that is a multiple of 256
@@ -774,8 +793,7 @@ int run_layer(const moe_mlp_config* c, const moe_mlp_weights* w, const uint16_t*
       gu.stride_q = int64_t(2) * I * H;
       gu.stride_s = int64_t(2) * (I / MOE_MLP_FP8_BLOCK) * (H / MOE_MLP_FP8_BLOCK);
       gu.gscale = nullptr;
-      launch(k_gemm_f8<GEMM_GATEUP>, dim3(static_cast<unsigned>(p.max_tiles), static_cast<unsigned>(cdiv(I, 128))),
-             dim3(256), s, ev(3).a, ev(3).b, gu);
+      gemm_fp8<GEMM_GATEUP>(gu, p.max_tiles, s, ev(3));
     } else {
       gemm<true, GEMM_GATEUP, true>(gu, p.max_tiles, s, ev(3));
     }
@@ -804,9 +822,7 @@ int run_layer(const moe_mlp_config* c, const moe_mlp_weights* w, const uint16_t*
       gd.stride_q = int64_t(H) * I;
       gd.stride_s = int64_t(H / MOE_MLP_FP8_BLOCK) * (I / MOE_MLP_FP8_BLOCK);
       gd.gscale = nullptr;
-      launch(k_gemm_f8<GEMM_DOWN_SLOT_F32>,
-             dim3(static_cast<unsigned>(p.max_tiles), static_cast<unsigned>(cdiv(H, 256))), dim3(256), s, ev(4).a,
-             ev(4).b, gd);
+      gemm_fp8<GEMM_DOWN_SLOT_F32>(gd, p.max_tiles, s, ev(4));
     } else {
       gemm<true, GEMM_DOWN_SLOT_F32, true>(gd, p.max_tiles, s, ev(4));
     }
