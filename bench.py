@@ -573,7 +573,7 @@ def main():
                     wts_tiled = [capi.with_tiled_weights(x) for x in wts]
                 wts_t = wts_tiled
             extra[f"decode_t{T}"] = decode_line(cfg, w, wts_t, xs_t, T, dev, max(40, args.steps // 4))
-            if T == 16:
+            if T in (16, 64):
                 outs_t = [torch.empty((T, w.H), dtype=torch.bfloat16, device=dev) for _ in range(R)]
                 st_t = stage_times(cfg, wts_t, xs_t, outs_t, False, 4 * R, ev, capi.workspace(cfg, T, False, dev))
                 extra[f"decode_t{T}"]["stage_us"] = {k: round(v * 1e3, 1) for k, v in st_t.items()}

@@ -82,7 +82,7 @@ extern "C" {
 #define MOE_MLP_MAX_TOP_K      16    /* Module glm5next_mlp, Constants, KERNEL_MAX_TOP_K */
 #define MOE_MLP_MAX_EXPERTS    1024  /* one wavefront holds at most 16 scores per lane */
 #define MOE_MLP_DECODE_MAX_T   256   /* moe_mlp_decode handles up to this many tokens */
-#define MOE_MLP_NOALLOC_SCRATCH_BYTES (32u << 20)   /* scratch of moe_mlp_decode_noalloc, per device */
+#define MOE_MLP_NOALLOC_SCRATCH_BYTES (64u << 20)   /* scratch of moe_mlp_decode_noalloc, per device */
 
 #define MOE_MLP_KIND_ROUTED 0   /* router + routed NVFP4 experts + optional shared expert */
 #define MOE_MLP_KIND_DENSE  1   /* dense BF16 FFN (layers before first_k_dense_replace) */
@@ -192,7 +192,7 @@ int moe_mlp_decode(const moe_mlp_config* cfg, const moe_mlp_weights* w, const ui
  * passes x, out, ids_out, w_out (as moe_mlp_decode) and enqueues on `stream`
  * of the current device.  Returns MOE_MLP_ERR_SCRATCH_LIMIT, before anything
  * is enqueued, when moe_mlp_workspace_size(cfg, T, 0) exceeds the array
- * (at H=4096, I=Is=1536, E=288, K=8: up to about 140 tokens fit).  Every call
+ * (at H=4096, I=Is=1536, E=288, K=8: up to about 100 tokens fit).  Every call
  * on one GPU uses that GPU's one array, which keeps the last call's contents
  * (the kernels never read scratch they have not written in the same call):
  * calls that overlap on one GPU (other streams, other host threads) race and

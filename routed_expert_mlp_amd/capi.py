@@ -33,7 +33,7 @@ ERR_SCRATCH_LIMIT = -9
 MAX_TOP_K = 16
 MAX_EXPERTS = 1024
 DECODE_MAX_T = 256
-NOALLOC_SCRATCH_BYTES = 32 << 20
+NOALLOC_SCRATCH_BYTES = 64 << 20
 KIND_ROUTED = 0
 KIND_DENSE = 1
 KIND_ROUTED_FP8 = 2

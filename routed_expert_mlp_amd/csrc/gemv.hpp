@@ -230,13 +230,14 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
   }
 }
 
-// out[t][c] = bf16(ys[t][c] + sum_k w[t,k] * y[t*K+k][c]), k in order (fp32).
+// out[t][c] = bf16(ys[t][c] + sum_k w[t,k] * y[t*K+k][c]), k in order (fp32);
+// ys the sum of ys_parts reduction parts [ys_parts][T][H] (added in order).
 // KMAX >= K: the K loads of a thread are all issued before the first sum (a
 // loop over a run-time K waited on each load in turn; measured slower).
 template <int KMAX>
 __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ y, const float* __restrict__ ys,
                                                  const float* __restrict__ wts, int T, int K, int H,
-                                                 uint16_t* __restrict__ out) {
+                                                 uint16_t* __restrict__ out, int ys_parts) {
   const int64_t q = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;   // float4 index
   const int64_t nq = static_cast<int64_t>(T) * (H >> 2);
   if (q >= nq) return;
@@ -251,7 +252,15 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ y, co
       v[k] = reinterpret_cast<const float4*>(y + (t * K + k) * H)[c4];
     }
   }
+  // the shared expert's output, or the sum of its reduction parts (in order)
   float4 acc = ys ? reinterpret_cast<const float4*>(ys)[q] : make_float4(0, 0, 0, 0);
+  for (int p = 1; p < ys_parts; ++p) {
+    const float4 v = reinterpret_cast<const float4*>(ys + static_cast<int64_t>(p) * T * H)[q];
+    acc.x += v.x;
+    acc.y += v.y;
+    acc.z += v.z;
+    acc.w += v.w;
+  }
 #pragma unroll
   for (int k = 0; k < KMAX; ++k) {
     if (k < K) {
@@ -265,6 +274,25 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ y, co
   o.x = pack_bf16x2(acc.x, acc.y);
   o.y = pack_bf16x2(acc.z, acc.w);
   reinterpret_cast<uint2*>(out)[q] = o;
+}
+
+
+// hs[t][j] = bf16(SwiGLU(sum_q gu[q][t][j], sum_q gu[q][t][Is + j])) over the
+// nparts reduction parts [nparts][T][2 Is] (added in order) of the shared
+// expert's gate/up, clamped as in every other gate/up path.
+__global__ __launch_bounds__(256) void k_swiglu_parts(const float* __restrict__ gu, int nparts, int64_t pstride,
+                                                      int T, int Is, float L, uint16_t* __restrict__ hs) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= static_cast<int64_t>(T) * Is) return;
+  const int64_t t = i / Is;
+  const int j = static_cast<int>(i - t * Is);
+  const float* r = gu + t * 2 * Is;
+  float g = r[j], u = r[Is + j];
+  for (int q = 1; q < nparts; ++q) {
+    g += r[q * pstride + j];
+    u += r[q * pstride + Is + j];
+  }
+  hs[i] = f32_to_bf16(swiglu_clamped(g, u, L));
 }
 
 }  // namespace moe

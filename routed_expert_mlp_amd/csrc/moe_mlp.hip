@@ -81,6 +81,11 @@ struct Plan {
   size_t wsplit = 0;                                                             // router weight, 3 bf16 planes
   int logit_planes = 1;
   int logit_splits = 1;       // reduction parts of the split-weight logits GEMM
+  // few-token grouped-GEMM form: the shared expert's GEMMs split their
+  // reduction (gate/up into sgu_splits parts, down into sd_splits) so that
+  // their few output tiles still fill the GPU; parts are fp32, added in order
+  int sgu_splits = 1, sd_splits = 1;
+  size_t sgu_parts = 0;
   size_t total = 0;
   int64_t max_tiles = 0;
 };
@@ -112,6 +117,17 @@ bool mfma_logits(const moe_mlp_config* c, int64_t T, int prefill) {
   return prefill && T >= 64 && c->hidden % 64 == 0;
 }
 
+// Reduction parts for a BF16 GEMM with `tiles` output tiles over a reduction
+// of kdim: the most parts (of at most 16) that keep tiles x parts within one
+// workgroup per CU (256) and every part a multiple of 128 long; 1 when the
+// tiles alone give half the CUs work.
+int reduction_splits(int64_t tiles, int64_t kdim) {
+  if (tiles >= 128) return 1;
+  for (int s : {16, 12, 8, 6, 4, 3, 2})
+    if (tiles * s <= 256 && kdim % (128 * s) == 0) return s;
+  return 1;
+}
+
 Plan make_plan(const moe_mlp_config* c, int64_t T, int prefill) {
   Plan p;
   Alloc a;
@@ -126,8 +142,10 @@ Plan make_plan(const moe_mlp_config* c, int64_t T, int prefill) {
   if (mfma_logits(c, T, prefill)) {
     p.logit_planes = 3;
     p.wsplit = a.take(size_t(3 * E * H) * 2);
-    // the logits GEMM has only ceil(T/128) x ceil(3E/256) output tiles: cut
-    // its reduction into 4 parts when H allows, for 4x the workgroups
+    // the logits GEMM has only ceil(T/256) x ceil(3E/256) output tiles: cut
+    // its reduction into 4 parts when H allows, for 4x the workgroups (more
+    // parts made the few-token GEMM faster but the top-k, which adds 3 x
+    // parts values per logit, slower by more: measured at 64 tokens)
     if (H % 256 == 0) p.logit_splits = 4;
   }
   p.logits = a.take(size_t(T * E * p.logit_planes * p.logit_splits) * 4);
@@ -153,8 +171,13 @@ Plan make_plan(const moe_mlp_config* c, int64_t T, int prefill) {
   }
   p.h = a.take(size_t(S * I) * 2);
   if (Is) {
+    if (prefill) {
+      p.sgu_splits = reduction_splits(cdiv(T, B16_BM) * cdiv(2 * Is, B16_BN), H);
+      p.sd_splits = reduction_splits(cdiv(T, B16_BM) * cdiv(H, B16_BN), Is);
+      if (p.sgu_splits > 1) p.sgu_parts = a.take(size_t(p.sgu_splits) * T * 2 * Is * 4);
+    }
     p.hs = a.take(size_t(T * Is) * 2);
-    p.ys = a.take(size_t(T * H) * 4);
+    p.ys = a.take(size_t(p.sd_splits) * T * H * 4);
   }
   p.y = a.take(size_t(S * H) * 4);
   p.total = a.cur;
@@ -827,10 +850,31 @@ int run_layer(const moe_mlp_config* c, const moe_mlp_weights* w, const uint16_t*
       gemm<true, GEMM_DOWN_SLOT_F32, true>(gd, p.max_tiles, s, ev(4));
     }
     const int64_t mt = cdiv(T, GM_BM);
-    if (Is) {
+    if (Is && p.sgu_splits > 1) {
+      // few tokens: gate and up rows as plain fp32 outputs in sgu_splits
+      // reduction parts, then the SwiGLU over the parts added in order
+      GemmArgs gs = bf16_gemm_args(x, H / p.sgu_splits, w->shared_w13, 2 * Is, Ti, at<float>(ws, p.sgu_parts),
+                                   2 * Is, L);
+      gs.lda = gs.ldb = H;
+      gs.ksplit = p.sgu_splits;
+      gs.split_out = int64_t(T) * 2 * Is;
+      gemm<false, GEMM_DOWN_F32, false>(gs, mt, s, Ev{ev(5).a, nullptr});
+      launch(k_swiglu_parts, dim3(static_cast<unsigned>(cdiv(T * Is, 256))), dim3(256), s, nullptr, ev(5).b,
+             static_cast<const float*>(at<float>(ws, p.sgu_parts)), p.sgu_splits, gs.split_out, Ti, Is, L, hs);
+    } else if (Is) {
       gemm<false, GEMM_GATEUP, false>(bf16_gemm_args(x, H, w->shared_w13, Is, Ti, hs, Is, L), mt, s, ev(5));
+    }
+    if (Is && p.sd_splits > 1) {
+      // down in sd_splits reduction parts; the combine adds them in order
+      GemmArgs gs = bf16_gemm_args(hs, Is / p.sd_splits, w->shared_w2, H, Ti, ys, H, L);
+      gs.lda = gs.ldb = Is;
+      gs.ksplit = p.sd_splits;
+      gs.split_out = int64_t(T) * H;
+      gemm<false, GEMM_DOWN_F32, false>(gs, mt, s, ev(6));
+    } else if (Is) {
       gemm<false, GEMM_DOWN_F32, false>(bf16_gemm_args(hs, Is, w->shared_w2, H, Ti, ys, H, L), mt, s, ev(6));
-    } else {
+    }
+    if (!Is) {
       empty_stage(ev(5));
       empty_stage(ev(6));
     }
@@ -880,11 +924,11 @@ int run_layer(const moe_mlp_config* c, const moe_mlp_weights* w, const uint16_t*
   const dim3 cgrid(static_cast<unsigned>(cdiv(nq, 256)));
   const float *yc = y, *ysc = ys, *wc = wts;
   if (K <= 4)
-    launch(k_combine<4>, cgrid, dim3(256), s, ce.a, ce.b, yc, ysc, wc, Ti, K, H, out);
+    launch(k_combine<4>, cgrid, dim3(256), s, ce.a, ce.b, yc, ysc, wc, Ti, K, H, out, p.sd_splits);
   else if (K <= 8)
-    launch(k_combine<8>, cgrid, dim3(256), s, ce.a, ce.b, yc, ysc, wc, Ti, K, H, out);
+    launch(k_combine<8>, cgrid, dim3(256), s, ce.a, ce.b, yc, ysc, wc, Ti, K, H, out, p.sd_splits);
   else
-    launch(k_combine<MOE_MLP_MAX_TOP_K>, cgrid, dim3(256), s, ce.a, ce.b, yc, ysc, wc, Ti, K, H, out);
+    launch(k_combine<MOE_MLP_MAX_TOP_K>, cgrid, dim3(256), s, ce.a, ce.b, yc, ysc, wc, Ti, K, H, out, p.sd_splits);
   return launch_status();
 }
 
