@@ -72,6 +72,9 @@ struct GemmArgs {
   int lda, ldb;
   int ksplit;
   int64_t split_out;
+  // routed NVFP4 kernel only: tiles of at most skip_rows rows are left to
+  // k_gemm_nvfp4_m32 (0 = none)
+  int skip_rows;
 };
 
 template <bool NVFP4, int MODE, bool ROUTED>

@@ -269,7 +269,8 @@ __device__ __forceinline__ void f4_mainloop(const F4Lds& L, const F4Src& src, in
 template <int MODE, bool TILED>
 __global__ __launch_bounds__(F4_THREADS, 1) void k_gemm_nvfp4(GemmArgs a) {
   const int nbn = a.n_blocks;
-  const int ntl = *a.n_tiles;
+  // with skip_rows, the tiles of more than skip_rows rows (the scheduler puts them first)
+  const int ntl = a.skip_rows ? a.n_tiles[1] : a.n_tiles[0];
   const int total = ntl * nbn, chunk = (total + 7) >> 3;
   const int kk = blockIdx.x >> 3;
   if (kk >= chunk) return;
@@ -279,6 +280,7 @@ __global__ __launch_bounds__(F4_THREADS, 1) void k_gemm_nvfp4(GemmArgs a) {
   const int e = a.tile_expert[tile];
   const int m0 = a.tile_m0[tile];
   const int valid = min(GM_BM, a.count[e] - m0);
+  if (valid <= a.skip_rows) return;
   const int p0 = a.offset[e] + m0;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int kdim = a.kdim;
@@ -335,6 +337,16 @@ __global__ __launch_bounds__(F4_THREADS, 1) void k_gemm_nvfp4(GemmArgs a) {
   __shared__ uint4 lc0[2048], lc1[2048];                          // code ring (32 KB each)
   __shared__ __attribute__((aligned(16))) uint8_t ls0[F4_WROWS * 16], ls1[F4_WROWS * 16];   // scale ring
   const F4Lds L{{la0, la1, la2, la3}, {lc0, lc1}, {ls0, ls1}};
+  // down: the tile's output rows, lane l holding rows l and 64 + l, read before
+  // the main loop (a read per row in the epilogue waits for every store before it)
+  int orow_l[2] = {0, 0};
+  if constexpr (MODE != GEMM_GATEUP) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int r = 64 * i + lane;
+      orow_l[i] = a.perm[p0 + (r < valid ? r : 0)];
+    }
+  }
   f32x16 acc[4][2];
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt)
@@ -373,6 +385,8 @@ __global__ __launch_bounds__(F4_THREADS, 1) void k_gemm_nvfp4(GemmArgs a) {
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
       const int row = mt * 32 + c32_row(lane, j);
+      int orow_i = 0;
+      if constexpr (MODE != GEMM_GATEUP) orow_i = __shfl(orow_l[mt >> 1], row & 63);
       if (row >= valid) continue;
       if (MODE == GEMM_GATEUP) {
         const int jc = nblk * 256 + 32 * wv + ln;
@@ -380,7 +394,7 @@ __global__ __launch_bounds__(F4_THREADS, 1) void k_gemm_nvfp4(GemmArgs a) {
         static_cast<uint16_t*>(a.out)[static_cast<int64_t>(p0 + row) * a.ldo + jc] =
             f32_to_bf16(swiglu_clamped(g0 * acc[mt][0][j], g1 * acc[mt][1][j], a.limit));
       } else {
-        const int64_t orow = a.perm[p0 + row];
+        const int64_t orow = orow_i;
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) {
           const int n = nblk * F4_WROWS + 64 * wv + 32 * nt + ln;

@@ -239,6 +239,13 @@ __global__ __launch_bounds__(F8D_THREADS, 1) void k_gemm_f8d(GemmArgs a) {
   // lane l holds the scales of k block l (kdim <= 8192), loaded before any DMA
   const float sreg0 = bsf[sr0 * nkb128 + min(lane, nkb128 - 1)];
   const float sreg1 = bsf[sr1 * nkb128 + min(lane, nkb128 - 1)];
+  // down: this wavefront's output rows (lane l: tile row 64 (wv % 2) + l), read
+  // before the main loop (a read per row in the epilogue waits for every store before it)
+  int orow_l = 0;
+  if constexpr (MODE != GEMM_GATEUP) {
+    const int r = 64 * (wv & 1) + lane;
+    orow_l = a.perm[p0 + (r < valid ? r : 0)];
+  }
 
   __shared__ uint4 la0[1024], la1[1024], la2[1024], la3[1024];   // activation ring (16 KB each)
   __shared__ uint4 lc0[1024], lc1[1024], lc2[1024], lc3[1024];   // code ring (16 KB each)
@@ -266,6 +273,8 @@ __global__ __launch_bounds__(F8D_THREADS, 1) void k_gemm_f8d(GemmArgs a) {
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
       const int row = (2 * mh + m) * 32 + c32_row(lane, j);
+      int orow_i = 0;
+      if constexpr (MODE != GEMM_GATEUP) orow_i = __shfl(orow_l, row & 63);
       if (row >= valid) continue;
       if (MODE == GEMM_GATEUP) {
         const int jc = nblk * 128 + 32 * nq + ln;
@@ -273,7 +282,7 @@ __global__ __launch_bounds__(F8D_THREADS, 1) void k_gemm_f8d(GemmArgs a) {
         static_cast<uint16_t*>(a.out)[static_cast<int64_t>(p0 + row) * a.ldo + jc] =
             f32_to_bf16(swiglu_clamped(acc[m][0][j], acc[m][1][j], a.limit));
       } else {
-        const int64_t orow = a.perm[p0 + row];
+        const int64_t orow = orow_i;
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) {
           const int n = nblk * F8D_WROWS + 64 * nq + 32 * nt + ln;

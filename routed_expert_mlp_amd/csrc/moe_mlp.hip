@@ -7,6 +7,7 @@
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cmath>
 #include <cstdint>
@@ -21,8 +22,10 @@
 #include "gemm.hpp"
 #include "gemm_bf16.hpp"
 #include "gemm_fp4.hpp"
+#include "gemm_fp4s.hpp"
 #include "gemm_fp8.hpp"
 #include "gemm_fp8d.hpp"
+#include "gemm_skinny.hpp"
 #include "gemv.hpp"
 #include "permute.hpp"
 #include "router.hpp"
@@ -86,6 +89,9 @@ struct Plan {
   // their few output tiles still fill the GPU; parts are fp32, added in order
   int sgu_splits = 1, sd_splits = 1;
   size_t sgu_parts = 0;
+  // up to 64 tokens the shared expert's projections run on k_skinny_bf16
+  // (fp32 parts of kr columns; gate/up then always through the parts)
+  bool skinny = false;
   size_t total = 0;
   int64_t max_tiles = 0;
 };
@@ -114,8 +120,15 @@ int gemm_form(const moe_mlp_config* c, int64_t T, int prefill) {
 // Prefill router logits on the matrix cores (split fp32 weight, see router.hpp)
 // when there are enough tokens and the reduction length suits the fast GEMM.
 bool mfma_logits(const moe_mlp_config* c, int64_t T, int prefill) {
-  return prefill && T >= 64 && c->hidden % 64 == 0;
+  return prefill && T > MOE_MLP_DECODE_MAX_T && c->hidden % 64 == 0;
 }
+
+// k_skinny_bf16 takes up to 64 tokens and reductions that are a multiple of
+// 512; its part length: 1024 up to 32 tokens when the reduction allows (the
+// token columns of a part in LDS and the weights in registers stay within
+// budget), else 512.
+bool skinny_ok(int64_t T, int64_t K) { return T >= 1 && T <= 64 && K % 512 == 0; }
+int skinny_kr(int64_t T, int64_t K) { return (T <= 32 && K % 1024 == 0) ? 1024 : 512; }
 
 // Reduction parts for a BF16 GEMM with `tiles` output tiles over a reduction
 // of kdim: the most parts (of at most 16) that keep tiles x parts within one
@@ -156,7 +169,7 @@ Plan make_plan(const moe_mlp_config* c, int64_t T, int prefill) {
     p.count = a.take(size_t(E) * 4);
     p.offset = a.take(size_t(E + 1) * 4);
     p.perm = a.take(size_t(S) * 4);
-    p.n_tiles = a.take(4);
+    p.n_tiles = a.take(8);
     p.tile_e = a.take(size_t(p.max_tiles) * 4);
     p.tile_m0 = a.take(size_t(p.max_tiles) * 4);
     p.phist = a.take(size_t(cdiv(S, PERM_CHUNK)) * E * 4);
@@ -171,7 +184,12 @@ Plan make_plan(const moe_mlp_config* c, int64_t T, int prefill) {
   }
   p.h = a.take(size_t(S * I) * 2);
   if (Is) {
-    if (prefill) {
+    if (skinny_ok(T, H) && skinny_ok(T, Is)) {
+      p.skinny = true;
+      p.sgu_splits = static_cast<int>(H / skinny_kr(T, H));
+      p.sd_splits = static_cast<int>(Is / skinny_kr(T, Is));
+      p.sgu_parts = a.take(size_t(p.sgu_splits) * T * 2 * Is * 4);
+    } else if (prefill) {
       p.sgu_splits = reduction_splits(cdiv(T, B16_BM) * cdiv(2 * Is, B16_BN), H);
       p.sd_splits = reduction_splits(cdiv(T, B16_BM) * cdiv(H, B16_BN), Is);
       if (p.sgu_splits > 1) p.sgu_parts = a.take(size_t(p.sgu_splits) * T * 2 * Is * 4);
@@ -302,9 +320,26 @@ void topk_tokens(int E, const float* logits, const float* bias, int T, int K, fl
 
 void router_logits(const uint16_t* x, const float* wr, float* logits, int64_t T, int H, int E, hipStream_t s,
                    Ev ev) {
-  // one workgroup per expert row up to the decode limit (the tile GEMM below
-  // has only ceil(T/64) x ceil(E/64) workgroups, too few for small T)
-  if (T <= MOE_MLP_DECODE_MAX_T) {
+  // up to the decode limit: k_logits_rows (H a multiple of 8 up to 8192),
+  // else one workgroup per expert row (the tile GEMM below has only
+  // ceil(T/64) x ceil(E/64) workgroups, too few for small T)
+  if (T <= MOE_MLP_DECODE_MAX_T && H % 8 == 0 && H <= 8192) {
+    const int cpt = static_cast<int>(cdiv(H / 8, 256));
+    auto go = [&](auto kern, int ne) {
+      const dim3 grid(static_cast<unsigned>(8 * cdiv(cdiv(E, ne), 8)), static_cast<unsigned>(cdiv(T, LOGIT_TG)));
+      launch(kern, grid, dim3(256), s, ev.a, ev.b, x, wr, logits, static_cast<int>(T), H, E);
+    };
+    // two experts per workgroup up to 16 tokens, four beyond when H <= 4096
+    // (each token row is then read from L2 by E / 4 workgroups; the weights
+    // of four experts at larger H would not fit the registers)
+    const bool ne4 = T > 16;
+    switch (cpt) {
+      case 1: ne4 ? go(k_logits_rows<1, 4>, 4) : go(k_logits_rows<1, 2>, 2); break;
+      case 2: ne4 ? go(k_logits_rows<2, 4>, 4) : go(k_logits_rows<2, 2>, 2); break;
+      case 3: go(k_logits_rows<3, 2>, 2); break;
+      default: go(k_logits_rows<4, 2>, 2); break;
+    }
+  } else if (T <= MOE_MLP_DECODE_MAX_T) {
     launch(k_logits_gemv, dim3(E), dim3(256), s, ev.a, ev.b, x, wr, logits, static_cast<int>(T), H, E);
   } else {
     const dim3 grid(static_cast<unsigned>(cdiv(T, 64)), static_cast<unsigned>(cdiv(E, 64)));
@@ -368,13 +403,26 @@ void gemm_fp8(const GemmArgs& a0, int64_t m_tiles, hipStream_t s, Ev ev) {
   launch(k_gemm_f8<MODE>, grid, dim3(256), s, ev.a, ev.b, a);
 }
 
+// Tiles of at most this many rows go to k_gemm_nvfp4_m32 (the scheduler puts
+// them after the others): up to MOE_MLP_DECODE_MAX_T tokens, in the gate/up
+// projection.  With thousands of tokens the few short tiles cost more as a
+// launch of their own, after the large ones, than inside k_gemm_nvfp4; the
+// down projection (its reduction is the short one, I) ran 3% slower on the
+// small-tile kernel at 64 tokens (both measured).
+int small_tile_rows(int64_t T) { return T <= MOE_MLP_DECODE_MAX_T ? F4M_ROWS : 0; }
+
 // Routed NVFP4 projections with a reduction length that is a multiple of 256
-// and at least 512 take k_gemm_nvfp4, BF16 projections (shared expert, dense
-// FFN, router logits) with a reduction length that is a multiple of 128 take
-// k_gemm_bf16; other reduction lengths that are a multiple of 64 the
-// 32x32x16-MFMA kernel (k_gemm_fast); the rest the general 16x16x32 kernel.
+// and at least 512 take k_gemm_nvfp4; with small_rows (gate/up) it takes only
+// the tiles of more than small_rows rows (at most slots / (small_rows + 1) of
+// them) and k_gemm_nvfp4_m32 the rest; max_count = the most rows an expert can
+// hold (the token count): at most 32, k_gemm_nvfp4 is not launched.  BF16
+// projections (shared expert, dense FFN, router logits) with a reduction
+// length that is a multiple of 128 take k_gemm_bf16; other reduction lengths
+// that are a multiple of 64 the 32x32x16-MFMA kernel (k_gemm_fast); the rest
+// the general 16x16x32 kernel.
 template <bool NVFP4, int MODE, bool ROUTED>
-void gemm(const GemmArgs& a0, int64_t m_tiles, hipStream_t s, Ev ev) {
+void gemm(const GemmArgs& a0, int64_t m_tiles, hipStream_t s, Ev ev, int small_rows = 0, int64_t slots = 0,
+          int64_t max_count = -1) {
   GemmArgs a = a0;
   if constexpr (NVFP4 && ROUTED && (MODE == GEMM_GATEUP || MODE == GEMM_DOWN_SLOT_F32)) {
     // its DMA offsets are 32-bit: activation rows (T here) and weight rows
@@ -383,11 +431,19 @@ void gemm(const GemmArgs& a0, int64_t m_tiles, hipStream_t s, Ev ev) {
     if (a.kdim % 256 == 0 && a.kdim >= 512 && int64_t(a.T) * a.kdim * 2 < (int64_t(1) << 31) &&
         w_rows * a.kdim / 2 < (int64_t(1) << 31)) {
       a.n_blocks = static_cast<int>(cdiv(a.half_n, MODE == GEMM_GATEUP ? F4_WROWS / 2 : F4_WROWS));
-      const dim3 grid(static_cast<unsigned>(8 * cdiv(m_tiles * a.n_blocks, 8)));
-      if (a.bq_t && a.bs_t)
-        launch(k_gemm_nvfp4<MODE, true>, grid, dim3(F4_THREADS), s, ev.a, ev.b, a);
-      else
-        launch(k_gemm_nvfp4<MODE, false>, grid, dim3(F4_THREADS), s, ev.a, ev.b, a);
+      const bool use_small = MODE == GEMM_GATEUP && small_rows == F4M_ROWS;
+      const bool small_only = use_small && max_count >= 0 && max_count <= F4M_ROWS;
+      const int64_t big_tiles = use_small ? std::min<int64_t>(m_tiles, slots / (F4M_ROWS + 1)) : m_tiles;
+      a.skip_rows = use_small ? F4M_ROWS : 0;
+      with_ct(a.bq_t && a.bs_t, [&](auto ctc) {
+        constexpr bool CT = decltype(ctc)::value;
+        if (!small_only && big_tiles > 0)
+          launch(k_gemm_nvfp4<MODE, CT>, dim3(static_cast<unsigned>(8 * cdiv(big_tiles * a.n_blocks, 8))),
+                 dim3(F4_THREADS), s, ev.a, use_small ? nullptr : ev.b, a);
+        if (use_small)
+          launch(k_gemm_nvfp4_m32<MODE, CT>, dim3(static_cast<unsigned>(8 * cdiv(m_tiles * a.n_blocks, 8))),
+                 dim3(F4_THREADS), s, (small_only || big_tiles == 0) ? ev.a : nullptr, ev.b, a);
+      });
       return;
     }
   }
@@ -412,6 +468,27 @@ void gemm(const GemmArgs& a0, int64_t m_tiles, hipStream_t s, Ev ev) {
     const int nb = MODE == GEMM_GATEUP ? 128 : 256;
     const dim3 grid(static_cast<unsigned>(m_tiles), static_cast<unsigned>(cdiv(a.half_n, nb)));
     launch(k_gemm<NVFP4, MODE, ROUTED>, grid, dim3(256), s, ev.a, ev.b, a);
+  }
+}
+
+// out[q][t][n] (q < K / kr parts, part stride T * N) = x[t] . w[n] over the
+// part's kr columns, on k_skinny_bf16 (skinny_ok(T, K) holds).
+void skinny_gemm(const uint16_t* x, const uint16_t* w, int N, int K, int T, float* out, hipStream_t s, Ev ev) {
+  const int kr = skinny_kr(T, K), nparts = K / kr;
+  const dim3 grid(static_cast<unsigned>(cdiv(N, F16S_ROWS) * nparts));
+  const int64_t ps = int64_t(T) * N;
+  auto go = [&](auto kern) { launch(kern, grid, dim3(256), s, ev.a, ev.b, x, K, w, K, N, T, nparts, out, ps); };
+  const int tb = static_cast<int>(cdiv(T, 16));
+  if (kr == 1024) {
+    if (tb == 1) go(k_skinny_bf16<1, 1024>);
+    else go(k_skinny_bf16<2, 1024>);
+  } else {
+    switch (tb) {
+      case 1: go(k_skinny_bf16<1, 512>); break;
+      case 2: go(k_skinny_bf16<2, 512>); break;
+      case 3: go(k_skinny_bf16<3, 512>); break;
+      default: go(k_skinny_bf16<4, 512>); break;
+    }
   }
 }
 
@@ -760,7 +837,7 @@ int run_layer(const moe_mlp_config* c, const moe_mlp_weights* w, const uint16_t*
   // decode of up to 16 tokens with H <= 4096: router logits and the shared
   // expert's gate/up share one launch (stage router_logits; shared_gateup
   // then records an empty stage)
-  const bool fused_k1 = !prefill && T <= 16 && H <= kDec1MaxH && Is <= 2048;
+  const bool fused_k1 = !prefill && T <= 16 && H <= kDec1MaxH && Is <= 2048 && !p.skinny;
   if (fused_k1) {
     const int nlb = static_cast<int>(cdiv(E, 4)), nsb = static_cast<int>(cdiv(Is, 4));
     launch(k_dec_logits_shared_t<16, 8>, logits_shared_t_grid(nlb + nsb, Ti), dim3(256), s, ev(0).a, ev(0).b, x, w->router_w, logits,
@@ -779,7 +856,9 @@ int run_layer(const moe_mlp_config* c, const moe_mlp_weights* w, const uint16_t*
     int32_t* prank = at<int32_t>(ws, p.prank);
     launch(k_perm_hist, dim3(nchunk), dim3(PERM_CHUNK), s, pe.a, nullptr, ids, static_cast<int>(S), E, phist, prank);
     int32_t* pbase = at<int32_t>(ws, p.pbase);
-    launch(k_perm_schedule, dim3(1), dim3(1024), s, nullptr, nullptr, E, nchunk, GM_BM, phist, pbase, pm);
+    const int small_rows = small_tile_rows(T);
+    launch(k_perm_schedule, dim3(1), dim3(1024), s, nullptr, nullptr, E, nchunk, GM_BM, small_rows, phist, pbase,
+           pm);
     launch(k_perm_scatter, dim3(static_cast<unsigned>(cdiv(S, 256))), dim3(256), s, nullptr, pe.b, ids,
            static_cast<int>(S), E, pbase, prank, pm);
     GemmArgs g{};
@@ -818,7 +897,7 @@ int run_layer(const moe_mlp_config* c, const moe_mlp_weights* w, const uint16_t*
       gu.gscale = nullptr;
       gemm_fp8<GEMM_GATEUP>(gu, p.max_tiles, s, ev(3));
     } else {
-      gemm<true, GEMM_GATEUP, true>(gu, p.max_tiles, s, ev(3));
+      gemm<true, GEMM_GATEUP, true>(gu, p.max_tiles, s, ev(3), small_rows, S, T);
     }
     // routed down -> y (slot rows)
     GemmArgs gd = g;
@@ -847,10 +926,15 @@ int run_layer(const moe_mlp_config* c, const moe_mlp_weights* w, const uint16_t*
       gd.gscale = nullptr;
       gemm_fp8<GEMM_DOWN_SLOT_F32>(gd, p.max_tiles, s, ev(4));
     } else {
-      gemm<true, GEMM_DOWN_SLOT_F32, true>(gd, p.max_tiles, s, ev(4));
+      gemm<true, GEMM_DOWN_SLOT_F32, true>(gd, p.max_tiles, s, ev(4), small_rows, S, T);
     }
     const int64_t mt = cdiv(T, GM_BM);
-    if (Is && p.sgu_splits > 1) {
+    if (Is && p.skinny) {
+      float* parts = at<float>(ws, p.sgu_parts);
+      skinny_gemm(x, w->shared_w13, 2 * Is, H, Ti, parts, s, Ev{ev(5).a, nullptr});
+      launch(k_swiglu_parts, dim3(static_cast<unsigned>(cdiv(T * Is, 256))), dim3(256), s, nullptr, ev(5).b,
+             static_cast<const float*>(parts), p.sgu_splits, int64_t(T) * 2 * Is, Ti, Is, L, hs);
+    } else if (Is && p.sgu_splits > 1) {
       // few tokens: gate and up rows as plain fp32 outputs in sgu_splits
       // reduction parts, then the SwiGLU over the parts added in order
       GemmArgs gs = bf16_gemm_args(x, H / p.sgu_splits, w->shared_w13, 2 * Is, Ti, at<float>(ws, p.sgu_parts),
@@ -864,7 +948,9 @@ int run_layer(const moe_mlp_config* c, const moe_mlp_weights* w, const uint16_t*
     } else if (Is) {
       gemm<false, GEMM_GATEUP, false>(bf16_gemm_args(x, H, w->shared_w13, Is, Ti, hs, Is, L), mt, s, ev(5));
     }
-    if (Is && p.sd_splits > 1) {
+    if (Is && p.skinny) {
+      skinny_gemm(hs, w->shared_w2, H, Is, Ti, ys, s, ev(6));
+    } else if (Is && p.sd_splits > 1) {
       // down in sd_splits reduction parts; the combine adds them in order
       GemmArgs gs = bf16_gemm_args(hs, Is / p.sd_splits, w->shared_w2, H, Ti, ys, H, L);
       gs.lda = gs.ldb = Is;
@@ -883,8 +969,16 @@ int run_layer(const moe_mlp_config* c, const moe_mlp_weights* w, const uint16_t*
               at<int32_t>(ws, p.g_offset), at<int32_t>(ws, p.g_slots)};
     topk_bucket(E, logits, w->router_bias, Ti, K, rsf, ids, wts, ids_out, w_out, gr, s, ev(1));
     const int groups = static_cast<int>(S < E ? S : E);
-    if (Is && !fused_k1) gemv<false, GEMV_GATEUP, 1>(bf16_gemv_args(w->shared_w13, Is, H, Ti, x, hs, L), 1, s, ev(2));
-    else empty_stage(ev(2));
+    if (Is && p.skinny) {
+      float* parts = at<float>(ws, p.sgu_parts);
+      skinny_gemm(x, w->shared_w13, 2 * Is, H, Ti, parts, s, Ev{ev(2).a, nullptr});
+      launch(k_swiglu_parts, dim3(static_cast<unsigned>(cdiv(T * Is, 256))), dim3(256), s, nullptr, ev(2).b,
+             static_cast<const float*>(parts), p.sgu_splits, int64_t(T) * 2 * Is, Ti, Is, L, hs);
+    } else if (Is && !fused_k1) {
+      gemv<false, GEMV_GATEUP, 1>(bf16_gemv_args(w->shared_w13, Is, H, Ti, x, hs, L), 1, s, ev(2));
+    } else {
+      empty_stage(ev(2));
+    }
     GemvArgs r{};
     r.n_groups = gr.n_groups;
     r.g_expert = gr.expert;
@@ -905,7 +999,8 @@ int run_layer(const moe_mlp_config* c, const moe_mlp_weights* w, const uint16_t*
     gu.in = x;
     gu.out = h;
     gemv<true, GEMV_GATEUP, 2>(gu, groups, s, ev(3), !w->w13_q);
-    if (Is) gemv<false, GEMV_DOWN_F32, 2>(bf16_gemv_args(w->shared_w2, H, Is, Ti, hs, ys, L), 1, s, ev(4));
+    if (Is && p.skinny) skinny_gemm(hs, w->shared_w2, H, Is, Ti, ys, s, ev(4));
+    else if (Is) gemv<false, GEMV_DOWN_F32, 2>(bf16_gemv_args(w->shared_w2, H, Is, Ti, hs, ys, L), 1, s, ev(4));
     else empty_stage(ev(4));
     GemvArgs gd = r;
     gd.wq = codes2(w);

@@ -7,8 +7,9 @@
 //                       slot's rank among the chunk's slots of its expert;
 //   2. k_perm_schedule: one workgroup sums the histograms into expert counts,
 //                       scans them into offsets, cuts each expert's rows into
-//                       BM-row GEMM tiles and turns the histograms into the
-//                       sorted position of each (chunk, expert) run;
+//                       BM-row GEMM tiles (those of more than small_rows rows
+//                       first) and turns the histograms into the sorted
+//                       position of each (chunk, expert) run;
 //   3. k_perm_scatter:  one thread per slot writes it at run start + rank.
 #pragma once
 
@@ -20,7 +21,7 @@ struct Perm {
   int32_t* count;        // [E]
   int32_t* offset;       // [E + 1]
   int32_t* perm;         // [T*K]   sorted position -> slot
-  int32_t* n_tiles;      // [1]
+  int32_t* n_tiles;      // [2]    tiles, and how many of them (the first) hold more than small_rows rows
   int32_t* tile_expert;  // [max_tiles]
   int32_t* tile_m0;      // [max_tiles] first row of the tile within its expert
 };
@@ -54,10 +55,14 @@ __global__ __launch_bounds__(PERM_CHUNK) void k_perm_hist(const int32_t* __restr
 // chunks), their exclusive scan into offsets, the cut of each expert's rows
 // into bm-row GEMM tiles, and base[b][e] = the sorted position of chunk b's
 // first slot of expert e (a separate array, so the loads of both passes over
-// the chunks stay in flight together).
-__global__ __launch_bounds__(1024) void k_perm_schedule(int E, int nblk, int bm, const int32_t* __restrict__ hist,
-                                                        int32_t* __restrict__ base, Perm p) {
-  __shared__ int s_w[2][16];
+// the chunks stay in flight together).  Tiles of more than small_rows rows
+// come first, in expert order, then the rest (an expert's last tile when it
+// is that short), so that two GEMM kernels can each take one range; with
+// small_rows = 0 the order is plain expert order.
+__global__ __launch_bounds__(1024) void k_perm_schedule(int E, int nblk, int bm, int small_rows,
+                                                        const int32_t* __restrict__ hist, int32_t* __restrict__ base,
+                                                        Perm p) {
+  __shared__ int s_w[3][16];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   int c = 0;
   if (tid < E) {
@@ -65,36 +70,49 @@ __global__ __launch_bounds__(1024) void k_perm_schedule(int E, int nblk, int bm,
     for (int b = 0; b < nblk; ++b) c += hist[static_cast<int64_t>(b) * E + tid];
   }
   const int nt = static_cast<int>(cdiv(c, bm));
-  int ic = c, it = nt;
+  const int ns = (nt > 0 && c - (nt - 1) * bm <= small_rows) ? 1 : 0;   // a short last tile
+  const int nb = nt - ns;
+  int ic = c, ib = nb, is = ns;
 #pragma unroll
   for (int m = 1; m < 64; m <<= 1) {
-    const int a = __shfl_up(ic, m, 64), t = __shfl_up(it, m, 64);
+    const int a = __shfl_up(ic, m, 64), t = __shfl_up(ib, m, 64), u = __shfl_up(is, m, 64);
     if (lane >= m) {
       ic += a;
-      it += t;
+      ib += t;
+      is += u;
     }
   }
   if (lane == 63) {
     s_w[0][wv] = ic;
-    s_w[1][wv] = it;
+    s_w[1][wv] = ib;
+    s_w[2][wv] = is;
   }
   __syncthreads();
-  int bc = 0, bt = 0;
-  for (int w = 0; w < wv; ++w) {
-    bc += s_w[0][w];
-    bt += s_w[1][w];
+  int bc = 0, bb = 0, bs = 0, nbig = 0;
+  for (int w = 0; w < 16; ++w) {
+    if (w < wv) {
+      bc += s_w[0][w];
+      bb += s_w[1][w];
+      bs += s_w[2][w];
+    }
+    nbig += s_w[1][w];
   }
-  const int off = bc + ic - c, toff = bt + it - nt;
+  const int off = bc + ic - c, boff = bb + ib - nb, soff = nbig + bs + is - ns;
   if (tid < E) {
     p.count[tid] = c;
     p.offset[tid] = off;
-    for (int j = 0; j < nt; ++j) {
-      p.tile_expert[toff + j] = tid;
-      p.tile_m0[toff + j] = j * bm;
+    for (int j = 0; j < nb; ++j) {
+      p.tile_expert[boff + j] = tid;
+      p.tile_m0[boff + j] = j * bm;
+    }
+    if (ns) {
+      p.tile_expert[soff] = tid;
+      p.tile_m0[soff] = nb * bm;
     }
     if (tid == E - 1) {
       p.offset[E] = off + c;
-      *p.n_tiles = toff + nt;
+      p.n_tiles[0] = soff + ns;
+      p.n_tiles[1] = nbig;
     }
     int run = off;
 #pragma unroll 16

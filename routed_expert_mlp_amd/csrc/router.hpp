@@ -63,6 +63,80 @@ __global__ __launch_bounds__(256) void k_logits_gemv(const uint16_t* __restrict_
 }
 
 // ---------------------------------------------------------------------------
+// Logits for up to a few hundred tokens, H a multiple of 8 up to 2048 CPT:
+// workgroup (b, g) takes experts NE b .. NE b + NE - 1 and tokens LOGIT_TG g ..
+// + LOGIT_TG - 1.  Thread tid keeps the experts' weights at columns
+// 8 (tid + 256 i) .. + 7 (i < CPT) in registers and reads each token's
+// matching 16 bytes once for all NE experts, every load issued before the
+// first product.  grid.x is a multiple of 8, so all token groups of an expert
+// block run on one XCD (blocks go to the XCDs round-robin) and read its
+// weight rows from that XCD's L2.  Per logit: a sequential fmaf run over the
+// thread's columns, a wave tree, then the four waves' sums.
+// ---------------------------------------------------------------------------
+template <int CPT, int NE>
+__global__ __launch_bounds__(256) void k_logits_rows(const uint16_t* __restrict__ x, const float* __restrict__ wr,
+                                                     float* __restrict__ logits, int T, int H, int E) {
+  const int e0 = blockIdx.x * NE;
+  if (e0 >= E) return;
+  const int t0 = blockIdx.y * LOGIT_TG;
+  const int nt = min(LOGIT_TG, T - t0);
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int n8 = H >> 3;
+  float4 w[NE][CPT][2];
+#pragma unroll
+  for (int n = 0; n < NE; ++n) {
+    const float4* row = reinterpret_cast<const float4*>(wr + static_cast<int64_t>(min(e0 + n, E - 1)) * H);
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int c = tid + 256 * i;
+      w[n][i][0] = c < n8 ? row[2 * c] : make_float4(0.f, 0.f, 0.f, 0.f);
+      w[n][i][1] = c < n8 ? row[2 * c + 1] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  }
+  // tokens past T read token T - 1 again (their sums are dropped)
+  uint4 xv[LOGIT_TG][CPT];
+#pragma unroll
+  for (int t = 0; t < LOGIT_TG; ++t) {
+    const uint4* xr = reinterpret_cast<const uint4*>(x + static_cast<int64_t>(min(t0 + t, T - 1)) * H);
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int c = tid + 256 * i;
+      xv[t][i] = c < n8 ? xr[c] : make_uint4(0u, 0u, 0u, 0u);
+    }
+  }
+  __shared__ float red[4][NE * LOGIT_TG];
+#pragma unroll
+  for (int n = 0; n < NE; ++n) {
+#pragma unroll
+    for (int t = 0; t < LOGIT_TG; ++t) {
+      float a = 0.0f;
+#pragma unroll
+      for (int i = 0; i < CPT; ++i) {
+        const uint4 v = xv[t][i];
+        const float4 wa = w[n][i][0], wb = w[n][i][1];
+        a = fmaf(__uint_as_float(v.x << 16), wa.x, a);
+        a = fmaf(__uint_as_float(v.x & 0xffff0000u), wa.y, a);
+        a = fmaf(__uint_as_float(v.y << 16), wa.z, a);
+        a = fmaf(__uint_as_float(v.y & 0xffff0000u), wa.w, a);
+        a = fmaf(__uint_as_float(v.z << 16), wb.x, a);
+        a = fmaf(__uint_as_float(v.z & 0xffff0000u), wb.y, a);
+        a = fmaf(__uint_as_float(v.w << 16), wb.z, a);
+        a = fmaf(__uint_as_float(v.w & 0xffff0000u), wb.w, a);
+      }
+      const float s = wave_sum(a);
+      if (lane == 0) red[wv][n * LOGIT_TG + t] = s;
+    }
+  }
+  __syncthreads();
+  if (tid < NE * LOGIT_TG) {
+    const int n = tid / LOGIT_TG, t = tid - n * LOGIT_TG;
+    if (e0 + n < E && t < nt)
+      logits[static_cast<int64_t>(t0 + t) * E + e0 + n] =
+          (red[0][tid] + red[1][tid]) + (red[2][tid] + red[3][tid]);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Logits for many tokens (prefill): fp32 tiled GEMM on the vector ALUs,
 // 64 tokens x 64 experts per workgroup, each thread 4 x 4 outputs.  Every
 // 32-wide k tile is summed into a fresh partial before joining the total.

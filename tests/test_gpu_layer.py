@@ -149,6 +149,31 @@ def test_grouped_gemm_nvfp4_tiles(overrides):
     _fresh("ragged_prefill", True, n_sample=100000, **overrides)
 
 
+# Up to 256 tokens the gate/up tiles of at most 32 rows run on the small-tile
+# NVFP4 kernel (the rest on the 128-row one, which the scheduler gives the
+# tiles of more than 32 rows, listed first): expert counts around 128 (short
+# second tiles), around 32 and 25 (both kernels side by side), and at most 32
+# tokens (the small-tile kernel alone); reductions (H) of 768, 1280, 1536 and
+# 512, and 1024 below (2 to 6 blocks of four stages: the first block doubling
+# as the second to last, and both parities of the last).
+SMALL_TILES = [dict(T=256, H=768, I=768, E=4, K=2, Is=0),
+               dict(T=256, H=1280, I=1024, E=8, K=1, Is=64),
+               dict(T=200, H=1536, I=512, E=16, K=2, Is=64),
+               dict(T=32, H=512, I=1024, E=4, K=2, Is=0)]
+
+
+@pytest.mark.parametrize("overrides", SMALL_TILES,
+                         ids=[f"T{o['T']}_H{o['H']}_I{o['I']}_E{o['E']}_K{o['K']}" for o in SMALL_TILES])
+def test_grouped_gemm_small_tiles(overrides):
+    _fresh("ragged_prefill", True, n_sample=100000, **overrides)
+
+
+def test_decode_gemm_form_small_tiles():
+    """The decode form at 64 tokens and more runs the grouped GEMM: 100 tokens over 8 experts
+    (K=2: 25 rows per expert on average, both kernels)."""
+    _fresh("ragged_decode", False, n_sample=100000, T=100, H=1024, I=512, E=8, K=2, Is=64)
+
+
 @pytest.mark.parametrize("prefill", [False, True])
 def test_top_k_equals_e_at_the_kernel_limit(prefill):
     _fresh("tiny_decode", prefill, T=8, K=16)
