@@ -214,13 +214,16 @@ __device__ __forceinline__ void f4m_mainloop(const F4MLds& L, const F4Src& src, 
   }
 }
 
-// Work mapping as k_gemm_nvfp4 (same n_blocks) over the tiles after the
-// first n_tiles[1] (the scheduler puts the tiles of more than 32 rows first);
-// a workgroup whose tile holds more than 32 rows exits all the same.
+// Work mapping as k_gemm_nvfp4 (same n_blocks).  With skip_rows (the
+// scheduler lists the tiles of more than skip_rows rows first, for
+// k_gemm_nvfp4) it takes the tiles after the first n_tiles[1], each of at
+// most 32 rows; without, every tile, in passes of 32 rows that each stream
+// the tile's weights again (for few tokens, where a tile of more than 32 rows
+// is rare and an extra launch of k_gemm_nvfp4 for it would cost more).
 template <int MODE, bool TILED>
 __global__ __launch_bounds__(F4_THREADS, 1) void k_gemm_nvfp4_m32(GemmArgs a) {
   const int nbn = a.n_blocks;
-  const int nbig = a.n_tiles[1];
+  const int nbig = a.skip_rows ? a.n_tiles[1] : 0;
   const int ntl = a.n_tiles[0] - nbig;
   const int total = ntl * nbn, chunk = (total + 7) >> 3;
   const int kk = blockIdx.x >> 3;
@@ -231,21 +234,13 @@ __global__ __launch_bounds__(F4_THREADS, 1) void k_gemm_nvfp4_m32(GemmArgs a) {
   const int e = a.tile_expert[tile];
   const int m0 = a.tile_m0[tile];
   const int valid = min(GM_BM, a.count[e] - m0);
-  if (valid > F4M_ROWS) return;
-  const int p0 = a.offset[e] + m0;
+  if (a.skip_rows && valid > F4M_ROWS) return;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int kdim = a.kdim;
 
-  // activation DMA (wavefronts 0-3): tile rows 8 wv .. +7, 8 lanes per row
   F4Src src;
   src.a = reinterpret_cast<const uint8_t*>(a.a);
-  {
-    const int r = 8 * (wv & 3) + (lane >> 3);
-    const int rr = r < valid ? r : 0;
-    const int64_t row = (MODE == GEMM_GATEUP) ? a.perm[p0 + rr] / a.K : p0 + rr;
-    src.ao[0] = static_cast<uint32_t>((row * kdim + 8 * ((lane & 7) ^ f4_swz_a(r))) * 2);
-    src.ao[1] = 0;
-  }
+  src.ao[1] = 0;
   auto wrow = [&](int p) -> int64_t {
     if (MODE == GEMM_GATEUP) {
       const int j = nblk * 256 + (p & 255);
@@ -272,25 +267,6 @@ __global__ __launch_bounds__(F4_THREADS, 1) void k_gemm_nvfp4_m32(GemmArgs a) {
   } else {
     src.so = static_cast<uint32_t>(wrow(64 * wv + lane) * (kdim >> 4));
   }
-
-  __shared__ uint4 la0[256], la1[256], la2[256], la3[256];       // activation ring (4 KB each)
-  __shared__ uint4 lc0[2048], lc1[2048], lc2[2048], lc3[2048];   // code ring (32 KB each)
-  __shared__ __attribute__((aligned(16))) uint8_t ls0[F4_WROWS * 16], ls1[F4_WROWS * 16];   // scale ring
-  const F4MLds L{{la0, la1, la2, la3}, {lc0, lc1, lc2, lc3}, {ls0, ls1}};
-  // down: the tile's output rows (lane l: row l % 32), read before the main loop
-  int orow_l = 0;
-  if constexpr (MODE != GEMM_GATEUP) orow_l = a.perm[p0 + ((lane & 31) < valid ? (lane & 31) : 0)];
-  f32x16 acc[2];
-#pragma unroll
-  for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-    for (int j = 0; j < 16; ++j) acc[nt][j] = 0.0f;
-  if (wv < 4)
-    f4m_mainloop<MODE, TILED, 1>(L, src, wv, lane, kdim, acc);
-  else
-    f4m_mainloop<MODE, TILED, 0>(L, src, wv, lane, kdim, acc);
-
-  const int ln = lane & 31;
   float g0, g1 = 1.0f;
   if (MODE == GEMM_GATEUP) {
     g0 = a.gscale ? a.gscale[2 * e] : 1.0f;
@@ -298,23 +274,56 @@ __global__ __launch_bounds__(F4_THREADS, 1) void k_gemm_nvfp4_m32(GemmArgs a) {
   } else {
     g0 = a.gscale ? a.gscale[e] : 1.0f;
   }
+
+  __shared__ uint4 la0[256], la1[256], la2[256], la3[256];       // activation ring (4 KB each)
+  __shared__ uint4 lc0[2048], lc1[2048], lc2[2048], lc3[2048];   // code ring (32 KB each)
+  __shared__ __attribute__((aligned(16))) uint8_t ls0[F4_WROWS * 16], ls1[F4_WROWS * 16];   // scale ring
+  const F4MLds L{{la0, la1, la2, la3}, {lc0, lc1, lc2, lc3}, {ls0, ls1}};
+  const int ln = lane & 31;
+
+  for (int mp = 0; mp < valid; mp += F4M_ROWS) {
+    const int pv = min(F4M_ROWS, valid - mp);   // rows of this pass
+    const int p0 = a.offset[e] + m0 + mp;
+    // every wavefront has left the previous pass's last stage before its rings refill
+    if (mp) __syncthreads();
+    // activation DMA (wavefronts 0-3): pass rows 8 wv .. +7, 8 lanes per row
+    {
+      const int r = 8 * (wv & 3) + (lane >> 3);
+      const int rr = r < pv ? r : 0;
+      const int64_t row = (MODE == GEMM_GATEUP) ? a.perm[p0 + rr] / a.K : p0 + rr;
+      src.ao[0] = static_cast<uint32_t>((row * kdim + 8 * ((lane & 7) ^ f4_swz_a(r))) * 2);
+    }
+    // down: the pass's output rows (lane l: row l % 32), read before the main loop
+    int orow_l = 0;
+    if constexpr (MODE != GEMM_GATEUP) orow_l = a.perm[p0 + ((lane & 31) < pv ? (lane & 31) : 0)];
+    f32x16 acc[2];
 #pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    const int row = c32_row(lane, j);
-    int orow_i = 0;
-    if constexpr (MODE != GEMM_GATEUP) orow_i = __shfl(orow_l, row);
-    if (row >= valid) continue;
-    if (MODE == GEMM_GATEUP) {
-      const int jc = nblk * 256 + 32 * wv + ln;
-      if (jc >= a.half_n) continue;
-      static_cast<uint16_t*>(a.out)[static_cast<int64_t>(p0 + row) * a.ldo + jc] =
-          f32_to_bf16(swiglu_clamped(g0 * acc[0][j], g1 * acc[1][j], a.limit));
-    } else {
-      const int64_t orow = orow_i;
+    for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        const int n = nblk * F4_WROWS + 64 * wv + 32 * nt + ln;
-        if (n < a.half_n) static_cast<float*>(a.out)[orow * a.ldo + n] = g0 * acc[nt][j];
+      for (int j = 0; j < 16; ++j) acc[nt][j] = 0.0f;
+    if (wv < 4)
+      f4m_mainloop<MODE, TILED, 1>(L, src, wv, lane, kdim, acc);
+    else
+      f4m_mainloop<MODE, TILED, 0>(L, src, wv, lane, kdim, acc);
+
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int row = c32_row(lane, j);
+      int orow_i = 0;
+      if constexpr (MODE != GEMM_GATEUP) orow_i = __shfl(orow_l, row);
+      if (row >= pv) continue;
+      if (MODE == GEMM_GATEUP) {
+        const int jc = nblk * 256 + 32 * wv + ln;
+        if (jc >= a.half_n) continue;
+        static_cast<uint16_t*>(a.out)[static_cast<int64_t>(p0 + row) * a.ldo + jc] =
+            f32_to_bf16(swiglu_clamped(g0 * acc[0][j], g1 * acc[1][j], a.limit));
+      } else {
+        const int64_t orow = orow_i;
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+          const int n = nblk * F4_WROWS + 64 * wv + 32 * nt + ln;
+          if (n < a.half_n) static_cast<float*>(a.out)[orow * a.ldo + n] = g0 * acc[nt][j];
+        }
       }
     }
   }

@@ -415,7 +415,9 @@ int small_tile_rows(int64_t T) { return T <= MOE_MLP_DECODE_MAX_T ? F4M_ROWS : 0
 // and at least 512 take k_gemm_nvfp4; with small_rows (gate/up) it takes only
 // the tiles of more than small_rows rows (at most slots / (small_rows + 1) of
 // them) and k_gemm_nvfp4_m32 the rest; max_count = the most rows an expert can
-// hold (the token count): at most 32, k_gemm_nvfp4 is not launched.  BF16
+// hold (the token count): at most 64, k_gemm_nvfp4_m32 takes every tile and
+// k_gemm_nvfp4 is not launched (its launch cost 4.4 us at 64 tokens, where no
+// tile had more than 32 rows).  BF16
 // projections (shared expert, dense FFN, router logits) with a reduction
 // length that is a multiple of 128 take k_gemm_bf16; other reduction lengths
 // that are a multiple of 64 the 32x32x16-MFMA kernel (k_gemm_fast); the rest
@@ -432,9 +434,11 @@ void gemm(const GemmArgs& a0, int64_t m_tiles, hipStream_t s, Ev ev, int small_r
         w_rows * a.kdim / 2 < (int64_t(1) << 31)) {
       a.n_blocks = static_cast<int>(cdiv(a.half_n, MODE == GEMM_GATEUP ? F4_WROWS / 2 : F4_WROWS));
       const bool use_small = MODE == GEMM_GATEUP && small_rows == F4M_ROWS;
-      const bool small_only = use_small && max_count >= 0 && max_count <= F4M_ROWS;
+      // up to 64 tokens k_gemm_nvfp4_m32 takes every tile (a tile of more
+      // than 32 rows in two passes)
+      const bool small_only = use_small && max_count >= 0 && max_count <= 2 * F4M_ROWS;
       const int64_t big_tiles = use_small ? std::min<int64_t>(m_tiles, slots / (F4M_ROWS + 1)) : m_tiles;
-      a.skip_rows = use_small ? F4M_ROWS : 0;
+      a.skip_rows = (use_small && !small_only) ? F4M_ROWS : 0;
       with_ct(a.bq_t && a.bs_t, [&](auto ctc) {
         constexpr bool CT = decltype(ctc)::value;
         if (!small_only && big_tiles > 0)

@@ -168,10 +168,19 @@ def test_grouped_gemm_small_tiles(overrides):
     _fresh("ragged_prefill", True, n_sample=100000, **overrides)
 
 
-def test_decode_gemm_form_small_tiles():
-    """The decode form at 64 tokens and more runs the grouped GEMM: 100 tokens over 8 experts
-    (K=2: 25 rows per expert on average, both kernels)."""
-    _fresh("ragged_decode", False, n_sample=100000, T=100, H=1024, I=512, E=8, K=2, Is=64)
+# The decode form runs the grouped GEMM from 64 tokens.  Up to 64 tokens the
+# small-tile kernel takes every gate/up tile, one of more than 32 rows in two
+# passes (expert counts 40, 36, 25, 27 and 27, 37 here, reductions of 768 and
+# 1280); above, the tiles of more than 32 rows go to the 128-row kernel (100
+# tokens over 8 experts, K=2: 25 rows per expert on average).
+DECODE_GEMM_SMALL = [dict(T=64, H=768, I=512, E=4, K=2, Is=64), dict(T=64, H=1280, I=512, E=2, K=1, Is=64),
+                     dict(T=100, H=1024, I=512, E=8, K=2, Is=64)]
+
+
+@pytest.mark.parametrize("overrides", DECODE_GEMM_SMALL,
+                         ids=[f"T{o['T']}_H{o['H']}_E{o['E']}_K{o['K']}" for o in DECODE_GEMM_SMALL])
+def test_decode_gemm_form_small_tiles(overrides):
+    _fresh("ragged_decode", False, n_sample=100000, **overrides)
 
 
 @pytest.mark.parametrize("prefill", [False, True])
