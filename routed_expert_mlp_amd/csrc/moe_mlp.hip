@@ -855,16 +855,21 @@ int run_layer(const moe_mlp_config* c, const moe_mlp_weights* w, const uint16_t*
     Perm pm{at<int32_t>(ws, p.count), at<int32_t>(ws, p.offset), at<int32_t>(ws, p.perm),
             at<int32_t>(ws, p.n_tiles), at<int32_t>(ws, p.tile_e), at<int32_t>(ws, p.tile_m0)};
     const Ev pe = ev(2);
-    const int nchunk = static_cast<int>(cdiv(S, PERM_CHUNK));
-    int32_t* phist = at<int32_t>(ws, p.phist);
-    int32_t* prank = at<int32_t>(ws, p.prank);
-    launch(k_perm_hist, dim3(nchunk), dim3(PERM_CHUNK), s, pe.a, nullptr, ids, static_cast<int>(S), E, phist, prank);
-    int32_t* pbase = at<int32_t>(ws, p.pbase);
     const int small_rows = small_tile_rows(T);
-    launch(k_perm_schedule, dim3(1), dim3(1024), s, nullptr, nullptr, E, nchunk, GM_BM, small_rows, phist, pbase,
-           pm);
-    launch(k_perm_scatter, dim3(static_cast<unsigned>(cdiv(S, 256))), dim3(256), s, nullptr, pe.b, ids,
-           static_cast<int>(S), E, pbase, prank, pm);
+    if (S <= PERM_SMALL_MAX) {
+      launch(k_perm_small, dim3(1), dim3(1024), s, pe.a, pe.b, ids, static_cast<int>(S), E, GM_BM, small_rows, pm);
+    } else {
+      const int nchunk = static_cast<int>(cdiv(S, PERM_CHUNK));
+      int32_t* phist = at<int32_t>(ws, p.phist);
+      int32_t* prank = at<int32_t>(ws, p.prank);
+      launch(k_perm_hist, dim3(nchunk), dim3(PERM_CHUNK), s, pe.a, nullptr, ids, static_cast<int>(S), E, phist,
+             prank);
+      int32_t* pbase = at<int32_t>(ws, p.pbase);
+      launch(k_perm_schedule, dim3(1), dim3(1024), s, nullptr, nullptr, E, nchunk, GM_BM, small_rows, phist, pbase,
+             pm);
+      launch(k_perm_scatter, dim3(static_cast<unsigned>(cdiv(S, 256))), dim3(256), s, nullptr, pe.b, ids,
+             static_cast<int>(S), E, pbase, prank, pm);
+    }
     GemmArgs g{};
     g.n_tiles = pm.n_tiles;
     g.tile_expert = pm.tile_expert;

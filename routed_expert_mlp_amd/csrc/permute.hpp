@@ -11,6 +11,8 @@
 //                       first) and turns the histograms into the sorted
 //                       position of each (chunk, expert) run;
 //   3. k_perm_scatter:  one thread per slot writes it at run start + rank.
+// Up to PERM_SMALL_MAX slots (decode-sized batches) k_perm_small does all
+// three in one workgroup, with the order within an expert left free.
 #pragma once
 
 #include "common.hpp"
@@ -51,24 +53,14 @@ __global__ __launch_bounds__(PERM_CHUNK) void k_perm_hist(const int32_t* __restr
   for (int x = tid; x < E; x += PERM_CHUNK) hist[static_cast<int64_t>(b) * E + x] = s_h[x];
 }
 
-// 2. One workgroup of 1024 threads (E <= 1024): expert counts (sums over the
-// chunks), their exclusive scan into offsets, the cut of each expert's rows
-// into bm-row GEMM tiles, and base[b][e] = the sorted position of chunk b's
-// first slot of expert e (a separate array, so the loads of both passes over
-// the chunks stay in flight together).  Tiles of more than small_rows rows
-// come first, in expert order, then the rest (an expert's last tile when it
-// is that short), so that two GEMM kernels can each take one range; with
-// small_rows = 0 the order is plain expert order.
-__global__ __launch_bounds__(1024) void k_perm_schedule(int E, int nblk, int bm, int small_rows,
-                                                        const int32_t* __restrict__ hist, int32_t* __restrict__ base,
-                                                        Perm p) {
-  __shared__ int s_w[3][16];
+// Expert counts -> offsets, tiles and tile counts, for one workgroup of 1024
+// threads (E <= 1024; thread tid < E holds expert tid's count c); returns the
+// expert's offset.  s_w: LDS for the 16 wavefronts' partial sums.  Tiles of
+// more than small_rows rows come first, in expert order, then the rest (an
+// expert's last tile when it is that short), so that two GEMM kernels can
+// each take one range; with small_rows = 0 the order is plain expert order.
+__device__ __forceinline__ int perm_tiles(int c, int E, int bm, int small_rows, Perm p, int (*s_w)[16]) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  int c = 0;
-  if (tid < E) {
-#pragma unroll 16
-    for (int b = 0; b < nblk; ++b) c += hist[static_cast<int64_t>(b) * E + tid];
-  }
   const int nt = static_cast<int>(cdiv(c, bm));
   const int ns = (nt > 0 && c - (nt - 1) * bm <= small_rows) ? 1 : 0;   // a short last tile
   const int nb = nt - ns;
@@ -114,6 +106,26 @@ __global__ __launch_bounds__(1024) void k_perm_schedule(int E, int nblk, int bm,
       p.n_tiles[0] = soff + ns;
       p.n_tiles[1] = nbig;
     }
+  }
+  return off;
+}
+
+// 2. One workgroup of 1024 threads: expert counts (sums over the chunks),
+// offsets and tiles (perm_tiles), and base[b][e] = the sorted position of
+// chunk b's first slot of expert e (a separate array, so the loads of both
+// passes over the chunks stay in flight together).
+__global__ __launch_bounds__(1024) void k_perm_schedule(int E, int nblk, int bm, int small_rows,
+                                                        const int32_t* __restrict__ hist, int32_t* __restrict__ base,
+                                                        Perm p) {
+  __shared__ int s_w[3][16];
+  const int tid = threadIdx.x;
+  int c = 0;
+  if (tid < E) {
+#pragma unroll 16
+    for (int b = 0; b < nblk; ++b) c += hist[static_cast<int64_t>(b) * E + tid];
+  }
+  const int off = perm_tiles(c, E, bm, small_rows, p, s_w);
+  if (tid < E) {
     int run = off;
 #pragma unroll 16
     for (int b = 0; b < nblk; ++b) {
@@ -121,6 +133,38 @@ __global__ __launch_bounds__(1024) void k_perm_schedule(int E, int nblk, int bm,
       base[q] = run;
       run += hist[q];
     }
+  }
+}
+
+// All three steps in one workgroup of 1024 threads for up to PERM_SMALL_MAX
+// slots (decode-sized batches, where the three launches cost more than the
+// work): LDS counts, the same offsets and tiles (perm_tiles), then each slot
+// at its expert's offset plus an LDS counter.  The order of the slots within
+// an expert is the order of those atomic increments, not ascending; no result
+// depends on it (every row of a tile is computed alone and written back to its
+// own slot).
+constexpr int PERM_SMALL_MAX = 8192;
+
+__global__ __launch_bounds__(1024) void k_perm_small(const int32_t* __restrict__ ids, int nslot, int E, int bm,
+                                                     int small_rows, Perm p) {
+  __shared__ int s_cnt[PERM_MAX_E];
+  __shared__ int s_off[PERM_MAX_E];
+  __shared__ int s_w[3][16];
+  const int tid = threadIdx.x;
+  for (int e = tid; e < E; e += 1024) s_cnt[e] = 0;
+  __syncthreads();
+  for (int i = tid; i < nslot; i += 1024) atomicAdd(&s_cnt[ids[i]], 1);
+  __syncthreads();
+  const int c = tid < E ? s_cnt[tid] : 0;
+  const int off = perm_tiles(c, E, bm, small_rows, p, s_w);
+  if (tid < E) {
+    s_off[tid] = off;
+    s_cnt[tid] = 0;
+  }
+  __syncthreads();
+  for (int i = tid; i < nslot; i += 1024) {
+    const int e = ids[i];
+    p.perm[s_off[e] + atomicAdd(&s_cnt[e], 1)] = i;
   }
 }
 
