@@ -1,6 +1,6 @@
-// Routed NVFP4 grouped GEMM for tiles of at most 32 rows (decode from a few
-// dozen tokens, where an expert holds a handful of rows, and the ragged last
-// tile of an expert in prefill): the products, their order and the outputs of
+// Routed NVFP4 grouped GEMM, gate/up + clamped SwiGLU, for tiles of at most
+// 32 rows (decode with up to a few hundred tokens, where an expert holds a
+// handful of rows): the products, their order and the outputs of
 // k_gemm_nvfp4, with the LDS spent on the weight stream.
 //
 // A tile of at most 32 rows runs a single 32-row MFMA slice per weight
@@ -65,7 +65,7 @@ constexpr int f4m_wait() {
 template <int MODE, bool TILED, int NA>
 __device__ __forceinline__ void f4m_mainloop(const F4MLds& L, const F4Src& src, int wv, int lane, int kdim,
                                              f32x16 (&acc)[2]) {
-  constexpr int NT_ROWS = MODE == GEMM_GATEUP ? 256 : 32;
+  constexpr int NT_ROWS = 256;                 // gate row -> its up row
   const int g = lane >> 5, ln = lane & 31;
   const int nblk4 = kdim >> 8;                 // blocks of four stages, at least 2
 
@@ -92,7 +92,7 @@ __device__ __forceinline__ void f4m_mainloop(const F4MLds& L, const F4Src& src, 
                                      (void __attribute__((address_space(3)))*)(L.s[SSL] + wv * 1024), 16, 0, 0);
   };
 
-  const int prow = (MODE == GEMM_GATEUP ? 32 * wv : 64 * wv) + ln;
+  const int prow = 32 * wv + ln;               // this lane's gate row within the workgroup
   const int sc = f4_swz_c(prow), sa = f4_swz_a(ln);
   constexpr int S_STAGE = TILED ? 128 : 4;
   int aidx[4];
@@ -222,6 +222,9 @@ __device__ __forceinline__ void f4m_mainloop(const F4MLds& L, const F4Src& src, 
 // is rare and an extra launch of k_gemm_nvfp4 for it would cost more).
 template <int MODE, bool TILED>
 __global__ __launch_bounds__(F4_THREADS, 1) void k_gemm_nvfp4_m32(GemmArgs a) {
+  // gate/up only: the down projection stays on k_gemm_nvfp4 (its short
+  // reduction did not pay for this kernel's deeper ring: 3% slower, measured)
+  static_assert(MODE == GEMM_GATEUP, "k_gemm_nvfp4_m32 computes the gate/up projection");
   const int nbn = a.n_blocks;
   const int nbig = a.skip_rows ? a.n_tiles[1] : 0;
   const int ntl = a.n_tiles[0] - nbig;
@@ -241,14 +244,10 @@ __global__ __launch_bounds__(F4_THREADS, 1) void k_gemm_nvfp4_m32(GemmArgs a) {
   F4Src src;
   src.a = reinterpret_cast<const uint8_t*>(a.a);
   src.ao[1] = 0;
+  // weight row of workgroup row p (0..511: 256 gate rows, then the matching up rows)
   auto wrow = [&](int p) -> int64_t {
-    if (MODE == GEMM_GATEUP) {
-      const int j = nblk * 256 + (p & 255);
-      return j < a.half_n ? (p < 256 ? j : a.half_n + j) : 0;
-    } else {
-      const int n = nblk * F4_WROWS + p;
-      return n < a.half_n ? n : 0;
-    }
+    const int j = nblk * 256 + (p & 255);
+    return j < a.half_n ? (p < 256 ? j : a.half_n + j) : 0;
   };
   src.c = (TILED ? a.bq_t : a.bq) + e * a.stride_q;
 #pragma unroll
@@ -267,13 +266,8 @@ __global__ __launch_bounds__(F4_THREADS, 1) void k_gemm_nvfp4_m32(GemmArgs a) {
   } else {
     src.so = static_cast<uint32_t>(wrow(64 * wv + lane) * (kdim >> 4));
   }
-  float g0, g1 = 1.0f;
-  if (MODE == GEMM_GATEUP) {
-    g0 = a.gscale ? a.gscale[2 * e] : 1.0f;
-    g1 = a.gscale ? a.gscale[2 * e + 1] : 1.0f;
-  } else {
-    g0 = a.gscale ? a.gscale[e] : 1.0f;
-  }
+  const float g0 = a.gscale ? a.gscale[2 * e] : 1.0f;
+  const float g1 = a.gscale ? a.gscale[2 * e + 1] : 1.0f;
 
   __shared__ uint4 la0[256], la1[256], la2[256], la3[256];       // activation ring (4 KB each)
   __shared__ uint4 lc0[2048], lc1[2048], lc2[2048], lc3[2048];   // code ring (32 KB each)
@@ -290,12 +284,9 @@ __global__ __launch_bounds__(F4_THREADS, 1) void k_gemm_nvfp4_m32(GemmArgs a) {
     {
       const int r = 8 * (wv & 3) + (lane >> 3);
       const int rr = r < pv ? r : 0;
-      const int64_t row = (MODE == GEMM_GATEUP) ? a.perm[p0 + rr] / a.K : p0 + rr;
+      const int64_t row = a.perm[p0 + rr] / a.K;   // the slot's token
       src.ao[0] = static_cast<uint32_t>((row * kdim + 8 * ((lane & 7) ^ f4_swz_a(r))) * 2);
     }
-    // down: the pass's output rows (lane l: row l % 32), read before the main loop
-    int orow_l = 0;
-    if constexpr (MODE != GEMM_GATEUP) orow_l = a.perm[p0 + ((lane & 31) < pv ? (lane & 31) : 0)];
     f32x16 acc[2];
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt)
@@ -306,25 +297,14 @@ __global__ __launch_bounds__(F4_THREADS, 1) void k_gemm_nvfp4_m32(GemmArgs a) {
     else
       f4m_mainloop<MODE, TILED, 0>(L, src, wv, lane, kdim, acc);
 
+    // lane holds rows c32_row(lane, j) of gate column jc (acc[0]) and up column jc (acc[1])
+    const int jc = nblk * 256 + 32 * wv + ln;
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
       const int row = c32_row(lane, j);
-      int orow_i = 0;
-      if constexpr (MODE != GEMM_GATEUP) orow_i = __shfl(orow_l, row);
-      if (row >= pv) continue;
-      if (MODE == GEMM_GATEUP) {
-        const int jc = nblk * 256 + 32 * wv + ln;
-        if (jc >= a.half_n) continue;
-        static_cast<uint16_t*>(a.out)[static_cast<int64_t>(p0 + row) * a.ldo + jc] =
-            f32_to_bf16(swiglu_clamped(g0 * acc[0][j], g1 * acc[1][j], a.limit));
-      } else {
-        const int64_t orow = orow_i;
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
-          const int n = nblk * F4_WROWS + 64 * wv + 32 * nt + ln;
-          if (n < a.half_n) static_cast<float*>(a.out)[orow * a.ldo + n] = g0 * acc[nt][j];
-        }
-      }
+      if (row >= pv || jc >= a.half_n) continue;
+      static_cast<uint16_t*>(a.out)[static_cast<int64_t>(p0 + row) * a.ldo + jc] =
+          f32_to_bf16(swiglu_clamped(g0 * acc[0][j], g1 * acc[1][j], a.limit));
     }
   }
 }

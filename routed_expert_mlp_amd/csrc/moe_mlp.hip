@@ -444,9 +444,11 @@ void gemm(const GemmArgs& a0, int64_t m_tiles, hipStream_t s, Ev ev, int small_r
         if (!small_only && big_tiles > 0)
           launch(k_gemm_nvfp4<MODE, CT>, dim3(static_cast<unsigned>(8 * cdiv(big_tiles * a.n_blocks, 8))),
                  dim3(F4_THREADS), s, ev.a, use_small ? nullptr : ev.b, a);
-        if (use_small)
-          launch(k_gemm_nvfp4_m32<MODE, CT>, dim3(static_cast<unsigned>(8 * cdiv(m_tiles * a.n_blocks, 8))),
-                 dim3(F4_THREADS), s, (small_only || big_tiles == 0) ? ev.a : nullptr, ev.b, a);
+        if constexpr (MODE == GEMM_GATEUP) {
+          if (use_small)
+            launch(k_gemm_nvfp4_m32<MODE, CT>, dim3(static_cast<unsigned>(8 * cdiv(m_tiles * a.n_blocks, 8))),
+                   dim3(F4_THREADS), s, (small_only || big_tiles == 0) ? ev.a : nullptr, ev.b, a);
+        }
       });
       return;
     }
