@@ -432,10 +432,10 @@ def main():
         lines = summarize_traffic(*args.summarize_traffic)
         head = ["# HBM traffic of the one-token decode kernels, flash_decode_t1 (T=1, H=4096, I=1536, E=288, K=8,",
                 "# Is=1536), from two rocprofv3 counter runs on one MI355X (from the repository root):",
-                "#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch -o run -- \\",
+                "#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d <out>/pmc_fetch -o run -- \\",
                 "#       python3 bench.py --steps 20 --warmup 5 --no-prefill --no-extra-decode --no-variants \\",
                 "#       --no-cpu-baseline --calibrate-copy",
-                "#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write -o run -- (same)",
+                "#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d <out>/pmc_write -o run -- (same)",
                 "#   python3 bench.py --summarize-traffic <fetch counter_collection.csv> <write counter_collection.csv>",
                 "# FETCH_SIZE / WRITE_SIZE are KiB per dispatch; each is scaled so that the run's 512 MiB device",
                 "# copies read and write 512 MiB.  bench.py reports hbm_bytes_per_launch (k_dec_gateup) as",
