@@ -566,9 +566,10 @@ def main():
         for T in (2, 4, 16, 64):
             xs_t = [x_dev(w, range(100 + r * T, 100 + (r + 1) * T), dev) for r in range(R)]
             wts_t = wts
-            if T >= 64:
-                # from 64 tokens decode runs the grouped GEMM, which reads the
-                # tile-layout copies of the routed weights (packed once at load)
+            if T >= 16:
+                # decode batches read the tile-layout copies of the routed
+                # weights (packed once at load) in their few-token MFMA
+                # kernels and the grouped GEMM
                 if wts_tiled is None:
                     wts_tiled = [capi.with_tiled_weights(x) for x in wts]
                 wts_t = wts_tiled
@@ -577,8 +578,9 @@ def main():
                 outs_t = [torch.empty((T, w.H), dtype=torch.bfloat16, device=dev) for _ in range(R)]
                 st_t = stage_times(cfg, wts_t, xs_t, outs_t, False, 4 * R, ev, capi.workspace(cfg, T, False, dev))
                 extra[f"decode_t{T}"]["stage_us"] = {k: round(v * 1e3, 1) for k, v in st_t.items()}
-            if T >= 64:
-                extra[f"decode_t{T}"]["weights"] = "routed NVFP4 in the tile layout (grouped-GEMM form)"
+            if T >= 16:
+                extra[f"decode_t{T}"]["weights"] = ("routed NVFP4: row-major and tile-layout copies resident "
+                                                    "(the few-token MFMA kernels read the tile layout)")
         # one resident copy of the codes: the same copies with the row-major
         # codes left out, so every kernel reads the tile-layout codes
         one = [dataclasses.replace(x, w13_q=None, w2_q=None) for x in wts_tiled]
@@ -614,7 +616,8 @@ def main():
             line["workload"] = f"T={T}, K={wv.K}, E={wv.E}, bias " + (
                 "+1.0 on 8 hot experts, U(-0.1,0.1) elsewhere" if wv.hot_experts else f"U(-{wv.bias_amp}, {wv.bias_amp})")
             if T >= 64:
-                line["weights"] = "routed NVFP4 in the tile layout (grouped-GEMM form)"
+                line["weights"] = ("routed NVFP4: row-major and tile-layout copies resident "
+                                   "(the few-token MFMA kernels read the tile layout)")
             extra[name] = line
             del wts_v, bv, xs_v
             torch.cuda.empty_cache()

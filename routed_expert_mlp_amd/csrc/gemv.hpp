@@ -45,6 +45,7 @@ struct GemvArgs {
   const uint16_t* in;    // input rows (bf16), row length `cols`
   void* out;             // gate/up: bf16 [.., half_rows]; down: fp32 or bf16 [.., half_rows]
   float limit;
+  int sorted_out;        // routed gate/up: output row = the slot's position in the group lists
 };
 
 // One 16-byte chunk of an NVFP4 row against one token's 32 activations.
@@ -143,7 +144,7 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
     for (int t = 0; t < TC; ++t) {
       const int p = t0 + min(t, nt - 1);
       const int slot = a.n_groups ? a.g_slots[slot_base + p] : slot_base + p;
-      out_row[t] = slot;
+      out_row[t] = a.sorted_out ? slot_base + p : slot;
       in_row[t] = (a.n_groups && MODE == GEMV_GATEUP) ? slot / a.K : slot;
     }
     float acc[NR][TC];

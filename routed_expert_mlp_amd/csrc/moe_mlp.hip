@@ -385,6 +385,36 @@ void gemv(const GemvArgs& a, int groups, hipStream_t s, Ev ev, bool tiled_codes 
   }
 }
 
+// Routed NVFP4 down projection of decode batches (up to MOE_MLP_DECODE_MAX_T
+// tokens, a few per expert) on k_skinny_f4_down: reductions of 512, 1024,
+// 1536 or 2048 columns and output rows a multiple of 64.
+bool skinny_down_ok(const moe_mlp_config* c, int64_t T) {
+  const int I = c->moe_intermediate;
+  return c->kind == MOE_MLP_KIND_ROUTED && T <= MOE_MLP_DECODE_MAX_T && c->hidden % SF4_ROWS == 0 && I % 512 == 0 &&
+         I <= 2048;
+}
+
+// groups = grid.y (the largest number of expert groups); tiled = the codes
+// are the tile-layout copy.  8 activation rows of LDS per pass (decode
+// groups hold about 1..8 tokens) keep four workgroups on a CU; 16 rows per
+// pass measured slower at 16 and 64 tokens (occupancy 3).
+void skinny_down(const SkinnyF4Args& a, int kdim, int groups, bool tiled, hipStream_t s, Ev ev) {
+  const dim3 grid(static_cast<unsigned>(a.N / SF4_ROWS), static_cast<unsigned>(groups));
+  with_ct(tiled, [&](auto ctc) {
+    constexpr bool CT = decltype(ctc)::value;
+    auto go = [&](auto nu) {
+      constexpr int NU = decltype(nu)::value;
+      launch(k_skinny_f4_down<NU, 8, CT>, grid, dim3(256), s, ev.a, ev.b, a);
+    };
+    switch (kdim / 128) {
+      case 4: go(std::integral_constant<int, 4>{}); break;
+      case 8: go(std::integral_constant<int, 8>{}); break;
+      case 12: go(std::integral_constant<int, 12>{}); break;
+      default: go(std::integral_constant<int, 16>{}); break;
+    }
+  });
+}
+
 // Routed FP8 projections: k_gemm_f8d (LDS DMA rings) when its 32-bit DMA
 // offsets hold (activation rows and weight rows times the row length below
 // 2^31) and the reduction is at most 8192; otherwise k_gemm_f8.
@@ -936,6 +966,20 @@ int run_layer(const moe_mlp_config* c, const moe_mlp_weights* w, const uint16_t*
       gd.stride_s = int64_t(H / MOE_MLP_FP8_BLOCK) * (I / MOE_MLP_FP8_BLOCK);
       gd.gscale = nullptr;
       gemm_fp8<GEMM_DOWN_SLOT_F32>(gd, p.max_tiles, s, ev(4));
+    } else if (skinny_down_ok(c, T)) {
+      SkinnyF4Args sa{};
+      const bool tiled = w->w2_q_tiled && (!w->w2_q || w->w2_s_tiled);
+      sa.wq = tiled ? w->w2_q_tiled : w->w2_q;
+      sa.ws = w->w2_s;
+      sa.stride_q = int64_t(H) * I / 2;
+      sa.stride_s = int64_t(H) * I / 16;
+      sa.gscale = w->w2_g;
+      sa.N = H;
+      sa.offsets = pm.offset;
+      sa.out_idx = pm.perm;
+      sa.in = h;
+      sa.out = y;
+      skinny_down(sa, I, E, tiled, s, ev(4));
     } else {
       gemm<true, GEMM_DOWN_SLOT_F32, true>(gd, p.max_tiles, s, ev(4), small_rows, S, T);
     }
@@ -1009,6 +1053,10 @@ int run_layer(const moe_mlp_config* c, const moe_mlp_weights* w, const uint16_t*
     gu.cols = H;
     gu.in = x;
     gu.out = h;
+    // with k_skinny_f4_down the h rows are in group order, else in slot
+    // order for the down GEMV
+    const bool sk_down = skinny_down_ok(c, T);
+    gu.sorted_out = sk_down ? 1 : 0;
     gemv<true, GEMV_GATEUP, 2>(gu, groups, s, ev(3), !w->w13_q);
     if (Is && p.skinny) skinny_gemm(hs, w->shared_w2, H, Is, Ti, ys, s, ev(4));
     else if (Is) gemv<false, GEMV_DOWN_F32, 2>(bf16_gemv_args(w->shared_w2, H, Is, Ti, hs, ys, L), 1, s, ev(4));
@@ -1023,7 +1071,26 @@ int run_layer(const moe_mlp_config* c, const moe_mlp_weights* w, const uint16_t*
     gd.cols = I;
     gd.in = h;
     gd.out = y;
-    gemv<true, GEMV_DOWN_F32, 4>(gd, groups, s, ev(5), !w->w2_q);
+    if (sk_down) {
+      SkinnyF4Args sa{};
+      const bool tiled = w->w2_q_tiled && (!w->w2_q || w->w2_s_tiled);
+      sa.wq = tiled ? w->w2_q_tiled : w->w2_q;
+      sa.ws = w->w2_s;
+      sa.stride_q = gd.stride_q;
+      sa.stride_s = gd.stride_s;
+      sa.gscale = w->w2_g;
+      sa.N = H;
+      sa.n_groups = gr.n_groups;
+      sa.g_expert = gr.expert;
+      sa.g_count = gr.count;
+      sa.g_offset = gr.offset;
+      sa.out_idx = gr.slots;
+      sa.in = h;
+      sa.out = y;
+      skinny_down(sa, I, groups, tiled, s, ev(5));
+    } else {
+      gemv<true, GEMV_DOWN_F32, 4>(gd, groups, s, ev(5), !w->w2_q);
+    }
   }
   const int64_t nq = T * (H / 4);
   const Ev ce = ev(prefill ? 7 : 6);

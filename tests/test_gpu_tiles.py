@@ -98,8 +98,9 @@ def test_tiled_weights_bitwise_full_size():
 
 @pytest.mark.parametrize("T", [1, 16, 64])
 def test_tiled_weights_decode_bitwise(T):
-    """Decode ignores the tiled copies below 64 tokens (GEMV forms) and reads
-    them from 64 tokens on (grouped-GEMM form): bitwise the same either way."""
+    """Decode reads the tiled copies in the down projection of the expert-GEMV
+    form (below 64 tokens) and in both projections from 64 tokens on
+    (grouped-GEMM form): bitwise the same either way."""
     w = synth.workload("ragged_decode", T=T, H=512, I=512, E=16, K=4, Is=128)
     say(f"[case] tiled weights, decode T={w.T} H={w.H} I={w.I} E={w.E} K={w.K}")
     _run_both(DeviceRouted(RoutedInputs(w)), f"decode T={T}", prefill=False)
