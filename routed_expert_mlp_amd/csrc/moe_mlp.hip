@@ -395,16 +395,18 @@ bool skinny_down_ok(const moe_mlp_config* c, int64_t T) {
 }
 
 // groups = grid.y (the largest number of expert groups); tiled = the codes
-// are the tile-layout copy.  8 activation rows of LDS per pass (decode
-// groups hold about 1..8 tokens) keep four workgroups on a CU; 16 rows per
-// pass measured slower at 16 and 64 tokens (occupancy 3).
+// are the tile-layout copy.  12 activation rows of LDS per pass (37 KB) are
+// the most that keep four workgroups on a CU; measured against 8 rows (the
+// same at 16 and 64 tokens; 64 tokens top-16 with 8 hot experts 148.9 ->
+// 135.0 us, 256 tokens 236.9 -> 220.0 us) and 16 rows (three workgroups on
+// a CU: 64 tokens 158 -> 175 us).
 void skinny_down(const SkinnyF4Args& a, int kdim, int groups, bool tiled, hipStream_t s, Ev ev) {
   const dim3 grid(static_cast<unsigned>(a.N / SF4_ROWS), static_cast<unsigned>(groups));
   with_ct(tiled, [&](auto ctc) {
     constexpr bool CT = decltype(ctc)::value;
     auto go = [&](auto nu) {
       constexpr int NU = decltype(nu)::value;
-      launch(k_skinny_f4_down<NU, 8, CT>, grid, dim3(256), s, ev.a, ev.b, a);
+      launch(k_skinny_f4_down<NU, 12, CT>, grid, dim3(256), s, ev.a, ev.b, a);
     };
     switch (kdim / 128) {
       case 4: go(std::integral_constant<int, 4>{}); break;

@@ -58,16 +58,16 @@ def test_decode_parity(name, n_sample):
 
 # Decode batches whose routed down projection runs k_skinny_f4_down
 # (reduction I a multiple of 512 up to 2048, output rows a multiple of 64):
-# groups within one LDS pass (8 rows) and groups of several passes, the
+# groups within one LDS pass (12 rows) and groups of several passes, the
 # expert-GEMV form (below 64 tokens) and the grouped-GEMM form (64..256
 # tokens), each unit count the kernel is built for.
-SKINNY = [dict(T=12, H=512, I=512, E=4, K=4, Is=128),       # 12 rows per expert: 2 passes
+SKINNY = [dict(T=16, H=512, I=512, E=4, K=4, Is=128),       # 16 rows per expert: 2 passes
           dict(T=7, H=1024, I=1024, E=16, K=4, Is=0),
           dict(T=24, H=2048, I=1536, E=16, K=4, Is=128),
           dict(T=24, H=256, I=1536, E=16, K=4, Is=128),
           dict(T=40, H=512, I=512, E=16, K=4, Is=128),
           dict(T=48, H=192, I=2048, E=6, K=2, Is=96),       # 16 rows per expert
-          dict(T=100, H=1024, I=1536, E=8, K=4, Is=128),    # ~50 rows per expert: 7 passes
+          dict(T=100, H=1024, I=1536, E=8, K=4, Is=128),    # ~50 rows per expert: 5 passes
           dict(T=256, H=512, I=512, E=16, K=2, Is=128)]
 
 
