@@ -498,6 +498,16 @@ __global__ __launch_bounds__(1024) void k_dec_down_combine1(
   __shared__ float part[16][R];
   __shared__ float ysp[R];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  {
+    // grid.y = token (decode of a few tokens): token t's K slots, its shared
+    // vector and its output row
+    const int t = blockIdx.y;
+    ids += t * K;
+    wts += t * K;
+    h += static_cast<int64_t>(t) * K * I;
+    hs += static_cast<int64_t>(t) * Is;
+    out += static_cast<int64_t>(t) * H;
+  }
   const int r0 = blockIdx.x * R;
   if (wv < K) {
     // routed slot wv: ids first; then h_k (independent of the ids); then the R down rows

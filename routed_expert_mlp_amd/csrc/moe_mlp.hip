@@ -688,11 +688,12 @@ void launch_down_combine(const moe_mlp_config* c, const moe_mlp_weights* w, cons
 constexpr int kDown1Rows = 16, kDown1Shared = 4;
 
 void launch_down_combine1(const moe_mlp_config* c, const moe_mlp_weights* w, const uint16_t* h, const uint16_t* hs,
-                          const int32_t* ids, const float* wts, uint16_t* out, hipStream_t s, Ev ev) {
+                          const int32_t* ids, const float* wts, uint16_t* out, int T, hipStream_t s, Ev ev) {
   constexpr int R = kDown1Rows, NSW = kDown1Shared;
   const int H = c->hidden, K = c->top_k;
   const int Is = c->n_shared_experts ? c->shared_intermediate : 0;
-  const dim3 grid(static_cast<unsigned>(cdiv(H, R))), block(static_cast<unsigned>((K + NSW) * 64));
+  const dim3 grid(static_cast<unsigned>(cdiv(H, R)), static_cast<unsigned>(T)),
+      block(static_cast<unsigned>((K + NSW) * 64));
   const uint8_t* q2 = codes2(w);
   auto go = [&](auto kern) {
     launch(kern, grid, block, s, ev.a, ev.b, h, q2, w->w2_s, w->w2_g, w->shared_w2, hs, Is, ids, wts,
@@ -787,8 +788,8 @@ void decode1(const moe_mlp_config* c, const moe_mlp_weights* w, const uint16_t* 
     return;
   }
   dec_gateup(c, w, x, logits, ids, wts, ids_out, w_out, h, T, s, e1);
-  if (T == 1 && K + kDown1Shared <= 16) {
-    launch_down_combine1(c, w, h, hs, ids, wts, out, s, e2);
+  if (K + kDown1Shared <= 16) {
+    launch_down_combine1(c, w, h, hs, ids, wts, out, T, s, e2);
     return;
   }
   // one slot per wavefront up to 8 slots (4 or 8 wavefronts), else 16 wavefronts with up to 4 slots each
