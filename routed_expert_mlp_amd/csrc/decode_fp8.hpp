@@ -291,4 +291,136 @@ __global__ __launch_bounds__(NW * 64) void k_dec_down_combine_f8(
   }
 }
 
+// -------------------------------------------------------------------------
+// 3' (FP8). The same step with R output rows per block and a grid row per
+// token (blockIdx.y = t: token t's K slots, shared vector and output row),
+// in the layout of k_dec_down_combine1: wavefront k < K takes slot t*K + k
+// (its R FP8 down rows, lane l its chunks l, l+64, ..., ND of them, and the
+// slot's h chunks, read once for all R rows), wavefronts K..K+NSW-1 take R/NSW
+// shared down rows each.  Per (slot, row) and per shared row the products
+// and their orders, and the combine order, are those of
+// k_dec_down_combine_f8, so the two kernels agree bit for bit.
+//   requires K + NSW <= 16; R divides 128 (the block's rows share one scale
+//   row block); I <= 1024 ND
+// -------------------------------------------------------------------------
+template <int R, int NSW, int NSC, int ND, class G>
+__global__ __launch_bounds__(1024) void k_dec_down_combine1_f8(
+    const uint16_t* __restrict__ h, const uint8_t* __restrict__ q2, const float* __restrict__ s2,
+    const uint16_t* __restrict__ sw2, const uint16_t* __restrict__ hs, int Is_, const int32_t* __restrict__ ids,
+    const float* __restrict__ wts, int E_, int K_, int H_, int I_, uint16_t* __restrict__ out) {
+  static_assert(R % NSW == 0, "whole shared rows per wavefront");
+  static_assert(F8_BLOCK % R == 0, "a block's rows share one scale row block");
+  constexpr int SR = R / NSW;
+  const int K = G::K ? G::K : K_, E = G::E ? G::E : E_, H = G::H ? G::H : H_, I = G::I ? G::I : I_;
+  const int Is = G::IS >= 0 ? G::IS : Is_;
+  __shared__ float part[16][R];
+  __shared__ float ysp[R];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  {
+    const int t = blockIdx.y;
+    ids += t * K;
+    wts += t * K;
+    h += static_cast<int64_t>(t) * K * I;
+    hs += static_cast<int64_t>(t) * Is;
+    out += static_cast<int64_t>(t) * H;
+  }
+  const int r0 = blockIdx.x * R;
+  if (wv < K) {
+    // routed slot wv: ids first; then h_k (independent of the ids); then the R down rows
+    const int nd = I >> 4;                      // 16-byte chunks per routed down row
+    const int nsb = I / F8_BLOCK;
+    const int idv = ids[wv];
+    const float wsl = wts[wv];
+    uint32_t xp[ND][8];
+#pragma unroll
+    for (int i = 0; i < ND; ++i) {
+      const int c = min(lane + 64 * i, nd - 1);
+      const uint4* hp = reinterpret_cast<const uint4*>(h + static_cast<int64_t>(wv) * I + 16 * c);
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const uint4 v = hp[q];
+        xp[i][4 * q] = v.x; xp[i][4 * q + 1] = v.y; xp[i][4 * q + 2] = v.z; xp[i][4 * q + 3] = v.w;
+      }
+    }
+    const int e = min(max(idv, 0), E - 1);
+    uint4 cw[R][ND];
+    float sc[ND];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int64_t row = static_cast<int64_t>(e) * H + min(r0 + r, H - 1);
+#pragma unroll
+      for (int i = 0; i < ND; ++i)
+        cw[r][i] = *reinterpret_cast<const uint4*>(q2 + row * I + 16 * min(lane + 64 * i, nd - 1));
+    }
+    const float* srow = s2 + (static_cast<int64_t>(e) * (H / F8_BLOCK) + min(r0, H - 1) / F8_BLOCK) * nsb;
+#pragma unroll
+    for (int i = 0; i < ND; ++i) sc[i] = srow[min(lane + 64 * i, nd - 1) >> 3];
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < ND; ++i)
+      if (lane + 64 * i >= nd) {
+        sc[i] = 0.0f;
+#pragma unroll
+        for (int r = 0; r < R; ++r) cw[r][i] = make_uint4(0, 0, 0, 0);
+      }
+    float acc[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      acc[r] = 0.0f;
+#pragma unroll
+      for (int i = 0; i < ND; ++i) acc[r] = fmaf(e4m3x16_dot(cw[r][i], xp[i]), sc[i], acc[r]);
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) acc[r] = wave_sum(acc[r]);
+    if (lane == 0) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) part[wv][r] = wsl * acc[r];
+    }
+  } else if (wv < K + NSW && Is > 0) {
+    // shared rows r0 + sr0 .. + SR - 1 against hs
+    const int sr0 = (wv - K) * SR;
+    const int nsc = Is >> 3;
+    uint4 sw[SR][NSC];
+    uint32_t hv[NSC][4];
+#pragma unroll
+    for (int i = 0; i < SR; ++i) {
+      const uint4* row = reinterpret_cast<const uint4*>(sw2 + static_cast<int64_t>(min(r0 + sr0 + i, H - 1)) * Is);
+#pragma unroll
+      for (int c = 0; c < NSC; ++c) sw[i][c] = row[min(lane + 64 * c, nsc - 1)];
+    }
+#pragma unroll
+    for (int c = 0; c < NSC; ++c) {
+      const uint4 v = reinterpret_cast<const uint4*>(hs)[min(lane + 64 * c, nsc - 1)];
+      hv[c][0] = v.x; hv[c][1] = v.y; hv[c][2] = v.z; hv[c][3] = v.w;
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int c = 0; c < NSC; ++c)
+      if (lane + 64 * c >= nsc) {
+#pragma unroll
+        for (int i = 0; i < SR; ++i) sw[i][c] = make_uint4(0, 0, 0, 0);
+      }
+    float acc[SR];
+#pragma unroll
+    for (int i = 0; i < SR; ++i) {
+      acc[i] = 0.0f;
+#pragma unroll
+      for (int c = 0; c < NSC; ++c) acc[i] = bf16_chunk_dot(sw[i][c], hv[c], acc[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < SR; ++i) acc[i] = wave_sum(acc[i]);
+    if (lane == 0) {
+#pragma unroll
+      for (int i = 0; i < SR; ++i) ysp[sr0 + i] = acc[i];
+    }
+  }
+  __syncthreads();
+  const int tid = threadIdx.x;
+  if (tid < R && r0 + tid < H) {
+    float o = Is > 0 ? ysp[tid] : 0.0f;
+    for (int k = 0; k < K; ++k) o += part[k][tid];
+    out[r0 + tid] = f32_to_bf16(o);
+  }
+}
+
 }  // namespace moe

@@ -732,9 +732,21 @@ void dec_fp8_launch(const moe_mlp_config* c, const moe_mlp_weights* w, const uin
     launch(k_dec_gateup_f8<RJ, 4, false, NJ, G>, dim3(grid), dim3(256), s, e1.a, e1.b, x, w->w13_f8,
            w->w13_f8_scale, logits, w->router_bias, K, c->routed_scaling_factor, ids, wts, ids_out, w_out,
            c->num_experts, H, I, c->swiglu_limit, h);
-  // I <= 2048: at most 2 chunks of 16 bytes per lane and down row
-  launch(k_dec_down_combine_f8<R, NW, NP, NSC, 2, G>, dim3(static_cast<unsigned>(cdiv(H, R))), dim3(NW * 64), s,
-         e2.a, e2.b, h, w->w2_f8, w->w2_f8_scale, w->shared_w2, hs, Is, ids, wts, c->num_experts, K, H, I, out, T);
+  // I <= 2048: at most 2 chunks of 16 bytes per lane and down row.  More
+  // than 16 slots (3 or 4 tokens at top-8): 8 rows per block, a wavefront per
+  // slot and a grid row per token, so each h vector is read once per 8 rows
+  // (measured, 4 tokens: 65.5 -> 42.9 us); up to 16 slots the 4-row blocks,
+  // one slot per wavefront, are as fast (1 and 2 tokens: 13.6 / 13.4 us and
+  // 23.3 / 24.2 us; 16-row blocks 20.9 us at 1 token).
+  constexpr int R1 = 8, NSW1 = 4;
+  if (K + NSW1 <= 16 && T * K > 16)
+    launch(k_dec_down_combine1_f8<R1, NSW1, NSC, 2, G>,
+           dim3(static_cast<unsigned>(cdiv(H, R1)), static_cast<unsigned>(T)),
+           dim3(static_cast<unsigned>((K + NSW1) * 64)), s, e2.a, e2.b, h, w->w2_f8, w->w2_f8_scale, w->shared_w2,
+           hs, Is, ids, wts, c->num_experts, K, H, I, out);
+  else
+    launch(k_dec_down_combine_f8<R, NW, NP, NSC, 2, G>, dim3(static_cast<unsigned>(cdiv(H, R))), dim3(NW * 64), s,
+           e2.a, e2.b, h, w->w2_f8, w->w2_f8_scale, w->shared_w2, hs, Is, ids, wts, c->num_experts, K, H, I, out, T);
 }
 
 template <class G, int NJ, int NSC>
