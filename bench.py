@@ -578,6 +578,13 @@ def main():
                 outs_t = [torch.empty((T, w.H), dtype=torch.bfloat16, device=dev) for _ in range(R)]
                 st_t = stage_times(cfg, wts_t, xs_t, outs_t, False, 4 * R, ev, capi.workspace(cfg, T, False, dev))
                 extra[f"decode_t{T}"]["stage_us"] = {k: round(v * 1e3, 1) for k, v in st_t.items()}
+                # the routed expert projections alone: the touched experts' bytes over the
+                # routed gate/up + routed down kernel time (the decode expert-GEMV figure)
+                ue = extra[f"decode_t{T}"]["unique_experts"]
+                rt = (st_t["routed_gateup"] + st_t["routed_down"]) * 1e-3
+                gbs = ue * w.expert_bytes / rt / 1e9
+                extra[f"decode_t{T}"]["routed_expert_gbs"] = round(gbs, 1)
+                extra[f"decode_t{T}"]["routed_expert_frac_hbm_peak"] = round(gbs / HBM_PEAK_GBS, 4)
             if T >= 16:
                 extra[f"decode_t{T}"]["weights"] = ("routed NVFP4: row-major and tile-layout copies resident "
                                                     "(the few-token MFMA kernels read the tile layout)")
