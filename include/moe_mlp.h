@@ -129,8 +129,10 @@ typedef struct moe_mlp_weights {
    * tile layout of moe_nvfp4_tile_pack (same sizes as the row-major arrays).
    * When a projection's codes AND scales are given, the grouped-GEMM form
    * (moe_mlp_prefill, decode from 64 tokens) reads them instead of the
-   * row-major arrays wherever its NVFP4 tile kernel runs; the values and the
-   * arithmetic are the same, so the results are bitwise the same.
+   * row-major arrays wherever its NVFP4 tile kernel runs, and so does the
+   * few-token MFMA down projection of decode batches (5..256 tokens); the
+   * values and the arithmetic are the same, so the results are bitwise the
+   * same.
    * One resident copy of the codes: a projection's row-major codes (w13_q,
    * w2_q) may be NULL when its tile-layout codes and scales are given; every
    * kernel then reads the tile-layout codes (the decode forms with the
@@ -164,11 +166,14 @@ int moe_mlp_workspace_size(const moe_mlp_config* cfg, int64_t T, int prefill, si
 
 /*
  * Decode form ("forward": the page's one-token decode), for 1..MOE_MLP_DECODE_MAX_T
- * tokens.  Up to 63 tokens the routed experts run as W4A16 GEMVs that stream
- * the NVFP4 codes once per touched expert (1..4 tokens, the MTP verify
- * shapes: three fused launches), and the BF16 shared expert as a GEMV.  From 64 tokens on, the call runs the
- * grouped-GEMM kernels of moe_mlp_prefill (faster there; the workspace size
- * and stage list follow).
+ * tokens.  Up to 63 tokens the routed experts stream the NVFP4 codes once
+ * per touched expert: 1..4 tokens (the MTP verify shapes) in three fused
+ * launches of W4A16 GEMVs; 5..63 tokens with W4A16 GEMVs for gate/up and,
+ * when I is a multiple of 512 up to 2048 and H of 64, an MFMA down
+ * projection that dequantises each weight once for all of an expert's
+ * tokens.  From 64 tokens on, the call runs the kernels of moe_mlp_prefill
+ * (faster there; up to 256 tokens with the same MFMA down projection; the
+ * workspace size and stage list follow).
  *   x        [T, H] bf16 input.
  *   out      [T, H] bf16 output.
  *   ids_out  [T, K] int32 chosen expert ids, descending biased score
