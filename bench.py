@@ -582,9 +582,9 @@ def main():
                 # routed gate/up + routed down kernel time (the decode expert-GEMV figure)
                 ue = extra[f"decode_t{T}"]["unique_experts"]
                 rt = (st_t["routed_gateup"] + st_t["routed_down"]) * 1e-3
-                gbs = ue * w.expert_bytes / rt / 1e9
-                extra[f"decode_t{T}"]["routed_expert_gbs"] = round(gbs, 1)
-                extra[f"decode_t{T}"]["routed_expert_frac_hbm_peak"] = round(gbs / HBM_PEAK_GBS, 4)
+                r_gbs = ue * w.expert_bytes / rt / 1e9
+                extra[f"decode_t{T}"]["routed_expert_gbs"] = round(r_gbs, 1)
+                extra[f"decode_t{T}"]["routed_expert_frac_hbm_peak"] = round(r_gbs / HBM_PEAK_GBS, 4)
             if T >= 16:
                 extra[f"decode_t{T}"]["weights"] = ("routed NVFP4: row-major and tile-layout copies resident "
                                                     "(the few-token MFMA kernels read the tile layout)")
@@ -762,6 +762,10 @@ def main():
         "cpu_baseline": cpu,
     }
     rec.update(extra)
+    # the headline must be the bytes of a step over its measured time
+    chk = rec["bytes_per_step"] / (rec["ms_per_step"] * 1e-3) / 1e9
+    if abs(chk - rec["value"]) > 0.01 * chk:
+        raise RuntimeError(f"bench: value {rec['value']} is not bytes_per_step / ms_per_step ({chk:.1f})")
     print(json.dumps(rec), flush=True)
 
 
