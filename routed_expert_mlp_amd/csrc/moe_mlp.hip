@@ -466,9 +466,13 @@ void gemm(const GemmArgs& a0, int64_t m_tiles, hipStream_t s, Ev ev, int small_r
         w_rows * a.kdim / 2 < (int64_t(1) << 31)) {
       a.n_blocks = static_cast<int>(cdiv(a.half_n, MODE == GEMM_GATEUP ? F4_WROWS / 2 : F4_WROWS));
       const bool use_small = MODE == GEMM_GATEUP && small_rows == F4M_ROWS;
-      // up to 64 tokens k_gemm_nvfp4_m32 takes every tile (a tile of more
-      // than 32 rows in two passes)
-      const bool small_only = use_small && max_count >= 0 && max_count <= 2 * F4M_ROWS;
+      // up to 64 tokens and 512 slots k_gemm_nvfp4_m32 takes every tile (a
+      // tile of more than 32 rows in two passes; the 128-row kernel's launch
+      // would mostly find nothing to do: 4.4 us at 64 tokens); with more
+      // slots (top-16 at 64 tokens) the tiles of more than 32 rows go to the
+      // 128-row kernel in one pass (64 tokens top-16 with 8 hot experts:
+      // routed gate/up 283.6 -> 273.6 us)
+      const bool small_only = use_small && max_count >= 0 && max_count <= 2 * F4M_ROWS && slots <= 512;
       const int64_t big_tiles = use_small ? std::min<int64_t>(m_tiles, slots / (F4M_ROWS + 1)) : m_tiles;
       a.skip_rows = (use_small && !small_only) ? F4M_ROWS : 0;
       with_ct(a.bq_t && a.bs_t, [&](auto ctc) {
