@@ -52,11 +52,16 @@ using DecGeoAny = DecGeo<0, 0, 0, 0, -1>;
 //   NR: float4 chunks per lane of a router row (>= H / 256)
 //   NS: 8-bf16 chunks per lane of a shared row (>= H / 512)
 // -------------------------------------------------------------------------
+// keys (may be null): also the top-k sort key of each expert (router.hpp
+// topk_key of its logit and correction bias), so that the routed gate/up
+// launch starts its selection from the keys.
 template <int NR, int NS, class G>
 __global__ __launch_bounds__(256) void k_dec_logits_shared(const uint16_t* __restrict__ x,
                                                            const float* __restrict__ wr, float* __restrict__ logits,
                                                            int E_, int H_, const uint16_t* __restrict__ sw13, int Is_,
-                                                           uint16_t* __restrict__ hs, float L, int n_logit_blocks) {
+                                                           uint16_t* __restrict__ hs, float L, int n_logit_blocks,
+                                                           const float* __restrict__ bias = nullptr,
+                                                           uint64_t* __restrict__ keys = nullptr) {
   const int E = G::E ? G::E : E_, H = G::H ? G::H : H_;
   const int Is = G::IS >= 0 ? G::IS : Is_;
   // with the geometry compiled in and rows of exactly 64 NR float4 / 64 NS
@@ -68,6 +73,7 @@ __global__ __launch_bounds__(256) void k_dec_logits_shared(const uint16_t* __res
     if (e >= E) return;
     const float4* row = reinterpret_cast<const float4*>(wr + static_cast<int64_t>(e) * H);
     const uint2* xv = reinterpret_cast<const uint2*>(x);
+    const float be = keys ? bias[e] : 0.0f;
     float4 w[NR];
     uint2 xs[NR];
     const int nch = H >> 2;
@@ -86,7 +92,10 @@ __global__ __launch_bounds__(256) void k_dec_logits_shared(const uint16_t* __res
       acc = fmaf(__uint_as_float(xs[i].y & 0xffff0000u), w[i].w, acc);
     }
     acc = wave_sum(acc);
-    if (lane == 0) logits[e] = acc;
+    if (lane == 0) {
+      logits[e] = acc;
+      if (keys) keys[e] = topk_key(acc, be, e);
+    }
   } else {
     const int j = (blockIdx.x - n_logit_blocks) * 4 + wv;
     if (j >= Is) return;
@@ -235,7 +244,8 @@ __global__ __launch_bounds__(256) void k_dec_gateup(const uint16_t* __restrict__
                                                     const float* __restrict__ logits, const float* __restrict__ bias,
                                                     int K_, float rsf, int32_t* __restrict__ ids,
                                                     float* __restrict__ wts, int32_t* ids_out, float* w_out, int E_,
-                                                    int H_, int I_, float L, uint16_t* __restrict__ h) {
+                                                    int H_, int I_, float L, uint16_t* __restrict__ h,
+                                                    const uint64_t* __restrict__ keys = nullptr) {
   const int K = G::K ? G::K : K_, E = G::E ? G::E : E_, H = G::H ? G::H : H_, I = G::I ? G::I : I_;
   __shared__ int s_sel;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
@@ -250,9 +260,13 @@ __global__ __launch_bounds__(256) void k_dec_gateup(const uint16_t* __restrict__
   if (wv == 0) {
     const bool writer = jb == 0 && k == 0;
     const int64_t o = static_cast<int64_t>(t) * K;
-    const int sel = topk_wave<NJ>(logits + static_cast<int64_t>(t) * E, bias, E, K, rsf, k,
-                                  writer ? ids + o : nullptr, wts + o, ids_out ? ids_out + o : nullptr,
-                                  w_out ? w_out + o : nullptr);
+    // from the launch-1 sort keys when given (the same keys, built by the same expression)
+    const int sel = keys ? topk_wave_keys<NJ>(keys + static_cast<int64_t>(t) * E, logits + static_cast<int64_t>(t) * E,
+                                              E, K, rsf, k, writer ? ids + o : nullptr, wts + o,
+                                              ids_out ? ids_out + o : nullptr, w_out ? w_out + o : nullptr)
+                         : topk_wave<NJ>(logits + static_cast<int64_t>(t) * E, bias, E, K, rsf, k,
+                                         writer ? ids + o : nullptr, wts + o, ids_out ? ids_out + o : nullptr,
+                                         w_out ? w_out + o : nullptr);
     if (lane == 0) s_sel = sel;
   }
   __syncthreads();

@@ -81,6 +81,7 @@ struct Plan {
   size_t count = 0, offset = 0, perm = 0, n_tiles = 0, tile_e = 0, tile_m0 = 0;  // prefill permutation
   size_t phist = 0, pbase = 0, prank = 0;                                        // permutation scratch
   size_t h = 0, hs = 0, y = 0, ys = 0;
+  size_t keys = 0;                                                               // one-token decode: top-k sort keys
   size_t wsplit = 0;                                                             // router weight, 3 bf16 planes
   int logit_planes = 1;
   int logit_splits = 1;       // reduction parts of the split-weight logits GEMM
@@ -183,6 +184,7 @@ Plan make_plan(const moe_mlp_config* c, int64_t T, int prefill) {
     p.g_slots = a.take(size_t(S) * 4);
   }
   p.h = a.take(size_t(S * I) * 2);
+  if (!prefill && T == 1 && c->kind == MOE_MLP_KIND_ROUTED) p.keys = a.take(size_t(E) * 8);
   if (Is) {
     if (skinny_ok(T, H) && skinny_ok(T, Is)) {
       p.skinny = true;
@@ -635,14 +637,15 @@ dim3 logits_shared_t_grid(int row_blocks, int64_t T) {
 constexpr int kDecRJ = 4;
 
 void dec_gateup(const moe_mlp_config* c, const moe_mlp_weights* w, const uint16_t* x, const float* logits,
-                int32_t* ids, float* wts, int32_t* ids_out, float* w_out, uint16_t* h, int T, hipStream_t s, Ev ev) {
+                int32_t* ids, float* wts, int32_t* ids_out, float* w_out, uint16_t* h, int T, hipStream_t s, Ev ev,
+                const uint64_t* keys = nullptr) {
   constexpr int NC = 2;
   const int H = c->hidden, I = c->moe_intermediate, K = c->top_k;
   const unsigned grid = static_cast<unsigned>(T * K * cdiv(I, 4 * kDecRJ));
   const uint8_t* q13 = codes13(w);
   auto go = [&](auto kern) {
     launch(kern, dim3(grid), dim3(256), s, ev.a, ev.b, x, q13, w->w13_s, w->w13_g, logits, w->router_bias, K,
-           c->routed_scaling_factor, ids, wts, ids_out, w_out, c->num_experts, H, I, c->swiglu_limit, h);
+           c->routed_scaling_factor, ids, wts, ids_out, w_out, c->num_experts, H, I, c->swiglu_limit, h, keys);
   };
   with_ct(!w->w13_q, [&](auto ctc) {
     constexpr bool CT = decltype(ctc)::value;
@@ -796,16 +799,18 @@ void dec_fp8(const moe_mlp_config* c, const moe_mlp_weights* w, const uint16_t* 
 
 void decode1(const moe_mlp_config* c, const moe_mlp_weights* w, const uint16_t* x, int T, uint16_t* out,
              int32_t* ids_out, float* w_out, float* logits, int32_t* ids, float* wts, uint16_t* h, uint16_t* hs,
-             hipStream_t s, Ev e0, Ev e1, Ev e2) {
+             hipStream_t s, Ev e0, Ev e1, Ev e2, uint64_t* keys) {
   const int H = c->hidden, E = c->num_experts, K = c->top_k;
   const int Is = c->n_shared_experts ? c->shared_intermediate : 0;
   const int nlb = static_cast<int>(cdiv(E, 4)), nsb = static_cast<int>(cdiv(Is, 4));
+  // one token, NVFP4 experts: launch 1 also writes the top-k sort keys
+  if (T != 1 || is_fp8(c)) keys = nullptr;
   if (T == 1 && glm_flash_geometry(c))
     launch(k_dec_logits_shared<16, 8, DecGeoFlash>, dim3(nlb + nsb), dim3(256), s, e0.a, e0.b, x, w->router_w, logits,
-           E, H, w->shared_w13, Is, hs, c->swiglu_limit, nlb);
+           E, H, w->shared_w13, Is, hs, c->swiglu_limit, nlb, w->router_bias, keys);
   else if (T == 1)
     launch(k_dec_logits_shared<16, 8, DecGeoAny>, dim3(nlb + nsb), dim3(256), s, e0.a, e0.b, x, w->router_w, logits,
-           E, H, w->shared_w13, Is, hs, c->swiglu_limit, nlb);
+           E, H, w->shared_w13, Is, hs, c->swiglu_limit, nlb, w->router_bias, keys);
   else
     launch(k_dec_logits_shared_t<16, 8>, logits_shared_t_grid(nlb + nsb, T), dim3(256), s, e0.a, e0.b, x, w->router_w, logits, E, H,
            w->shared_w13, Is, hs, c->swiglu_limit, nlb, T);
@@ -813,7 +818,7 @@ void decode1(const moe_mlp_config* c, const moe_mlp_weights* w, const uint16_t* 
     dec_fp8(c, w, x, logits, ids, wts, ids_out, w_out, h, hs, out, T, s, e1, e2);
     return;
   }
-  dec_gateup(c, w, x, logits, ids, wts, ids_out, w_out, h, T, s, e1);
+  dec_gateup(c, w, x, logits, ids, wts, ids_out, w_out, h, T, s, e1, keys);
   if (K + kDown1Shared <= 16) {
     launch_down_combine1(c, w, h, hs, ids, wts, out, T, s, e2);
     return;
@@ -896,7 +901,8 @@ int run_layer(const moe_mlp_config* c, const moe_mlp_weights* w, const uint16_t*
   const float rsf = c->routed_scaling_factor;
 
   if (decode1_ok(c, T, prefill)) {
-    decode1(c, w, x, Ti, out, ids_out, w_out, logits, ids, wts, h, hs, s, ev(0), ev(1), ev(2));
+    decode1(c, w, x, Ti, out, ids_out, w_out, logits, ids, wts, h, hs, s, ev(0), ev(1), ev(2),
+            p.keys ? at<uint64_t>(ws, p.keys) : nullptr);
     return launch_status();
   }
   // decode of up to 16 tokens with H <= 4096: router logits and the shared

@@ -271,19 +271,21 @@ __device__ __forceinline__ float logit_of(const float* __restrict__ lrow, int E,
   return v;
 }
 
+// Sort key of expert e with router logit l and correction bias b (the biased
+// sigmoid score decides, then the lower id).  Every top-k path builds its
+// keys with this one expression, so they rank the experts bit for bit alike.
+__device__ __forceinline__ uint64_t topk_key(float l, float b, int e) {
+  return u64_of(0xFFFFFFFFu - static_cast<uint32_t>(e), f32_order_bits(1.0f / (1.0f + expf(-l)) + b));
+}
+
+// The rounds of topk_wave over this lane's NJ keys (experts lane + 64 j;
+// 0 for none), the winners' weights from their logits (lrow, planes, splits
+// as in logit_of).
 template <int NJ>
-__device__ __forceinline__ int topk_wave(const float* __restrict__ lrow, const float* __restrict__ bias, int E,
-                                         int K, float rsf, int want, int32_t* ids, float* wts, int32_t* ids2,
-                                         float* wts2, int planes = 1, int splits = 1, int64_t sstride = 0) {
+__device__ __forceinline__ int topk_rounds(uint64_t (&key)[NJ], const float* __restrict__ lrow, int E, int K,
+                                           float rsf, int want, int32_t* ids, float* wts, int32_t* ids2,
+                                           float* wts2, int planes, int splits, int64_t sstride) {
   const int lane = threadIdx.x & 63;
-  uint64_t key[NJ];
-#pragma unroll
-  for (int j = 0; j < NJ; ++j) {
-    const int e = lane + 64 * j;
-    key[j] = e < E ? u64_of(0xFFFFFFFFu - static_cast<uint32_t>(e),
-                            f32_order_bits(1.0f / (1.0f + expf(-logit_of(lrow, E, planes, e, splits, sstride))) + bias[e]))
-                   : 0;                          // below every real key
-  }
 #pragma unroll
   for (int i = 0; i < NJ - 1; ++i)
 #pragma unroll
@@ -326,7 +328,7 @@ __device__ __forceinline__ int topk_wave(const float* __restrict__ lrow, const f
     if (lane == k) my_id = id;
   }
   if (ids) {
-    // the same expression as above on the same logit: the same bits
+    // the same expression as in topk_key on the same logit: the same bits
     const float my_s = lane < K ? 1.0f / (1.0f + expf(-logit_of(lrow, E, planes, my_id, splits, sstride))) : 0.0f;
     float sum = 0.0f;
     for (int k = 0; k < K; ++k) sum += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_s), k));
@@ -339,6 +341,36 @@ __device__ __forceinline__ int topk_wave(const float* __restrict__ lrow, const f
     }
   }
   return want_id;
+}
+
+template <int NJ>
+__device__ __forceinline__ int topk_wave(const float* __restrict__ lrow, const float* __restrict__ bias, int E,
+                                         int K, float rsf, int want, int32_t* ids, float* wts, int32_t* ids2,
+                                         float* wts2, int planes = 1, int splits = 1, int64_t sstride = 0) {
+  const int lane = threadIdx.x & 63;
+  uint64_t key[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const int e = lane + 64 * j;
+    key[j] = e < E ? topk_key(logit_of(lrow, E, planes, e, splits, sstride), bias[e], e) : 0;   // 0: below every real key
+  }
+  return topk_rounds<NJ>(key, lrow, E, K, rsf, want, ids, wts, ids2, wts2, planes, splits, sstride);
+}
+
+// topk_wave on keys the logits kernel already built with topk_key (one
+// fp32 logit per expert, no planes or parts).
+template <int NJ>
+__device__ __forceinline__ int topk_wave_keys(const uint64_t* __restrict__ keys, const float* __restrict__ lrow,
+                                              int E, int K, float rsf, int want, int32_t* ids, float* wts,
+                                              int32_t* ids2, float* wts2) {
+  const int lane = threadIdx.x & 63;
+  uint64_t key[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const int e = lane + 64 * j;
+    key[j] = e < E ? keys[e] : 0;
+  }
+  return topk_rounds<NJ>(key, lrow, E, K, rsf, want, ids, wts, ids2, wts2, 1, 1, 0);
 }
 
 template <int NJ>
