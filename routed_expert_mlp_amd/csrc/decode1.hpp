@@ -146,7 +146,8 @@ __global__ __launch_bounds__(256) void k_dec_logits_shared_t(const uint16_t* __r
                                                              float* __restrict__ logits, int E, int H,
                                                              const uint16_t* __restrict__ sw13, int Is,
                                                              uint16_t* __restrict__ hs, float L, int n_logit_blocks,
-                                                             int T) {
+                                                             int T, const float* __restrict__ bias = nullptr,
+                                                             uint64_t* __restrict__ keys = nullptr) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int ta = blockIdx.y * DEC_TG, tb = min(T, ta + DEC_TG);
   // the group's x rows, staged once per block in LDS (after the weight loads
@@ -161,6 +162,7 @@ __global__ __launch_bounds__(256) void k_dec_logits_shared_t(const uint16_t* __r
   if (static_cast<int>(blockIdx.x) < n_logit_blocks) {
     const int e = blockIdx.x * 4 + wv;
     const float4* row = reinterpret_cast<const float4*>(wr + static_cast<int64_t>(min(e, E - 1)) * H);
+    const float be = keys ? bias[min(e, E - 1)] : 0.0f;
     float4 w[NR];
     const int nch = H >> 2;
 #pragma unroll
@@ -187,7 +189,10 @@ __global__ __launch_bounds__(256) void k_dec_logits_shared_t(const uint16_t* __r
         acc = fmaf(__uint_as_float(xs[i].y & 0xffff0000u), w[i].w, acc);
       }
       acc = wave_sum(acc);
-      if (lane == 0) logits[static_cast<int64_t>(t) * E + e] = acc;
+      if (lane == 0) {
+        logits[static_cast<int64_t>(t) * E + e] = acc;
+        if (keys) keys[static_cast<int64_t>(t) * E + e] = topk_key(acc, be, e);
+      }
     }
   } else {
     const int j = (blockIdx.x - n_logit_blocks) * 4 + wv;

@@ -184,7 +184,7 @@ Plan make_plan(const moe_mlp_config* c, int64_t T, int prefill) {
     p.g_slots = a.take(size_t(S) * 4);
   }
   p.h = a.take(size_t(S * I) * 2);
-  if (!prefill && T == 1 && c->kind == MOE_MLP_KIND_ROUTED) p.keys = a.take(size_t(E) * 8);
+  if (!prefill && T <= DEC_MAX_T && c->kind == MOE_MLP_KIND_ROUTED) p.keys = a.take(size_t(T * E) * 8);
   if (Is) {
     if (skinny_ok(T, H) && skinny_ok(T, Is)) {
       p.skinny = true;
@@ -803,8 +803,8 @@ void decode1(const moe_mlp_config* c, const moe_mlp_weights* w, const uint16_t* 
   const int H = c->hidden, E = c->num_experts, K = c->top_k;
   const int Is = c->n_shared_experts ? c->shared_intermediate : 0;
   const int nlb = static_cast<int>(cdiv(E, 4)), nsb = static_cast<int>(cdiv(Is, 4));
-  // one token, NVFP4 experts: launch 1 also writes the top-k sort keys
-  if (T != 1 || is_fp8(c)) keys = nullptr;
+  // NVFP4 experts: launch 1 also writes the top-k sort keys
+  if (is_fp8(c)) keys = nullptr;
   if (T == 1 && glm_flash_geometry(c))
     launch(k_dec_logits_shared<16, 8, DecGeoFlash>, dim3(nlb + nsb), dim3(256), s, e0.a, e0.b, x, w->router_w, logits,
            E, H, w->shared_w13, Is, hs, c->swiglu_limit, nlb, w->router_bias, keys);
@@ -813,7 +813,7 @@ void decode1(const moe_mlp_config* c, const moe_mlp_weights* w, const uint16_t* 
            E, H, w->shared_w13, Is, hs, c->swiglu_limit, nlb, w->router_bias, keys);
   else
     launch(k_dec_logits_shared_t<16, 8>, logits_shared_t_grid(nlb + nsb, T), dim3(256), s, e0.a, e0.b, x, w->router_w, logits, E, H,
-           w->shared_w13, Is, hs, c->swiglu_limit, nlb, T);
+           w->shared_w13, Is, hs, c->swiglu_limit, nlb, T, w->router_bias, keys);
   if (is_fp8(c)) {
     dec_fp8(c, w, x, logits, ids, wts, ids_out, w_out, h, hs, out, T, s, e1, e2);
     return;
@@ -912,7 +912,7 @@ int run_layer(const moe_mlp_config* c, const moe_mlp_weights* w, const uint16_t*
   if (fused_k1) {
     const int nlb = static_cast<int>(cdiv(E, 4)), nsb = static_cast<int>(cdiv(Is, 4));
     launch(k_dec_logits_shared_t<16, 8>, logits_shared_t_grid(nlb + nsb, Ti), dim3(256), s, ev(0).a, ev(0).b, x, w->router_w, logits,
-           E, H, w->shared_w13, Is, hs, L, nlb, Ti);
+           E, H, w->shared_w13, Is, hs, L, nlb, Ti, static_cast<const float*>(nullptr), static_cast<uint64_t*>(nullptr));
   } else {
     router_logits_plan(p, ws, x, w->router_w, logits, T, H, E, s, ev(0));
   }
