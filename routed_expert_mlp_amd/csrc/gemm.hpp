@@ -75,6 +75,10 @@ struct GemmArgs {
   // routed NVFP4 kernel only: tiles of at most skip_rows rows are left to
   // k_gemm_nvfp4_m32 (0 = none)
   int skip_rows;
+  // k_gemm_nvfp4_m32 only: with split_pass > 0 each of the first n_tiles[1]
+  // tiles (those of more than 32 rows) is taken by split_pass workgroups, one
+  // 32-row pass each, ahead of the other tiles (0 = passes in one workgroup)
+  int split_pass;
 };
 
 template <bool NVFP4, int MODE, bool ROUTED>

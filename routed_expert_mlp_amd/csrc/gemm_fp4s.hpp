@@ -219,24 +219,45 @@ __device__ __forceinline__ void f4m_mainloop(const F4MLds& L, const F4Src& src, 
 // k_gemm_nvfp4) it takes the tiles after the first n_tiles[1], each of at
 // most 32 rows; without, every tile, in passes of 32 rows that each stream
 // the tile's weights again (for few tokens, where a tile of more than 32 rows
-// is rare and an extra launch of k_gemm_nvfp4 for it would cost more).
+// is rare and an extra launch of k_gemm_nvfp4 for it would cost more).  With
+// split_pass = S the passes of those first n_tiles[1] tiles go to workgroups
+// of their own: the first blocks of the grid take (tile, column block, pass)
+// with the pass varying fastest inside each XCD's share, so the S passes over
+// the same weight rows run side by side in one L2, and the remaining blocks
+// take the tiles of at most 32 rows, each XCD a contiguous share.
 template <int MODE, bool TILED>
 __global__ __launch_bounds__(F4_THREADS, 1) void k_gemm_nvfp4_m32(GemmArgs a) {
   // gate/up only: the down projection stays on k_gemm_nvfp4 (its short
   // reduction did not pay for this kernel's deeper ring: 3% slower, measured)
   static_assert(MODE == GEMM_GATEUP, "k_gemm_nvfp4_m32 computes the gate/up projection");
   const int nbn = a.n_blocks;
-  const int nbig = a.skip_rows ? a.n_tiles[1] : 0;
+  const int nbig = (a.skip_rows || a.split_pass) ? a.n_tiles[1] : 0;
   const int ntl = a.n_tiles[0] - nbig;
   const int total = ntl * nbn, chunk = (total + 7) >> 3;
-  const int kk = blockIdx.x >> 3;
-  if (kk >= chunk) return;
-  const int w = (blockIdx.x & 7) * chunk + kk;
-  if (w >= total) return;
-  const int tile = nbig + w / nbn, nblk = w - (w / nbn) * nbn;
+  const int S = a.split_pass;
+  const int htotal = nbig * nbn * S, hchunk = (htotal + 7) >> 3;   // 0 without split_pass
+  int kk = blockIdx.x >> 3;
+  int tile, nblk, mp0 = 0, mp1 = GM_BM;
+  if (kk < hchunk) {
+    const int w = (blockIdx.x & 7) * hchunk + kk;
+    if (w >= htotal) return;
+    const int q = w / S;
+    tile = q / nbn;
+    nblk = q - tile * nbn;
+    mp0 = F4M_ROWS * (w - q * S);
+    mp1 = mp0 + F4M_ROWS;
+  } else {
+    kk -= hchunk;
+    if (kk >= chunk) return;
+    const int w = (blockIdx.x & 7) * chunk + kk;
+    if (w >= total) return;
+    tile = nbig + w / nbn;
+    nblk = w - (w / nbn) * nbn;
+  }
   const int e = a.tile_expert[tile];
   const int m0 = a.tile_m0[tile];
-  const int valid = min(GM_BM, a.count[e] - m0);
+  const int valid = min(mp1, min(GM_BM, a.count[e] - m0));
+  if (mp0 >= valid) return;
   if (a.skip_rows && valid > F4M_ROWS) return;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int kdim = a.kdim;
@@ -275,11 +296,11 @@ __global__ __launch_bounds__(F4_THREADS, 1) void k_gemm_nvfp4_m32(GemmArgs a) {
   const F4MLds L{{la0, la1, la2, la3}, {lc0, lc1, lc2, lc3}, {ls0, ls1}};
   const int ln = lane & 31;
 
-  for (int mp = 0; mp < valid; mp += F4M_ROWS) {
+  for (int mp = mp0; mp < valid; mp += F4M_ROWS) {
     const int pv = min(F4M_ROWS, valid - mp);   // rows of this pass
     const int p0 = a.offset[e] + m0 + mp;
     // every wavefront has left the previous pass's last stage before its rings refill
-    if (mp) __syncthreads();
+    if (mp > mp0) __syncthreads();
     // activation DMA (wavefronts 0-3): pass rows 8 wv .. +7, 8 lanes per row
     {
       const int r = 8 * (wv & 3) + (lane >> 3);

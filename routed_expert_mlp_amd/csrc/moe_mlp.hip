@@ -446,10 +446,16 @@ void gemm_fp8(const GemmArgs& a0, int64_t m_tiles, hipStream_t s, Ev ev) {
 // small-tile kernel at 64 tokens (both measured).
 int small_tile_rows(int64_t T) { return T <= MOE_MLP_DECODE_MAX_T ? F4M_ROWS : 0; }
 
+// Largest expert row count for which k_gemm_nvfp4_m32 splits the tiles of
+// more than 32 rows into one workgroup per pass (instead of k_gemm_nvfp4).
+constexpr int64_t SPLIT_PASS_MAX_ROWS = 2 * F4M_ROWS;
+
 // Routed NVFP4 projections with a reduction length that is a multiple of 256
 // and at least 512 take k_gemm_nvfp4; with small_rows (gate/up) it takes only
 // the tiles of more than small_rows rows (at most slots / (small_rows + 1) of
-// them) and k_gemm_nvfp4_m32 the rest; max_count = the most rows an expert can
+// them) and k_gemm_nvfp4_m32 the rest (up to 64 rows an expert
+// k_gemm_nvfp4_m32 takes the long tiles too, one workgroup per 32-row
+// pass); max_count = the most rows an expert can
 // hold (the token count): at most 64, k_gemm_nvfp4_m32 takes every tile and
 // k_gemm_nvfp4 is not launched (its launch cost 4.4 us at 64 tokens, where no
 // tile had more than 32 rows).  BF16
@@ -477,16 +483,28 @@ void gemm(const GemmArgs& a0, int64_t m_tiles, hipStream_t s, Ev ev, int small_r
       // routed gate/up 283.6 -> 273.6 us)
       const bool small_only = use_small && max_count >= 0 && max_count <= 2 * F4M_ROWS && slots <= 512;
       const int64_t big_tiles = use_small ? std::min<int64_t>(m_tiles, slots / (F4M_ROWS + 1)) : m_tiles;
-      a.skip_rows = (use_small && !small_only) ? F4M_ROWS : 0;
+      // with more slots but still at most 64 rows an expert (top-16 at 64
+      // tokens), the tiles of more than 32 rows are split into one workgroup
+      // per 32-row pass inside k_gemm_nvfp4_m32, dispatched first, instead:
+      // the few hot experts' tiles no longer hold a handful of CUs after the
+      // rest of the chip has finished (64 tokens top-16 with 8 hot experts:
+      // routed gate/up 269 -> 210 us, step 464 -> 421 us; 128 tokens, where
+      // the split would take up to 4 passes, measured the same either way)
+      const bool split = use_small && !small_only && max_count >= 0 && max_count <= SPLIT_PASS_MAX_ROWS;
+      const int split_s = split ? static_cast<int>(cdiv(max_count, F4M_ROWS)) : 0;
+      a.skip_rows = (use_small && !small_only && !split) ? F4M_ROWS : 0;
+      a.split_pass = split_s;
       with_ct(a.bq_t && a.bs_t, [&](auto ctc) {
         constexpr bool CT = decltype(ctc)::value;
-        if (!small_only && big_tiles > 0)
+        if (!small_only && !split && big_tiles > 0)
           launch(k_gemm_nvfp4<MODE, CT>, dim3(static_cast<unsigned>(8 * cdiv(big_tiles * a.n_blocks, 8))),
                  dim3(F4_THREADS), s, ev.a, use_small ? nullptr : ev.b, a);
         if constexpr (MODE == GEMM_GATEUP) {
-          if (use_small)
-            launch(k_gemm_nvfp4_m32<MODE, CT>, dim3(static_cast<unsigned>(8 * cdiv(m_tiles * a.n_blocks, 8))),
-                   dim3(F4_THREADS), s, (small_only || big_tiles == 0) ? ev.a : nullptr, ev.b, a);
+          if (use_small) {
+            const int64_t blocks = 8 * (cdiv(big_tiles * a.n_blocks * split_s, 8) + cdiv(m_tiles * a.n_blocks, 8));
+            launch(k_gemm_nvfp4_m32<MODE, CT>, dim3(static_cast<unsigned>(blocks)), dim3(F4_THREADS), s,
+                   (small_only || split || big_tiles == 0) ? ev.a : nullptr, ev.b, a);
+          }
         }
       });
       return;

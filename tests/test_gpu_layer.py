@@ -76,6 +76,21 @@ def test_decode_parity_skinny(o):
     _check_layer(device_workload("ragged_decode", **o), False, ALL, f"ragged_decode {o}")
 
 
+# Batches of 33..64 tokens with more than 512 slots (top-k above 8) in the
+# grouped-GEMM form (decode at 64 tokens, the prefill entry below): the routed
+# gate/up splits the tiles of more than 32 rows into one workgroup per 32-row
+# pass (every expert full at E = K; a mix of long and short tiles otherwise).
+SPLIT = [dict(T=64, H=512, I=512, E=16, K=16, Is=128),
+         dict(T=64, H=1024, I=1024, E=24, K=12, Is=128),
+         dict(T=48, H=512, I=512, E=40, K=16, Is=0),
+         dict(T=33, H=768, I=512, E=20, K=16, Is=64)]
+
+
+@pytest.mark.parametrize("o", SPLIT, ids=[f"T{o['T']}_E{o['E']}_K{o['K']}" for o in SPLIT])
+def test_parity_split_passes(o):
+    _check_layer(device_workload("ragged_decode", **o), o["T"] < 64, ALL, f"ragged_decode {o}")
+
+
 PREFILL = [("ragged_prefill", ALL), ("prefill_t4096", ALL), ("prefill_t4096_literal_bias", ALL)]
 
 

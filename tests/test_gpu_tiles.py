@@ -106,6 +106,16 @@ def test_tiled_weights_decode_bitwise(T):
     _run_both(DeviceRouted(RoutedInputs(w)), f"decode T={T}", prefill=False)
 
 
+@pytest.mark.parametrize("T,E,K", [(64, 16, 16), (48, 40, 16)])
+def test_tiled_weights_split_passes_bitwise(T, E, K):
+    """Batches whose routed gate/up splits the long tiles into one workgroup
+    per 32-row pass (decode at 64 tokens, prefill below), on both weight
+    layouts."""
+    w = synth.workload("ragged_decode", T=T, H=512, I=512, E=E, K=K, Is=128)
+    say(f"[case] tiled weights, {'prefill' if T < 64 else 'decode'} T={w.T} H={w.H} I={w.I} E={w.E} K={w.K}")
+    _run_both(DeviceRouted(RoutedInputs(w)), f"T={T} E={E} K={K}", prefill=T < 64)
+
+
 # One resident copy of the codes: the row-major codes left out, every kernel
 # (one-token and few-token decode, GEMV decode, grouped GEMM) reads the
 # tile-layout codes; the bytes and the arithmetic are the same, so the results
