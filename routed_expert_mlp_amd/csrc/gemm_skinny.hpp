@@ -134,9 +134,10 @@ struct SkinnyF4Args {
   int64_t stride_s;        // bytes of scales per expert
   const float* gscale;     // [E] or null (= 1)
   int N;                   // output rows
-  // expert groups: (n_groups, g_expert, g_count, g_offset), or (g_expert
-  // null) one group per expert e = blockIdx.y over positions
-  // offsets[e] .. offsets[e + 1]
+  // expert groups: (n_groups, g_expert, g_count, g_offset); or (g_count
+  // null) one group per expert over positions offsets[e] .. offsets[e + 1],
+  // e = g_expert[blockIdx.y] for blockIdx.y < n_groups (an expert order,
+  // each expert at most once), or e = blockIdx.y when g_expert is null too
   const int32_t* n_groups;
   const int32_t* g_expert;
   const int32_t* g_count;
@@ -161,13 +162,18 @@ void k_skinny_f4_down(SkinnyF4Args a) {
   constexpr int DPR = KD / 512;       // 1 KB DMA instructions per activation row
   __shared__ uint4 xs[NT * XS];
   int e, cnt, off;
-  if (a.g_expert) {
+  if (a.g_count) {
     if (static_cast<int>(blockIdx.y) >= *a.n_groups) return;
     e = a.g_expert[blockIdx.y];
     cnt = a.g_count[blockIdx.y];
     off = a.g_offset[blockIdx.y];
   } else {
-    e = blockIdx.y;
+    if (a.g_expert) {
+      if (static_cast<int>(blockIdx.y) >= *a.n_groups) return;
+      e = a.g_expert[blockIdx.y];
+    } else {
+      e = blockIdx.y;
+    }
     off = a.offsets[e];
     cnt = a.offsets[e + 1] - off;
   }

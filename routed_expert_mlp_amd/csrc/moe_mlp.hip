@@ -1030,6 +1030,12 @@ int run_layer(const moe_mlp_config* c, const moe_mlp_weights* w, const uint16_t*
       sa.gscale = w->w2_g;
       sa.N = H;
       sa.offsets = pm.offset;
+      if (small_rows && T <= GM_BM) {
+        // experts in the scheduler's tile order (at most one tile each up to
+        // 128 rows): those of more than 32 rows are dispatched first
+        sa.n_groups = pm.n_tiles;
+        sa.g_expert = pm.tile_expert;
+      }
       sa.out_idx = pm.perm;
       sa.in = h;
       sa.out = y;
