@@ -625,6 +625,14 @@ def main():
             if T >= 64:
                 line["weights"] = ("routed NVFP4: row-major and tile-layout copies resident "
                                    "(the few-token MFMA kernels read the tile layout)")
+            if wv.hot_experts:
+                # per-stage kernel times, and the routed projections' bytes over their time
+                outs_v = [torch.empty((T, wv.H), dtype=torch.bfloat16, device=dev) for _ in range(RV)]
+                st_v = stage_times(cfgv, wts_v, xs_v, outs_v, False, 4 * RV, ev, capi.workspace(cfgv, T, False, dev))
+                line["stage_us"] = {k: round(v * 1e3, 1) for k, v in st_v.items()}
+                rt = (st_v["routed_gateup"] + st_v["routed_down"]) * 1e-3
+                line["routed_expert_gbs"] = round(line["unique_experts"] * wv.expert_bytes / rt / 1e9, 1)
+                del outs_v
             extra[name] = line
             del wts_v, bv, xs_v
             torch.cuda.empty_cache()
